@@ -1,0 +1,134 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module only draws random numbers and arranges them; it holds none of the
+attention or softmax arithmetic, so the oracle and the HIP path can both be
+fed from it without sharing any of the method.
+
+Every tensor is drawn on the CPU with ``torch.Generator`` so the same bits
+reach the GPU and the oracle on any machine:
+
+* attention: Q, K, V drawn in that order as fp32 ``randn`` of shape
+  [B, H, N, d], then cast round-to-nearest-even to bf16 for the bf16
+  workloads; the causal N=4096 workload multiplies every 64th query row
+  (i % 64 == 0, every batch and head) by 8 after the cast, which is exact
+  in bf16, to force large jumps of the running row maximum;
+* row softmax: fp32 ``randn`` of shape [B, N] times ``std``; the small
+  workload overwrites row 0 with 1000 - j (a strictly falling row of huge
+  values that overflows a softmax without the max subtraction).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+SEED_BASE = 20260000
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    dtype: str            # "f32" or "bf16": element type of Q, K, V and O
+    seed: int
+    boost_every: int = 0  # >0: multiply query rows i % boost_every == 0 by boost
+    boost: float = 8.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def flops(self) -> float:
+        """Counted FLOPs: two N x N x d products, 2 FLOPs per multiply-add,
+        halved under the causal mask."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2.0 if self.causal else f
+
+    def describe(self) -> str:
+        return (f"{self.name}: {self.dtype} B={self.B} H={self.H} N={self.N} "
+                f"d={self.d} causal={int(self.causal)} seed={self.seed}")
+
+
+@dataclasses.dataclass(frozen=True)
+class SoftmaxWorkload:
+    name: str
+    B: int
+    N: int
+    std: float
+    seed: int
+    falling_row0: bool = False  # row 0 := 1000 - j
+
+    @property
+    def bytes(self) -> int:
+        """Algorithmic HBM bytes: each fp32 element read once and written once."""
+        return 8 * self.B * self.N
+
+    def describe(self) -> str:
+        return f"{self.name}: f32 [{self.B},{self.N}] std={self.std} seed={self.seed}"
+
+
+# The workloads the measurements and parity tests are defined on, named by
+# what they are.
+_ATTN_LIST = [
+    AttnWorkload("attn_f32_B1H1N128d64", 1, 1, 128, 64, False, "f32", SEED_BASE + 1),
+    AttnWorkload("attn_bf16_B2H8N1024d64", 2, 8, 1024, 64, False, "bf16", SEED_BASE + 2),
+    AttnWorkload("attn_bf16_B4H16N2048d128", 4, 16, 2048, 128, False, "bf16",
+                 SEED_BASE + 3),
+    AttnWorkload("attn_bf16_B2H16N4096d128_causal_x8rows", 2, 16, 4096, 128, True,
+                 "bf16", SEED_BASE + 4, boost_every=64),
+    AttnWorkload("attn_bf16_B1H32N8192d128_causal", 1, 32, 8192, 128, True, "bf16",
+                 SEED_BASE + 5),
+]
+_SOFTMAX_LIST = [
+    SoftmaxWorkload("softmax_f32_4x128", 4, 128, 2.0, SEED_BASE + 101,
+                    falling_row0=True),
+    SoftmaxWorkload("softmax_f32_32768x8192", 32768, 8192, 1.0, SEED_BASE + 105),
+]
+ATTN = {w.name: w for w in _ATTN_LIST}
+SOFTMAX = {w.name: w for w in _SOFTMAX_LIST}
+
+# The headline pair: the causal B*H=32, N=4096, d=128 bf16 forward and the
+# [32768, 8192] fp32 row softmax.
+HEADLINE_ATTN = "attn_bf16_B2H16N4096d128_causal_x8rows"
+HEADLINE_SOFTMAX = "softmax_f32_32768x8192"
+
+
+def attn_inputs(w: AttnWorkload, *, B: int | None = None, H: int | None = None,
+                N: int | None = None, d: int | None = None, seed: int | None = None):
+    """Return CPU tensors (Q, K, V) for workload ``w`` (shape overrides allowed
+    for edge-case tests; the recipe stays the same)."""
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    N = w.N if N is None else N
+    d = w.d if d is None else d
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    shape = (B, H, N, d)
+    out = []
+    for _ in range(3):
+        t = torch.randn(shape, generator=g, dtype=torch.float32)
+        if w.dtype == "bf16":
+            t = t.to(torch.bfloat16)
+        out.append(t)
+    q, k, v = out
+    if w.boost_every > 0 and N > 0:
+        q[:, :, ::w.boost_every, :] *= w.boost
+    return q, k, v
+
+
+def softmax_inputs(w: SoftmaxWorkload, *, B: int | None = None, N: int | None = None,
+                   seed: int | None = None) -> torch.Tensor:
+    B = w.B if B is None else B
+    N = w.N if N is None else N
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    x = torch.randn((B, N), generator=g, dtype=torch.float32) * w.std
+    if w.falling_row0 and B > 0:
+        x[0] = 1000.0 - torch.arange(N, dtype=torch.float32)
+    return x

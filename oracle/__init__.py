@@ -1,0 +1,189 @@
+"""fp64 CPU oracle for exact attention forward and the stable row softmax.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path never does.  It
+shares no code with the HIP library (``online_softmax_08_amd``) and imports
+nothing from it.
+
+The arithmetic lives in ``oracle.c`` (plain C, binary64), built by
+``oracle.build.build()`` into ``liboracle.so`` next to it.  This module only
+marshals numpy arrays to that library.  Each wrapper cites the passage its C
+routine follows; the header of ``oracle.c`` names the pages.
+
+Pinned by ``tests/test_oracle.py`` against the pages' worked examples, closed
+forms, invariants, brute force and independent library routines; the pins'
+power to catch plausible mistakes is itself checked by planting mistakes in
+copies of ``oracle.c`` (``tests/test_oracle_mutants.py``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_lp = ctypes.POINTER(ctypes.c_long)
+_L = ctypes.c_long
+
+
+def _f64(a) -> np.ndarray:
+    """Exact upcast to a contiguous float64 array (bf16/fp32 -> fp64 is exact)."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover - torch is always present here
+        pass
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_dp)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise RuntimeError(f"oracle {what} failed with code {rc}")
+
+
+class Oracle:
+    """Marshalling front end of one build of ``oracle.c`` (by default the
+    committed source; the mutant tests load deliberately broken copies)."""
+
+    def __init__(self, lib_path: str = LIB_PATH):
+        lib = ctypes.CDLL(lib_path)
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_row_softmax.argtypes = [_dp, _dp, _L, _L]
+        lib.oracle_attn_fwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _L, _L, _L, _L,
+                                        ctypes.c_double, ctypes.c_int]
+        lib.oracle_attn_rows.argtypes = [_dp, _dp, _dp, _L, _L, _L, _L,
+                                         ctypes.c_double, ctypes.c_int,
+                                         _lp, _lp, _L, _dp, _dp]
+        lib.oracle_online_row_trace.argtypes = [_dp, _L, _L, _dp, _dp]
+        lib.oracle_attn_online.argtypes = [_dp, _dp, _dp, _dp, _dp, _L, _L, _L, _L,
+                                           ctypes.c_double, ctypes.c_int, _L, _L]
+        for name in ("oracle_row_softmax", "oracle_attn_fwd", "oracle_attn_rows",
+                     "oracle_online_row_trace", "oracle_attn_online"):
+            getattr(lib, name).restype = ctypes.c_int
+        self._lib = lib
+
+    def num_threads(self) -> int:
+        """OpenMP threads the oracle's parallel loops use."""
+        return int(self._lib.oracle_num_threads())
+
+    def row_softmax(self, x) -> np.ndarray:
+        """Three-pass stable softmax of every row of x [B, N]
+        (Lesson 22, sections 2 and 3)."""
+        x = _f64(x)
+        if x.ndim != 2:
+            raise ValueError("x must be [B, N]")
+        y = np.empty_like(x)
+        _check(self._lib.oracle_row_softmax(_ptr(x), _ptr(y), x.shape[0], x.shape[1]),
+               "row_softmax")
+        return y
+
+    @staticmethod
+    def _attn_shapes(Q, K, V):
+        Q, K, V = _f64(Q), _f64(K), _f64(V)
+        if Q.ndim != 4 or K.shape != Q.shape or V.shape != Q.shape:
+            raise ValueError("Q, K, V must share one [B, H, N, d] shape")
+        return Q, K, V
+
+    def attn_fwd(self, Q, K, V, scale: float, causal: bool):
+        """Exact attention, three passes per row with the score and probability
+        rows materialised (Lesson 22, sections 12-14 and 34; four generations,
+        2.4 for lse = m + ln l).  Returns (O [B,H,N,d], lse [B,H,N])."""
+        Q, K, V = self._attn_shapes(Q, K, V)
+        B, H, N, d = Q.shape
+        O = np.empty_like(Q)
+        lse = np.empty((B, H, N), dtype=np.float64)
+        _check(self._lib.oracle_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse),
+                                         B, H, N, d, float(scale), int(bool(causal))),
+               "attn_fwd")
+        return O, lse
+
+    def attn_rows(self, Q, K, V, scale: float, causal: bool, bh, qi):
+        """The definition of ``attn_fwd`` evaluated for selected rows only:
+        row r is query qi[r] of slice bh[r] (bh = b*H + h).  Returns
+        (O_rows [nrows, d], lse_rows [nrows])."""
+        Q, K, V = self._attn_shapes(Q, K, V)
+        B, H, N, d = Q.shape
+        bh = np.ascontiguousarray(np.asarray(bh, dtype=np.int64))
+        qi = np.ascontiguousarray(np.asarray(qi, dtype=np.int64))
+        if bh.shape != qi.shape or bh.ndim != 1:
+            raise ValueError("bh and qi must be 1-D and of equal length")
+        n = bh.shape[0]
+        O = np.empty((n, d), dtype=np.float64)
+        lse = np.empty((n,), dtype=np.float64)
+        _check(self._lib.oracle_attn_rows(_ptr(Q), _ptr(K), _ptr(V), B, H, N, d,
+                                          float(scale), int(bool(causal)),
+                                          bh.ctypes.data_as(_lp), qi.ctypes.data_as(_lp),
+                                          n, _ptr(O), _ptr(lse)),
+               "attn_rows")
+        return O, lse
+
+    def online_row_trace(self, x, bc: int):
+        """Online softmax state (m, l) after each block of bc scores of one row
+        (Lesson 22, sections 18-20 and 33)."""
+        x = _f64(x).ravel()
+        nb = (x.shape[0] + bc - 1) // bc if bc >= 1 else 0
+        m = np.empty((nb,), dtype=np.float64)
+        l = np.empty((nb,), dtype=np.float64)
+        _check(self._lib.oracle_online_row_trace(_ptr(x), x.shape[0], int(bc),
+                                                 _ptr(m), _ptr(l)), "online_row_trace")
+        return m, l
+
+    def attn_online(self, Q, K, V, scale: float, causal: bool, br: int, bc: int):
+        """Tiled online attention with query blocks of br rows and key blocks of
+        bc (Lesson 22, sections 21-24 and 32).  Self-check of the recurrence."""
+        Q, K, V = self._attn_shapes(Q, K, V)
+        B, H, N, d = Q.shape
+        O = np.empty_like(Q)
+        lse = np.empty((B, H, N), dtype=np.float64)
+        _check(self._lib.oracle_attn_online(_ptr(Q), _ptr(K), _ptr(V), _ptr(O),
+                                            _ptr(lse), B, H, N, d, float(scale),
+                                            int(bool(causal)), int(br), int(bc)),
+               "attn_online")
+        return O, lse
+
+
+_default: Oracle | None = None
+
+
+def default() -> Oracle:
+    """The oracle built from the committed ``oracle.c`` (built on first use)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build
+            _build.build()
+        _default = Oracle(LIB_PATH)
+    return _default
+
+
+def num_threads() -> int:
+    return default().num_threads()
+
+
+def row_softmax(x):
+    return default().row_softmax(x)
+
+
+def attn_fwd(Q, K, V, scale, causal):
+    return default().attn_fwd(Q, K, V, scale, causal)
+
+
+def attn_rows(Q, K, V, scale, causal, bh, qi):
+    return default().attn_rows(Q, K, V, scale, causal, bh, qi)
+
+
+def online_row_trace(x, bc):
+    return default().online_row_trace(x, bc)
+
+
+def attn_online(Q, K, V, scale, causal, br, bc):
+    return default().attn_online(Q, K, V, scale, causal, br, bc)

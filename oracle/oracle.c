@@ -1,0 +1,331 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle for exact attention forward and
+ * the numerically stable row softmax.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+ * its Python binding) links, loads or calls this file.  Only the tests, the
+ * smoke check and the benchmark's CPU-baseline leg use it.  It shares no code,
+ * header, table or constant with the GPU kernels.
+ *
+ * Every routine works in IEEE binary64 with plain loops in the order the
+ * pages state; no blocking, fusion or reordering is added.  OpenMP only
+ * distributes independent rows over threads; the arithmetic of each output
+ * element is serial and identical for any thread count.
+ *
+ * Sources (web pages; title, then the section the code follows):
+ *  [L22]  "Lesson 22: why softmax is hard to make efficient, and how
+ *         FlashAttention reduces memory traffic" (lincklin.cn).
+ *  [FUS]  "Understanding operator fusion through FlashAttention" (jokeuncle).
+ *  [GEN]  "Moving less: four generations of FlashAttention" (chengshu-blog).
+ *
+ * Layouts: Q, K, V, O are contiguous [B][H][N][d] row-major; lse is [B][H][N];
+ * x and y of the row softmax are [B][N].  All buffers are host memory owned by
+ * the caller.  Return value: 0 on success, -1 on a bad argument, -2 when a
+ * scratch allocation fails.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Number of OpenMP threads a parallel region here will use (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------ *
+ * Row softmax, three passes over one row ([L22] sections 2 and 3):
+ *   pass 1  m = max_j x_j
+ *   pass 2  s = sum_j exp(x_j - m)
+ *   pass 3  y_j = exp(x_j - m) / s
+ * Subtracting the row maximum keeps every exponent <= 0, so no term
+ * overflows ([L22] section 2, shift invariance).
+ * ------------------------------------------------------------------------ */
+static void softmax_row(const double *x, double *y, long n)
+{
+    double m = -INFINITY;
+    for (long j = 0; j < n; ++j)
+        if (x[j] > m) m = x[j];
+    double s = 0.0;
+    for (long j = 0; j < n; ++j)
+        s += exp(x[j] - m);
+    for (long j = 0; j < n; ++j)
+        y[j] = exp(x[j] - m) / s;
+}
+
+int oracle_row_softmax(const double *x, double *y, long B, long N)
+{
+    if (B < 0 || N < 0) return -1;
+    if (B == 0 || N == 0) return 0;
+    if (!x || !y) return -1;
+    long b;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (b = 0; b < B; ++b)
+        softmax_row(x + b * N, y + b * N, N);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ *
+ * Exact attention for one query row i of one (batch, head) slice, by the
+ * three-kernel dataflow that the fused method avoids ([L22] sections 12-14
+ * and 25; [FUS] "naive model" and "plain attention dataflow"):
+ *   pass 1  s_j = scale * sum_k q_k K_jk  for every key j; under the causal
+ *           mask a key j > i is set to -inf without computing its product
+ *           ([L22] section 34);
+ *   pass 2  m = max_j s_j,  p_j = exp(s_j - m),  l = sum_j p_j,  p_j /= l;
+ *   pass 3  o = sum_j p_j V_j,  lse = m + ln l  ([GEN] 2.4: L = m + log l).
+ * The score row s and probability row p are materialised in full (n values
+ * each).  A row that sees no key (m = -inf) gets o = 0 and lse = -inf; square
+ * causal attention never produces one, since key i is visible to query i.
+ * ------------------------------------------------------------------------ */
+static void attn_row(const double *q, const double *K, const double *V,
+                     long n, long d, double scale, long visible,
+                     double *s, double *p, double *o, double *lse)
+{
+    for (long j = 0; j < n; ++j) {
+        if (j >= visible) { s[j] = -INFINITY; continue; }
+        const double *k = K + j * d;
+        double dot = 0.0;
+        for (long t = 0; t < d; ++t) dot += q[t] * k[t];
+        s[j] = scale * dot;
+    }
+    double m = -INFINITY;
+    for (long j = 0; j < n; ++j)
+        if (s[j] > m) m = s[j];
+    for (long t = 0; t < d; ++t) o[t] = 0.0;
+    if (m == -INFINITY) { *lse = -INFINITY; return; }
+    double l = 0.0;
+    for (long j = 0; j < n; ++j) {
+        p[j] = exp(s[j] - m);      /* exp(-inf) = 0: masked keys get weight 0 */
+        l += p[j];
+    }
+    for (long j = 0; j < n; ++j) p[j] /= l;
+    for (long j = 0; j < n; ++j) {
+        if (p[j] == 0.0) continue;  /* adds exactly +0.0 to every o[t] */
+        const double *v = V + j * d;
+        for (long t = 0; t < d; ++t) o[t] += p[j] * v[t];
+    }
+    *lse = m + log(l);
+}
+
+static int attn_args_ok(const void *Q, const void *K, const void *V,
+                        const void *O, const void *lse,
+                        long B, long H, long N, long d)
+{
+    if (B < 0 || H < 0 || N < 0 || d < 1) return 0;
+    if (B * H * N == 0) return 1;
+    return Q && K && V && O && lse;
+}
+
+/* Full forward over every (b, h, i): O [B][H][N][d], lse [B][H][N]. */
+int oracle_attn_fwd(const double *Q, const double *K, const double *V,
+                    double *O, double *lse, long B, long H, long N, long d,
+                    double scale, int causal)
+{
+    if (!attn_args_ok(Q, K, V, O, lse, B, H, N, d)) return -1;
+    long total = B * H * N;
+    if (total == 0) return 0;
+    int failed = 0;
+#pragma omp parallel reduction(|| : failed)
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        double *p = (double *)malloc(sizeof(double) * (size_t)N);
+        if (!s || !p) {
+            failed = 1;
+        } else {
+            long r;
+#pragma omp for schedule(dynamic, 8)
+            for (r = 0; r < total; ++r) {
+                long bh = r / N, i = r % N;
+                const double *base_k = K + bh * N * d;
+                const double *base_v = V + bh * N * d;
+                long visible = causal ? i + 1 : N;
+                attn_row(Q + r * d, base_k, base_v, N, d, scale, visible,
+                         s, p, O + r * d, lse + r);
+            }
+        }
+        free(s);
+        free(p);
+    }
+    return failed ? -2 : 0;
+}
+
+/* The same definition for a list of rows only: row r of the output is query
+ * index qi[r] of slice bh[r] (bh = b*H + h).  Used where the full tensor is
+ * too large for the oracle to finish in seconds; O_rows is [nrows][d]. */
+int oracle_attn_rows(const double *Q, const double *K, const double *V,
+                     long B, long H, long N, long d, double scale, int causal,
+                     const long *bh, const long *qi, long nrows,
+                     double *O_rows, double *lse_rows)
+{
+    if (!attn_args_ok(Q, K, V, O_rows, lse_rows, B, H, N, d) || nrows < 0)
+        return -1;
+    if (nrows == 0) return 0;
+    if (!bh || !qi) return -1;
+    for (long r = 0; r < nrows; ++r)
+        if (bh[r] < 0 || bh[r] >= B * H || qi[r] < 0 || qi[r] >= N) return -1;
+    int failed = 0;
+#pragma omp parallel reduction(|| : failed)
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        double *p = (double *)malloc(sizeof(double) * (size_t)N);
+        if (!s || !p) {
+            failed = 1;
+        } else {
+            long r;
+#pragma omp for schedule(dynamic, 1)
+            for (r = 0; r < nrows; ++r) {
+                long slice = bh[r], i = qi[r];
+                long visible = causal ? i + 1 : N;
+                attn_row(Q + (slice * N + i) * d, K + slice * N * d,
+                         V + slice * N * d, N, d, scale, visible,
+                         s, p, O_rows + r * d, lse_rows + r);
+            }
+        }
+        free(s);
+        free(p);
+    }
+    return failed ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ *
+ * Online softmax over one score row, visited in blocks of bc elements
+ * ([L22] sections 18-20 and 33; [GEN] 2.2).  After block t the state is
+ *   m_t = max(m_{t-1}, max of block t),
+ *   l_t = exp(m_{t-1} - m_t) * l_{t-1} + sum over block t of exp(x - m_t),
+ * starting from m_0 = -inf, l_0 = 0.  The state after each block is written
+ * to m_trace[t], l_trace[t] (ceil(n / bc) entries each).  The first block
+ * would otherwise need exp(-inf - -inf); the correction factor of an empty
+ * history (l = 0) is taken as 0 there.
+ * ------------------------------------------------------------------------ */
+int oracle_online_row_trace(const double *x, long n, long bc,
+                            double *m_trace, double *l_trace)
+{
+    if (n < 0 || bc < 1) return -1;
+    if (n == 0) return 0;
+    if (!x || !m_trace || !l_trace) return -1;
+    double m = -INFINITY, l = 0.0;
+    for (long t0 = 0, t = 0; t0 < n; t0 += bc, ++t) {
+        long t1 = t0 + bc < n ? t0 + bc : n;
+        double block_max = -INFINITY;
+        for (long j = t0; j < t1; ++j)
+            if (x[j] > block_max) block_max = x[j];
+        double m_new = m > block_max ? m : block_max;
+        double correction = (m == -INFINITY) ? 0.0 : exp(m - m_new);
+        double block_sum = 0.0;
+        if (m_new != -INFINITY)
+            for (long j = t0; j < t1; ++j) block_sum += exp(x[j] - m_new);
+        l = correction * l + block_sum;
+        m = m_new;
+        m_trace[t] = m;
+        l_trace[t] = l;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ *
+ * Tiled online attention ([L22] sections 21-24 and 32; [GEN] 2.2-2.3 with
+ * the deferred normalisation of [GEN] 3.2).  For each block of br query
+ * rows the keys are visited in blocks of bc; each row keeps a running
+ * maximum m, denominator l and unnormalised output a:
+ *   S     = scale * Q_i K_j^T               (masked entries -inf)
+ *   m_new = max(m, row max of S)
+ *   P     = exp(S - m_new)
+ *   c     = exp(m - m_new)
+ *   l     = c * l + row sum of P
+ *   a     = c * a + P V_j
+ *   m     = m_new
+ * and at the end o = a / l, lse = m + ln l.  This exists only so the tests
+ * can show that the recurrence reaches the three-pass result; it is never
+ * compared with the GPU.
+ * ------------------------------------------------------------------------ */
+int oracle_attn_online(const double *Q, const double *K, const double *V,
+                       double *O, double *lse, long B, long H, long N, long d,
+                       double scale, int causal, long br, long bc)
+{
+    if (!attn_args_ok(Q, K, V, O, lse, B, H, N, d) || br < 1 || bc < 1)
+        return -1;
+    if (B * H * N == 0) return 0;
+    long nqb = (N + br - 1) / br;
+    long units = B * H * nqb;
+    int failed = 0;
+#pragma omp parallel reduction(|| : failed)
+    {
+        double *m = (double *)malloc(sizeof(double) * (size_t)br);
+        double *l = (double *)malloc(sizeof(double) * (size_t)br);
+        double *a = (double *)malloc(sizeof(double) * (size_t)(br * d));
+        double *S = (double *)malloc(sizeof(double) * (size_t)(br * bc));
+        if (!m || !l || !a || !S) {
+            failed = 1;
+        } else {
+            long u;
+#pragma omp for schedule(dynamic, 1)
+            for (u = 0; u < units; ++u) {
+                long slice = u / nqb, i0 = (u % nqb) * br;
+                long i1 = i0 + br < N ? i0 + br : N, rows = i1 - i0;
+                const double *Qs = Q + slice * N * d;
+                const double *Ks = K + slice * N * d;
+                const double *Vs = V + slice * N * d;
+                for (long r = 0; r < rows; ++r) {
+                    m[r] = -INFINITY;
+                    l[r] = 0.0;
+                    for (long t = 0; t < d; ++t) a[r * d + t] = 0.0;
+                }
+                for (long j0 = 0; j0 < N; j0 += bc) {
+                    long j1 = j0 + bc < N ? j0 + bc : N, cols = j1 - j0;
+                    for (long r = 0; r < rows; ++r) {
+                        long i = i0 + r;
+                        for (long c = 0; c < cols; ++c) {
+                            long j = j0 + c;
+                            if (causal && j > i) { S[r * bc + c] = -INFINITY; continue; }
+                            double dot = 0.0;
+                            for (long t = 0; t < d; ++t)
+                                dot += Qs[i * d + t] * Ks[j * d + t];
+                            S[r * bc + c] = scale * dot;
+                        }
+                        double bmax = -INFINITY;
+                        for (long c = 0; c < cols; ++c)
+                            if (S[r * bc + c] > bmax) bmax = S[r * bc + c];
+                        double m_new = m[r] > bmax ? m[r] : bmax;
+                        if (m_new == -INFINITY) continue;  /* nothing visible yet */
+                        double corr = (m[r] == -INFINITY) ? 0.0 : exp(m[r] - m_new);
+                        double psum = 0.0;
+                        for (long t = 0; t < d; ++t) a[r * d + t] *= corr;
+                        for (long c = 0; c < cols; ++c) {
+                            double pv = exp(S[r * bc + c] - m_new);
+                            psum += pv;
+                            if (pv == 0.0) continue;
+                            const double *v = Vs + (j0 + c) * d;
+                            for (long t = 0; t < d; ++t) a[r * d + t] += pv * v[t];
+                        }
+                        l[r] = corr * l[r] + psum;
+                        m[r] = m_new;
+                    }
+                }
+                for (long r = 0; r < rows; ++r) {
+                    long idx = slice * N + i0 + r;
+                    if (m[r] == -INFINITY) {
+                        for (long t = 0; t < d; ++t) O[idx * d + t] = 0.0;
+                        lse[idx] = -INFINITY;
+                        continue;
+                    }
+                    for (long t = 0; t < d; ++t) O[idx * d + t] = a[r * d + t] / l[r];
+                    lse[idx] = m[r] + log(l[r]);
+                }
+            }
+        }
+        free(m);
+        free(l);
+        free(a);
+        free(S);
+    }
+    return failed ? -2 : 0;
+}

@@ -1,0 +1,385 @@
+"""Pins for the fp64 oracle: checks against what the pages and the mathematics
+fix, never against the oracle itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with
+  * a value a page prints for a worked example (tests/golden, with the page's
+    title and section and a tolerance from its printed digits),
+  * a closed form,
+  * an invariant of softmax / attention,
+  * an independent library routine (torch / scipy in float64), or
+  * brute force on tiny inputs (the naive softmax without max subtraction,
+    and the online recurrence against the three-pass definition).
+``tests/test_oracle.py`` runs every pin on the committed oracle;
+``tests/test_oracle_mutants.py`` plants plausible mistakes in copies of the
+oracle's C source and requires each to fail at least one pin.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+_GOLDEN_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                            "worked_examples.json")
+with open(_GOLDEN_PATH) as _f:
+    GOLDEN = json.load(_f)
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, atol, rtol=0.0, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    assert np.all(np.isfinite(a) == np.isfinite(b)), f"{what}: finiteness differs"
+    fin = np.isfinite(a)
+    assert np.array_equal(a[~fin], b[~fin]), f"{what}: non-finite values differ"
+    err = np.abs(a[fin] - b[fin])
+    bound = atol + rtol * np.abs(b[fin])
+    if err.size and not np.all(err <= bound):
+        k = int(np.argmax(err - bound))
+        raise AssertionError(f"{what}: |{a[fin][k]} - {b[fin][k]}| = {err[k]:.3e} "
+                             f"> {bound[k]:.3e}")
+
+
+def _scores_as_attention(scores, values, causal=False):
+    """A one-dimensional attention problem whose every query row sees the
+    given scores: d = 1, scale = 1, q = 1, k_j = scores[j], v_j = values[j]."""
+    n = len(scores)
+    Q = np.ones((1, 1, n, 1))
+    K = np.asarray(scores, dtype=np.float64).reshape(1, 1, n, 1)
+    V = np.asarray(values, dtype=np.float64).reshape(1, 1, n, 1)
+    return Q, K, V
+
+
+def _rand_attn(rng, B, H, N, d, std=1.0):
+    return (rng.standard_normal((B, H, N, d)) * std,
+            rng.standard_normal((B, H, N, d)),
+            rng.standard_normal((B, H, N, d)))
+
+
+# --------------------------------------------------------------------------
+# Worked examples printed on the pages
+# --------------------------------------------------------------------------
+
+def pin_fusion_naive_three_keys(orc):
+    g = GOLDEN["fusion_naive_three_keys"]
+    p = orc.row_softmax(np.array([g["scores"]]))[0]
+    _close(p, g["printed_probabilities"], g["prob_tol"], what="printed probabilities")
+    Q, K, V = _scores_as_attention(g["scores"], g["values"])
+    O, lse = orc.attn_fwd(Q, K, V, 1.0, False)
+    _close(O[0, 0, :, 0], [g["printed_output"]] * 3, g["output_tol"],
+           what="printed output")
+    # Under the causal mask query 0 sees only key 0: its output is v_0 exactly.
+    Oc, lsec = orc.attn_fwd(Q, K, V, 1.0, True)
+    _close(Oc[0, 0, 0, 0], g["values"][0], 0.0, what="causal row 0")
+    _close(lsec[0, 0, 0], g["scores"][0], 0.0, what="causal row 0 lse")
+    # Query 2 sees every key, so it must match the non-causal row.
+    _close(Oc[0, 0, 2, 0], O[0, 0, 2, 0], 1e-14, what="causal last row")
+
+
+def pin_lesson22_two_blocks(orc):
+    g = GOLDEN["lesson22_two_blocks_2_1_then_4_3"]
+    m, l = orc.online_row_trace(g["scores"], g["block"])
+    _close(m, g["printed_max_after_block"], 0.0, what="running max")
+    e = math.e
+    l1 = 1.0 + e ** -1                         # the page's expression for block 1
+    l2 = e ** -2 * (1.0 + e ** -1) + 1.0 + e ** -1
+    _close(l, [l1, l2], 0.0, 1e-15, what="running denominator")
+    # The page notes the merged value equals the direct four-term sum, i.e. the
+    # full-row denominator: lse of the three-pass definition is m + ln l.
+    Q, K, V = _scores_as_attention(g["scores"], [1.0, 2.0, 3.0, 4.0])
+    _, lse = orc.attn_fwd(Q, K, V, 1.0, False)
+    _close(lse[0, 0, :], [4.0 + math.log(l2)] * 4, 0.0, 1e-15, what="lse")
+
+
+def pin_fusion_two_blocks(orc):
+    g = GOLDEN["fusion_two_blocks_2_1_then_4"]
+    m, l = orc.online_row_trace(g["scores"], g["block"])
+    _close(l[0], g["printed_sum_after_block1"], g["sum1_tol"], what="sum after block 1")
+    # The correction factor is the ratio the old sum was scaled by; recover it
+    # from the trace: l2 = c * l1 + (contribution of block 2, which is 1 here
+    # because block 2 holds only the new maximum).
+    corr = (l[1] - 1.0) / l[0]
+    _close(corr, g["printed_correction"], g["corr_tol"], what="correction")
+    _close(l[1], g["printed_sum_after_block2"], g["sum2_tol"], what="sum after block 2")
+
+
+def pin_four_generations_blocks(orc):
+    g = GOLDEN["four_generations_blocks_1_3_then_2_5"]
+    m, l = orc.online_row_trace(g["scores"], g["block"])
+    _close(m, g["printed_max_after_block"], 0.0, what="running max")
+    _close(l, g["printed_sum_after_block"], g["sum_tol"], what="running denominator")
+    # ... and the two-block result equals the one-shot row (three passes).
+    Q, K, V = _scores_as_attention(g["scores"], [0.0] * 4)
+    _, lse = orc.attn_fwd(Q, K, V, 1.0, False)
+    _close(lse[0, 0, 0], m[-1] + math.log(l[-1]), 0.0, 1e-15, what="full-row lse")
+
+
+def pin_overflow_row(orc):
+    g = GOLDEN["lesson22_overflow_row"]
+    with np.errstate(over="ignore", invalid="ignore"):
+        naive = np.exp(np.array(g["scores"])) / np.sum(np.exp(np.array(g["scores"])))
+    assert np.all(np.isnan(naive)), "the naive formula should give inf/inf = NaN"
+    p = orc.row_softmax(np.array([g["scores"], g["shift_equivalent"]]))
+    assert np.all(np.isfinite(p)), "stable softmax must stay finite"
+    _close(p[0], p[1], 0.0, 1e-15, what="shift invariance")
+    # Closed form of softmax([2,1,0]) = e^{-j} / (1 + e^-1 + e^-2).
+    z = 1.0 + math.exp(-1.0) + math.exp(-2.0)
+    _close(p[0], [1.0 / z, math.exp(-1.0) / z, math.exp(-2.0) / z], 0.0, 1e-15,
+           what="closed form")
+    # The same row reversed and placed among small values: only subtracting the
+    # true maximum (not, say, the first element) keeps every exponent <= 0.
+    q = orc.row_softmax(np.array([[0.0, 998.0, 999.0, 1000.0, -5.0]]))[0]
+    assert np.all(np.isfinite(q)), "stable softmax must stay finite"
+    _close(q[1:4], p[0][::-1], 1e-300, 1e-13, what="reversed overflow row")
+
+
+# --------------------------------------------------------------------------
+# Closed forms
+# --------------------------------------------------------------------------
+
+def pin_falling_row_closed_form(orc):
+    # Row 1000 - j: a geometric sequence, p_j = e^{-j}(1 - e^-1)/(1 - e^-N).
+    for n in (3, 128, 700):
+        x = 1000.0 - np.arange(n, dtype=np.float64)
+        p = orc.row_softmax(x[None, :])[0]
+        j = np.arange(n, dtype=np.float64)
+        ref = np.exp(-j) * (-math.expm1(-1.0)) / (-math.expm1(-float(n)))
+        _close(p, ref, 1e-300, 1e-13, what=f"falling row N={n}")
+
+
+def pin_two_element_logistic(orc):
+    rng = _rng(11)
+    ab = rng.standard_normal((64, 2)) * 10.0
+    p = orc.row_softmax(ab)
+    ref0 = 1.0 / (1.0 + np.exp(ab[:, 1] - ab[:, 0]))
+    _close(p[:, 0], ref0, 0.0, 1e-14, what="logistic")
+    _close(p[:, 1], 1.0 - ref0, 1e-15, 1e-13, what="logistic complement")
+
+
+def pin_uniform_rows(orc):
+    for n in (1, 2, 7, 4096):
+        x = np.full((3, n), -3.25)
+        p = orc.row_softmax(x)
+        _close(p, np.full((3, n), 1.0 / n), 0.0, 1e-15, what=f"uniform N={n}")
+
+
+def pin_attn_zero_keys(orc):
+    rng = _rng(12)
+    B, H, N, d = 2, 3, 37, 5
+    Q, _, V = _rand_attn(rng, B, H, N, d)
+    K = np.zeros_like(Q)
+    O, lse = orc.attn_fwd(Q, K, V, 0.3, False)
+    _close(O, np.broadcast_to(V.mean(axis=2, keepdims=True), O.shape), 1e-14,
+           what="mean of V")
+    _close(lse, np.full(lse.shape, math.log(N)), 1e-14, what="ln N")
+    Oc, lsec = orc.attn_fwd(Q, K, V, 0.3, True)
+    cum = np.cumsum(V, axis=2) / np.arange(1, N + 1).reshape(1, 1, N, 1)
+    _close(Oc, cum, 1e-14, what="running mean of V")
+    _close(lsec, np.broadcast_to(np.log(np.arange(1, N + 1.0)), lsec.shape), 1e-14,
+           what="ln(i+1)")
+
+
+def pin_attn_constant_values(orc):
+    rng = _rng(13)
+    B, H, N, d = 1, 2, 29, 6
+    Q, K, _ = _rand_attn(rng, B, H, N, d, std=3.0)
+    c = rng.standard_normal(d)
+    V = np.broadcast_to(c, (B, H, N, d)).copy()
+    for causal in (False, True):
+        O, _ = orc.attn_fwd(Q, K, V, 0.5, causal)
+        _close(O, V, 1e-14, 1e-14, what=f"constant V causal={causal}")
+
+
+def pin_attn_causal_first_row_and_single_key(orc):
+    rng = _rng(14)
+    B, H, N, d = 2, 2, 9, 4
+    Q, K, V = _rand_attn(rng, B, H, N, d)
+    O, lse = orc.attn_fwd(Q, K, V, 0.7, True)
+    _close(O[:, :, 0, :], V[:, :, 0, :], 0.0, what="causal row 0 output")
+    dot0 = np.einsum("bhd,bhd->bh", Q[:, :, 0, :], K[:, :, 0, :])
+    _close(lse[:, :, 0], 0.7 * dot0, 0.0, 1e-15, what="causal row 0 lse")
+    for causal in (False, True):
+        O1, lse1 = orc.attn_fwd(Q[:, :, :1], K[:, :, :1], V[:, :, :1], 0.7, causal)
+        _close(O1, V[:, :, :1], 0.0, what="N=1 output")
+        _close(lse1[:, :, 0], 0.7 * dot0, 0.0, 1e-15, what="N=1 lse")
+
+
+# --------------------------------------------------------------------------
+# Independent library routines (torch / scipy, float64)
+# --------------------------------------------------------------------------
+
+def pin_softmax_library(orc):
+    import scipy.special
+    import torch
+    rng = _rng(15)
+    for B, N, std in ((5, 1, 1.0), (7, 33, 4.0), (3, 1000, 30.0), (2, 8192, 1.0)):
+        x = rng.standard_normal((B, N)) * std
+        p = orc.row_softmax(x)
+        _close(p, scipy.special.softmax(x, axis=1), 1e-300, 1e-12, what="scipy softmax")
+        _close(p, torch.softmax(torch.from_numpy(x), dim=1).numpy(), 1e-300, 1e-12,
+               what="torch softmax")
+
+
+def _torch_attn(Q, K, V, scale, causal):
+    import torch
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(a)) for a in (Q, K, V))
+    O = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal,
+                                                         scale=scale)
+    S = torch.matmul(q, k.transpose(-1, -2).contiguous()) * scale
+    if causal:
+        n = S.shape[-1]
+        S = S.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+    return O.numpy(), torch.logsumexp(S, dim=-1).numpy()
+
+
+def pin_attn_library(orc):
+    rng = _rng(16)
+    for (B, H, N, d) in ((1, 1, 1, 1), (1, 2, 7, 3), (2, 3, 33, 8), (1, 2, 130, 64),
+                         (1, 1, 257, 128)):
+        Q, K, V = _rand_attn(rng, B, H, N, d, std=2.0)
+        scale = 1.0 / math.sqrt(d)
+        for causal in (False, True):
+            O, lse = orc.attn_fwd(Q, K, V, scale, causal)
+            Ot, lset = _torch_attn(Q, K, V, scale, causal)
+            _close(O, Ot, 1e-12, 1e-12, what=f"sdpa O {B, H, N, d} causal={causal}")
+            _close(lse, lset, 1e-12, 1e-12, what=f"logsumexp {B, H, N, d} causal={causal}")
+
+
+# --------------------------------------------------------------------------
+# Invariants
+# --------------------------------------------------------------------------
+
+def pin_softmax_invariants(orc):
+    rng = _rng(17)
+    x = np.round(rng.standard_normal((6, 301)) * 8.0, 3)
+    p = orc.row_softmax(x)
+    assert np.all(p > 0.0) and np.all(p <= 1.0), "0 < p <= 1"
+    _close(p.sum(axis=1), np.ones(6), 1e-13, what="rows sum to 1")
+    _close(orc.row_softmax(x + 37.0), p, 1e-15, 1e-12, what="shift invariance")
+    perm = rng.permutation(301)
+    _close(orc.row_softmax(x[:, perm]), p[:, perm], 1e-15, 1e-13, what="permutation")
+
+
+def pin_attn_probabilities(orc):
+    # With V = I (N = d) the output row is the probability row itself, which can
+    # be brute-forced by the naive softmax (no max subtraction; scores are small).
+    rng = _rng(18)
+    N = d = 24
+    Q = rng.standard_normal((1, 1, N, d))
+    K = rng.standard_normal((1, 1, N, d))
+    V = np.eye(N).reshape(1, 1, N, d)
+    scale = 0.25
+    S = scale * (Q[0, 0] @ K[0, 0].T)
+    for causal in (False, True):
+        O, _ = orc.attn_fwd(Q, K, V, scale, causal)
+        P = O[0, 0]
+        E = np.exp(S)
+        if causal:
+            E = np.tril(E)
+            assert np.all(P[np.triu_indices(N, 1)] == 0.0), "masked probability must be 0"
+        _close(P, E / E.sum(axis=1, keepdims=True), 1e-15, 1e-13,
+               what=f"naive softmax causal={causal}")
+        _close(P.sum(axis=1), np.ones(N), 1e-14, what="rows of P sum to 1")
+
+
+def pin_attn_key_shift(orc):
+    # Adding u to every key adds scale*q_i.u to every score of row i: P and O
+    # are unchanged and lse_i moves by exactly that amount.
+    rng = _rng(19)
+    B, H, N, d = 1, 2, 40, 8
+    Q, K, V = _rand_attn(rng, B, H, N, d)
+    u = rng.standard_normal(d)
+    scale = 1.0 / math.sqrt(d)
+    for causal in (False, True):
+        O, lse = orc.attn_fwd(Q, K, V, scale, causal)
+        O2, lse2 = orc.attn_fwd(Q, K + u, V, scale, causal)
+        _close(O2, O, 1e-12, 1e-12, what="O under key shift")
+        _close(lse2, lse + scale * (Q @ u), 1e-12, 1e-12, what="lse under key shift")
+
+
+def pin_attn_permutations(orc):
+    rng = _rng(20)
+    B, H, N, d = 1, 1, 31, 5
+    Q, K, V = _rand_attn(rng, B, H, N, d)
+    O, lse = orc.attn_fwd(Q, K, V, 0.4, False)
+    pk = rng.permutation(N)
+    O2, lse2 = orc.attn_fwd(Q, K[:, :, pk], V[:, :, pk], 0.4, False)
+    _close(O2, O, 1e-13, 1e-13, what="joint key/value permutation")
+    _close(lse2, lse, 1e-13, 1e-13, what="lse under key permutation")
+    pq = rng.permutation(N)
+    O3, lse3 = orc.attn_fwd(Q[:, :, pq], K, V, 0.4, False)
+    _close(O3, O[:, :, pq], 0.0, what="query permutation")
+    _close(lse3, lse[:, :, pq], 0.0, what="lse under query permutation")
+
+
+def pin_attn_slices_independent(orc):
+    rng = _rng(21)
+    B, H, N, d = 2, 3, 17, 4
+    Q, K, V = _rand_attn(rng, B, H, N, d)
+    for causal in (False, True):
+        O, lse = orc.attn_fwd(Q, K, V, 0.6, causal)
+        for b in range(B):
+            for h in range(H):
+                sl = (slice(b, b + 1), slice(h, h + 1))
+                O1, lse1 = orc.attn_fwd(Q[sl], K[sl], V[sl], 0.6, causal)
+                _close(O[sl], O1, 0.0, what="slice output")
+                _close(lse[sl], lse1, 0.0, what="slice lse")
+
+
+def pin_attn_extreme_scores(orc):
+    # Scores of order 1e5: everything stays finite and every output lies in the
+    # convex hull of the value rows (each coordinate within [min V, max V]).
+    rng = _rng(22)
+    B, H, N, d = 1, 1, 50, 8
+    Q, K, V = _rand_attn(rng, B, H, N, d)
+    for causal in (False, True):
+        O, lse = orc.attn_fwd(Q * 1e4, K * 10.0, V, 1.0, causal)
+        assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse))
+        lo = V.min(axis=2, keepdims=True) - 1e-12
+        hi = V.max(axis=2, keepdims=True) + 1e-12
+        assert np.all(O >= lo) and np.all(O <= hi), "output outside the hull of V"
+
+
+# --------------------------------------------------------------------------
+# Brute force: the online recurrence reaches the three-pass result
+# --------------------------------------------------------------------------
+
+def pin_online_equals_three_pass(orc):
+    rng = _rng(23)
+    for N in (1, 2, 3, 5, 8, 17, 33):
+        for d in (1, 2, 3, 8):
+            Q, K, V = _rand_attn(rng, 1, 2, N, d, std=2.5)
+            for causal in (False, True):
+                O, lse = orc.attn_fwd(Q, K, V, 0.8, causal)
+                for br in sorted({1, 2, 3, 5, N}):
+                    for bc in sorted({1, 2, 3, 5, N}):
+                        O2, lse2 = orc.attn_online(Q, K, V, 0.8, causal, br, bc)
+                        _close(O2, O, 1e-12, 1e-12,
+                               what=f"online O N={N} d={d} br={br} bc={bc} c={causal}")
+                        _close(lse2, lse, 1e-12, 1e-12,
+                               what=f"online lse N={N} d={d} br={br} bc={bc} c={causal}")
+
+
+def pin_online_trace_final_state(orc):
+    # For any block size the final (m, l) of the online trace describes the
+    # whole row: m + ln l equals the three-pass lse of the same scores.
+    rng = _rng(24)
+    for n in (1, 4, 9, 64):
+        x = rng.standard_normal(n) * 6.0
+        Q, K, V = _scores_as_attention(x, np.zeros(n))
+        _, lse = orc.attn_fwd(Q, K, V, 1.0, False)
+        for bc in (1, 2, 3, 7, n):
+            m, l = orc.online_row_trace(x, bc)
+            assert m[-1] == x.max(), "final running max must be the row max"
+            _close(m[-1] + math.log(l[-1]), lse[0, 0, 0], 1e-13, 1e-13,
+                   what=f"online trace n={n} bc={bc}")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

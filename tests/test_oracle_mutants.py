@@ -1,0 +1,60 @@
+"""Plant plausible mistakes in copies of the oracle's C source (on the CPU) and
+require every one of them to fail at least one pin.  This is what makes the
+pins a check of the oracle rather than a restatement of it."""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+from oracle import build as oracle_build
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, text in oracle.c, replacement): each is a mistake someone could make.
+MUTANTS = [
+    ("dropped_scale", "s[j] = scale * dot;", "s[j] = dot;"),
+    ("mask_off_by_one", "if (j >= visible) { s[j] = -INFINITY; continue; }",
+     "if (j > visible) { s[j] = -INFINITY; continue; }"),
+    ("wrong_sign_in_exp", "p[j] = exp(s[j] - m);", "p[j] = exp(m - s[j]);"),
+    ("lse_without_max", "*lse = m + log(l);", "*lse = log(l);"),
+    ("q_dot_q", "for (long t = 0; t < d; ++t) dot += q[t] * k[t];",
+     "for (long t = 0; t < d; ++t) dot += q[t] * q[t];"),
+    ("missing_normalisation", "for (long j = 0; j < n; ++j) p[j] /= l;",
+     "for (long j = 0; j < n; ++j) p[j] /= 1.0;"),
+    ("value_without_weight", "for (long t = 0; t < d; ++t) o[t] += p[j] * v[t];",
+     "for (long t = 0; t < d; ++t) o[t] += v[t];"),
+    ("transposed_value_index", "const double *v = V + j * d;",
+     "const double *v = V + (n - 1 - j) * d;"),
+    ("softmax_not_normalised", "y[j] = exp(x[j] - m) / s;", "y[j] = exp(x[j] - m);"),
+    ("softmax_max_is_first", "if (x[j] > m) m = x[j];", "if (j == 0) m = x[j];"),
+    ("online_correction_sign",
+     "double correction = (m == -INFINITY) ? 0.0 : exp(m - m_new);",
+     "double correction = (m == -INFINITY) ? 0.0 : exp(m_new - m);"),
+    ("online_no_accumulator_rescale",
+     "for (long t = 0; t < d; ++t) a[r * d + t] *= corr;",
+     "for (long t = 0; t < d; ++t) a[r * d + t] *= 1.0;"),
+    ("online_causal_off_by_one",
+     "if (causal && j > i) { S[r * bc + c] = -INFINITY; continue; }",
+     "if (causal && j >= i) { S[r * bc + c] = -INFINITY; continue; }"),
+    ("online_denominator_not_rescaled", "l[r] = corr * l[r] + psum;",
+     "l[r] = l[r] + psum;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) == 1, f"mutation site for {name} not unique in oracle.c"
+    src = tmp_path / "oracle_mutant.c"
+    src.write_text(text.replace(old, new))
+    so = oracle_build.build(src=str(src), out=str(tmp_path / "liboracle_mutant.so"))
+    mutant = oracle.Oracle(so)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, RuntimeError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {name}"

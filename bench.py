@@ -1,0 +1,224 @@
+"""Benchmark of the hot path on one MI355X.
+
+One step = one fused attention forward on the causal bf16 workload
+(B=2, H=16 -> B*H = 32, N=4096, d=128, every 64th query row x8) followed by
+one stable row softmax over fp32 [32768, 8192].  Inputs are seeded synthetic
+tensors already resident in HBM.  W untimed warm-up steps, then K timed steps
+between device synchronisations; per-kernel times come from HIP events
+recorded on the stream the kernels are launched on (torch's current stream).
+
+Prints one JSON line:
+  value             attention TFLOPS, counted FLOPs 4*B*H*N^2*d / 2 (causal)
+                    over the mean attention launch time
+  roofline          attention kernel against the bf16 matrix-core peak
+  softmax           row-softmax GB/s (8 algorithmic bytes per element)
+  roofline_softmax  softmax kernel against the HBM peak
+  cpu_baseline      the fp64 oracle on the host cores, on a bounded sample
+                    of the same workload (and its parity on that sample)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOPS & % bf16 MFMA peak (B·H=32,N=4096,d=128); softmax GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+ATTN_SOURCES = ["online_softmax_08_amd/csrc/attn_fwd_bf16.hip",
+                "online_softmax_08_amd/csrc/device_common.h"]
+SOFTMAX_SOURCES = ["online_softmax_08_amd/csrc/row_softmax.hip",
+                   "online_softmax_08_amd/csrc/device_common.h"]
+
+
+def measured_traffic(tag: str, sources) -> float | None:
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, f"{tag}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != source_sha(sources):
+        return None
+    return float(rec["hbm_bytes_per_dispatch"])
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing leg (profiling runs)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy per step (outside the timed "
+                         "region) to calibrate HBM byte counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the kernels shard by batch*head with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import online_softmax_08_amd as osm
+    from online_softmax_08_amd import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wa = inputs.ATTN[inputs.HEADLINE_ATTN]
+    ws = inputs.SOFTMAX[inputs.HEADLINE_SOFTMAX]
+    print(f"# {wa.describe()}", file=sys.stderr, flush=True)
+    print(f"# {ws.describe()}", file=sys.stderr, flush=True)
+    q_cpu, k_cpu, v_cpu = inputs.attn_inputs(wa)
+    x_cpu = inputs.softmax_inputs(ws)
+    q, k, v = q_cpu.to(dev), k_cpu.to(dev), v_cpu.to(dev)
+    x = x_cpu.to(dev)
+    O = torch.empty_like(q)
+    lse = torch.empty((wa.B, wa.H, wa.N), dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    if args.copy_probe:
+        csrc = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        cdst = torch.empty_like(csrc)
+
+    def step():
+        osm.attention(q, k, v, causal=wa.causal, out=O, lse=lse)
+        osm.softmax(x, out=y)
+
+    for _ in range(args.warmup):
+        step()
+        if args.copy_probe:
+            cdst.copy_(csrc)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e0, e1, e2 = ev[i]
+        e0.record()
+        osm.attention(q, k, v, causal=wa.causal, out=O, lse=lse)
+        e1.record()
+        osm.softmax(x, out=y)
+        e2.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if args.copy_probe:
+        for _ in range(K):
+            cdst.copy_(csrc)
+        torch.cuda.synchronize()
+
+    attn_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / K
+    sm_ms = sum(b.elapsed_time(c) for _, b, c in ev) / K
+    attn_tflops = wa.flops / (attn_ms * 1e-3) / 1e12
+    sm_gbs = ws.bytes / (sm_ms * 1e-3) / 1e9
+    # Algorithmic HBM bytes of the attention kernel: Q, K, V read once, O and
+    # lse written once.
+    attn_bytes = 4 * wa.B * wa.H * wa.N * wa.d * 2 + wa.B * wa.H * wa.N * 4
+    traffic_attn = measured_traffic("attn_fwd_bf16_B2H16N4096d128_causal", ATTN_SOURCES)
+    traffic_sm = measured_traffic("row_softmax_32768x8192", SOFTMAX_SOURCES)
+
+    out = {
+        "metric": METRIC,
+        "value": round(attn_tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded randn, resident in HBM)",
+        "config": {"workload": f"{wa.name} + {ws.name}", "B": wa.B, "H": wa.H, "N": wa.N,
+                   "d": wa.d, "causal": wa.causal, "softmax_shape": [ws.B, ws.N],
+                   "seeds": [wa.seed, ws.seed]},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_attn,
+                     "kernel": "attn_fwd_bf16_kernel", "kernel_ms": round(attn_ms, 4),
+                     "flops_per_launch": wa.flops, "algorithmic_bytes": attn_bytes},
+        "softmax": {"value": round(sm_gbs, 1), "unit": "GB/s", "kernel_ms": round(sm_ms, 4)},
+        "roofline_softmax": {"bound": "hbm", "achieved": round(sm_gbs, 1), "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": round(sm_gbs / PEAK_HBM_GBS, 4),
+                             "traffic": traffic_sm, "kernel": "softmax_block_vec4",
+                             "algorithmic_bytes": ws.bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wa, ws, q_cpu, k_cpu, v_cpu, x_cpu, O, lse, y)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(wa, ws, q_cpu, k_cpu, v_cpu, x_cpu, O, lse, y):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same
+    workload, on this host's cores; also report the GPU's max-abs error on
+    that sample."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    n_slices = 16  # of B*H = 32 (batch, head) slices, every query row of each
+    bh = np.repeat(np.arange(n_slices), wa.N)
+    qi = np.tile(np.arange(wa.N), n_slices)
+    Q = q_cpu.reshape(wa.B * wa.H, 1, wa.N, wa.d)[:n_slices].reshape(1, n_slices, wa.N, wa.d)
+    Kc = k_cpu.reshape(wa.B * wa.H, 1, wa.N, wa.d)[:n_slices].reshape(1, n_slices, wa.N, wa.d)
+    Vc = v_cpu.reshape(wa.B * wa.H, 1, wa.N, wa.d)[:n_slices].reshape(1, n_slices, wa.N, wa.d)
+    Qd, Kd, Vd = (t.to(torch.float64).numpy() for t in (Q, Kc, Vc))
+    t0 = time.perf_counter()
+    Oref, lref = oracle.attn_rows(Qd, Kd, Vd, wa.scale, wa.causal, bh, qi)
+    dt = time.perf_counter() - t0
+    flops = n_slices * 4.0 * wa.d * (wa.N * (wa.N + 1) / 2 if wa.causal else wa.N * wa.N)
+    Og = O.reshape(wa.B * wa.H, wa.N, wa.d)[:n_slices].reshape(-1, wa.d).double().cpu().numpy()
+    lg = lse.reshape(wa.B * wa.H, wa.N)[:n_slices].reshape(-1).double().cpu().numpy()
+
+    rows = 512
+    xs = x_cpu[:rows].to(torch.float64).numpy()
+    t1 = time.perf_counter()
+    yref = oracle.row_softmax(xs)
+    dts = time.perf_counter() - t1
+    ys = y[:rows].double().cpu().numpy()
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOPS",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"attention: {n_slices} of {wa.B * wa.H} (batch, head) slices x all {wa.N} "
+                  f"query rows, fp64 three-pass ({dt:.2f} s); softmax: {rows} of {ws.B} rows "
+                  f"({dts:.2f} s)",
+        "seconds": round(dt, 3),
+        "softmax_gbs": round(rows * ws.N * 8 / dts / 1e9, 4),
+        "max_abs_err_O": float(np.max(np.abs(Og - Oref))),
+        "max_abs_err_lse": float(np.max(np.abs(lg - lref))),
+        "max_abs_err_softmax": float(np.max(np.abs(ys - yref))),
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

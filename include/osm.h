@@ -1,0 +1,101 @@
+/*
+ * osm.h -- C ABI of the MI355X (gfx950) online-softmax attention library.
+ *
+ * Two operations, both defined on the source pages:
+ *
+ *  attn_fwd / attn_fwd_f32
+ *    Exact attention forward O = softmax(scale * Q K^T) V for every
+ *    (batch, head), with an optional causal mask, plus the per-row
+ *    logsumexp.  Definition: "Lesson 22: why softmax is hard to make
+ *    efficient, and how FlashAttention reduces memory traffic", sections 12-13
+ *    (the attention product) and 34 (causal mask: key j is hidden from query
+ *    i when j > i); "Moving less: four generations of FlashAttention",
+ *    section 1.2 (S = QK^T / sqrt(d), P = softmax(S), O = PV) and section 2.4
+ *    (the row statistic L = m + log l, natural log, of the scaled scores).
+ *    The computation is the fused, tiled online softmax of Lesson 22,
+ *    sections 21-24 and 32: S and P are never written to memory.
+ *
+ *  row_softmax
+ *    Numerically stable softmax of each row of x [B][N]:
+ *    y[b][j] = exp(x[b][j] - m_b) / sum_t exp(x[b][t] - m_b),
+ *    m_b = max_t x[b][t].  Definition: Lesson 22, sections 2-3.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers (HIP device memory), owned by the
+ *    caller; the library never allocates, frees or retains them.
+ *  - Layouts are contiguous row-major: Q, K, V, O are [B][H][N][d]
+ *    (d fastest), lse is [B][H][N]; x and y are [B][N].
+ *  - Q, K, V, O must be 16-byte aligned (for bf16 also implied by d being 64
+ *    or 128 once the base is aligned).  lse needs 4-byte alignment.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default
+ *    stream.  Every call only enqueues work and returns without
+ *    synchronising; results are ready when the stream reaches that point.
+ *  - Arguments are validated on the host before any HIP call; an invalid call
+ *    enqueues nothing and returns a nonzero osm_status.  A launch failure
+ *    returns OSM_ERR_HIP.  The library keeps no mutable global state except a
+ *    per-device cache of the architecture check, so calls are thread-safe.
+ *  - Empty problems (B, H or N equal to 0) return OSM_OK and enqueue nothing;
+ *    their pointers may then be NULL.
+ */
+#ifndef OSM_H
+#define OSM_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    OSM_OK = 0,
+    OSM_ERR_NULL = 1,     /* a required pointer is NULL                        */
+    OSM_ERR_SIZE = 2,     /* a size is negative or the problem is too large    */
+    OSM_ERR_HEAD_DIM = 3, /* d is not 64 or 128                                */
+    OSM_ERR_SCALE = 4,    /* scale is not finite and > 0                       */
+    OSM_ERR_ALIAS = 5,    /* an output overlaps an input or the other output   */
+    OSM_ERR_ALIGN = 6,    /* a pointer is not aligned as required              */
+    OSM_ERR_DEVICE = 7,   /* the current device is not a gfx950 GPU            */
+    OSM_ERR_HIP = 8       /* the HIP runtime reported an error at launch       */
+} osm_status;
+
+/*
+ * attn_fwd -- bf16 inputs, fp32 accumulation.
+ *   Q, K, V : const bf16 [B][H][N][d]   (bf16 = IEEE binary32 upper half)
+ *   O       : bf16 [B][H][N][d], written with round-to-nearest-even
+ *   lse     : fp32 [B][H][N], lse[i] = max_j s_ij + ln(sum_j exp(s_ij - max_j s_ij))
+ *             over the visible keys j, with s_ij = scale * q_i . k_j
+ *   B, H, N : batch, heads, sequence length (queries = keys = N), >= 0
+ *   d       : head dimension, 64 or 128
+ *   scale   : score scale, finite and > 0 (usually 1/sqrt(d))
+ *   causal  : nonzero hides key j from query i when j > i
+ *   stream  : hipStream_t or NULL
+ * The probabilities are rounded to bf16 before they multiply V (the row sums
+ * use the unrounded fp32 values).  Returns an osm_status.
+ */
+int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* lse,
+             int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * attn_fwd_f32 -- the same operation with fp32 Q, K, V and O (fp32 matrix
+ * cores, fp32 probabilities).  Same arguments and errors as attn_fwd.
+ */
+int attn_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* lse,
+                 int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * row_softmax -- stable softmax of each fp32 row.
+ *   x : const fp32 [B][N];  y : fp32 [B][N]
+ *   y may be exactly x (in place); any other overlap is OSM_ERR_ALIAS.
+ *   Rows must hold finite values.  Any N >= 1 is accepted: rows up to 1024
+ *   elements use one wave per row, up to 32768 one workgroup per
+ *   register-resident row (one read, one write of each element), longer rows
+ *   a two-read online kernel.
+ */
+int row_softmax(const float* x, float* y, int B, int N, void* stream);
+
+/* Static, human-readable text for an osm_status value. */
+const char* osm_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSM_H */

@@ -1,0 +1,16 @@
+"""MI355X (gfx950) fused online-softmax attention forward and stable row softmax.
+
+The computation runs in hand-written HIP kernels inside ``libosm.so`` (built
+by ``online_softmax_08_amd.build``); this package only marshals arguments.
+
+* ``attn_fwd``, ``attn_fwd_f32``, ``row_softmax``, ``osm_status_str`` are the
+  C ABI of include/osm.h under the same names (device pointers as ints).
+* ``attention`` and ``softmax`` take torch tensors on the GPU, allocate the
+  outputs with torch and launch on torch's current stream.
+"""
+from ._abi import (OsmError, attn_fwd, attn_fwd_f32, library_path, osm_status_str,
+                   row_softmax)
+from .ops import attention, softmax
+
+__all__ = ["OsmError", "attn_fwd", "attn_fwd_f32", "row_softmax", "osm_status_str",
+           "library_path", "attention", "softmax"]

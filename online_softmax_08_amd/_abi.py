@@ -1,0 +1,84 @@
+"""ctypes binding of libosm.so: the C ABI of include/osm.h under the same names.
+
+Argument marshalling only: pointers are passed as Python ints (device
+addresses), sizes as ints, the stream as its integer handle (0 = default
+stream).  A nonzero status raises OsmError.  There is no fallback of any kind:
+if the library is missing or fails to load, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libosm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -c 'import __graft_entry__ as g; g.build()' or "
+        "python online_softmax_08_amd/build.py)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+
+_lib.attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]
+_lib.attn_fwd.restype = _i
+_lib.attn_fwd_f32.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]
+_lib.attn_fwd_f32.restype = _i
+_lib.row_softmax.argtypes = [_vp, _vp, _i, _i, _vp]
+_lib.row_softmax.restype = _i
+_lib.osm_status_str.argtypes = [_i]
+_lib.osm_status_str.restype = ctypes.c_char_p
+
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "row_softmax", "osm_status_str")
+
+OSM_OK = 0
+OSM_ERR_NULL = 1
+OSM_ERR_SIZE = 2
+OSM_ERR_HEAD_DIM = 3
+OSM_ERR_SCALE = 4
+OSM_ERR_ALIAS = 5
+OSM_ERR_ALIGN = 6
+OSM_ERR_DEVICE = 7
+OSM_ERR_HIP = 8
+
+
+class OsmError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {osm_status_str(status)} (status {status})")
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def osm_status_str(status: int) -> str:
+    return _lib.osm_status_str(int(status)).decode()
+
+
+def _call(fn: str, *args) -> None:
+    st = getattr(_lib, fn)(*args)
+    if st != OSM_OK:
+        raise OsmError(fn, st)
+
+
+def attn_fwd(Q: int, K: int, V: int, O: int, lse: int, B: int, H: int, N: int, d: int,
+             scale: float, causal: bool, stream: int = 0) -> None:
+    """bf16 attention forward; see include/osm.h."""
+    _call("attn_fwd", Q, K, V, O, lse, B, H, N, d, scale, int(bool(causal)), stream)
+
+
+def attn_fwd_f32(Q: int, K: int, V: int, O: int, lse: int, B: int, H: int, N: int, d: int,
+                 scale: float, causal: bool, stream: int = 0) -> None:
+    """fp32 attention forward; see include/osm.h."""
+    _call("attn_fwd_f32", Q, K, V, O, lse, B, H, N, d, scale, int(bool(causal)), stream)
+
+
+def row_softmax(x: int, y: int, B: int, N: int, stream: int = 0) -> None:
+    """Stable row softmax of fp32 [B, N]; see include/osm.h."""
+    _call("row_softmax", x, y, B, N, stream)

@@ -1,0 +1,127 @@
+// api.hip -- the C ABI (include/osm.h): host-side argument validation, the
+// gfx950 device check and dispatch to the kernels.  Validation runs before any
+// HIP call, so a rejected call touches neither the device nor the stream.
+
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "kernels.h"
+#include "osm.h"
+
+namespace {
+
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes)
+{
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return abytes && bbytes && a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return OSM_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return OSM_ERR_DEVICE;
+    int state = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return OSM_ERR_HIP;
+        state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_ok[dev].store(state, std::memory_order_relaxed);
+    }
+    return state == 1 ? OSM_OK : OSM_ERR_DEVICE;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? OSM_OK : OSM_ERR_HIP; }
+
+// Shared validation of attn_fwd / attn_fwd_f32.  *work is set to false for an
+// empty problem (valid, nothing to launch).
+int validate_attn(const void* Q, const void* K, const void* V, const void* O, const float* lse,
+                  int B, int H, int N, int d, float scale, size_t elem, bool* work)
+{
+    *work = false;
+    if (B < 0 || H < 0 || N < 0) return OSM_ERR_SIZE;
+    if (d != 64 && d != 128) return OSM_ERR_HEAD_DIM;
+    if (!(std::isfinite(scale) && scale > 0.f)) return OSM_ERR_SCALE;
+    if (B == 0 || H == 0 || N == 0) return OSM_OK;
+    const long long bh = (long long)B * H;
+    // Work-group ids (bh * query blocks of at least 128 rows) and row indices
+    // must fit in 32 bits.
+    if (bh > INT_MAX || bh * ((N + 127) / 128) > INT_MAX) return OSM_ERR_SIZE;
+    if (!Q || !K || !V || !O || !lse) return OSM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(lse, 4))
+        return OSM_ERR_ALIGN;
+    const size_t tbytes = (size_t)bh * N * d * elem, lbytes = (size_t)bh * N * sizeof(float);
+    if (overlaps(O, tbytes, Q, tbytes) || overlaps(O, tbytes, K, tbytes) ||
+        overlaps(O, tbytes, V, tbytes) || overlaps(lse, lbytes, Q, tbytes) ||
+        overlaps(lse, lbytes, K, tbytes) || overlaps(lse, lbytes, V, tbytes) ||
+        overlaps(lse, lbytes, O, tbytes))
+        return OSM_ERR_ALIAS;
+    *work = true;
+    return OSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H,
+             int N, int d, float scale, int causal, void* stream)
+{
+    bool work = false;
+    int st = validate_attn(Q, K, V, O, lse, B, H, N, d, scale, 2, &work);
+    if (st != OSM_OK || !work) return st;
+    if ((st = check_device()) != OSM_OK) return st;
+    return finish(osm::launch_attn_fwd_bf16(Q, K, V, O, lse, B * H, N, d, scale, causal != 0,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* lse, int B,
+                 int H, int N, int d, float scale, int causal, void* stream)
+{
+    bool work = false;
+    int st = validate_attn(Q, K, V, O, lse, B, H, N, d, scale, 4, &work);
+    if (st != OSM_OK || !work) return st;
+    if ((st = check_device()) != OSM_OK) return st;
+    return finish(osm::launch_attn_fwd_f32(Q, K, V, O, lse, B * H, N, d, scale, causal != 0,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int row_softmax(const float* x, float* y, int B, int N, void* stream)
+{
+    if (B < 0 || N < 0) return OSM_ERR_SIZE;
+    if (B == 0 || N == 0) return OSM_OK;
+    if (!x || !y) return OSM_ERR_NULL;
+    if (!aligned(x, 4) || !aligned(y, 4)) return OSM_ERR_ALIGN;
+    const size_t bytes = (size_t)B * N * sizeof(float);
+    if (x != y && overlaps(x, bytes, y, bytes)) return OSM_ERR_ALIAS;
+    int st = check_device();
+    if (st != OSM_OK) return st;
+    return finish(osm::launch_row_softmax(x, y, B, N, static_cast<hipStream_t>(stream)));
+}
+
+const char* osm_status_str(int status)
+{
+    switch (status) {
+    case OSM_OK: return "ok";
+    case OSM_ERR_NULL: return "a required pointer is NULL";
+    case OSM_ERR_SIZE: return "a size is negative or the problem is too large";
+    case OSM_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
+    case OSM_ERR_SCALE: return "scale must be finite and > 0";
+    case OSM_ERR_ALIAS: return "an output buffer overlaps another buffer";
+    case OSM_ERR_ALIGN: return "a pointer is not aligned as required";
+    case OSM_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
+    case OSM_ERR_HIP: return "the HIP runtime reported an error";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

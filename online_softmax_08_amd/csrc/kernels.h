@@ -1,0 +1,24 @@
+// kernels.h -- internal launch entry points of the HIP kernels (host side).
+// Arguments are validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace osm {
+
+// Row softmax dispatch thresholds: wave-per-row up to this N, then one
+// workgroup per register-resident row, then the two-read online kernel.
+constexpr int kSoftmaxWaveMaxN = 1024;
+constexpr int kSoftmaxBlockMaxN = 32768;
+
+hipError_t launch_row_softmax(const float* x, float* y, int B, int N, hipStream_t stream);
+
+// Q, K, V, O: [B*H][N][d] row-major; lse: [B*H][N].  d is 64 or 128.
+hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, void* O,
+                                float* lse, int BH, int N, int d, float scale, bool causal,
+                                hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const float* Q, const float* K, const float* V, float* O,
+                               float* lse, int BH, int N, int d, float scale, bool causal,
+                               hipStream_t stream);
+
+}  // namespace osm

@@ -1,0 +1,248 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle on
+the same seeded inputs, element by element.
+
+Tolerances (max-abs over every compared element): fp32 paths 1e-5 on O, lse
+and softmax outputs; bf16 attention 2e-2 on O and 1e-3 on lse.  Workloads the
+oracle finishes in seconds are compared in full; the large ones are run at
+full size in the launch configuration the benchmark times and compared on
+sampled rows (every row the oracle computes is compared in full), plus
+properties that hold at any size.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from online_softmax_08_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 1e-3)}
+
+
+@pytest.fixture(scope="module")
+def osm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import online_softmax_08_amd
+    return online_softmax_08_amd
+
+
+def _gpu_attn(osm, q, k, v, causal, scale=None):
+    dev = torch.device("cuda:0")
+    O, lse = osm.attention(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return O.to(torch.float64).cpu().numpy(), lse.to(torch.float64).cpu().numpy()
+
+
+def _maxabs(a, b):
+    if a.size == 0:
+        return 0.0
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+def _check_full(osm, q, k, v, causal, dtype, label, scale=None):
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    O, lse = _gpu_attn(osm, q, k, v, causal, scale)
+    Oref, lref = oracle.attn_fwd(q, k, v, scale, causal)
+    eo, el = _maxabs(O, Oref), _maxabs(lse, lref)
+    to, tl = TOL[dtype]
+    print(f"{label}: max|dO|={eo:.3e} (tol {to}) max|dlse|={el:.3e} (tol {tl})", flush=True)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse))
+    assert eo <= to and el <= tl, label
+    return O, lse
+
+
+def _sample_rows(w, rng, n_slices=8, n_random=16):
+    BH, N = w.B * w.H, w.N
+    slices = sorted({0, BH - 1, *rng.choice(BH, size=min(BH, n_slices - 2), replace=False).tolist()})
+    fixed = [0, 1, 2, 31, 32, 63, 64, 65, 127, 128, 255, 256, 257, N // 2, N - 65, N - 64, N - 2, N - 1]
+    bh, qi = [], []
+    for s in slices:
+        rows = sorted({r for r in fixed if 0 <= r < N} |
+                      set(rng.choice(N, size=n_random, replace=False).tolist()))
+        bh += [s] * len(rows)
+        qi += rows
+    return np.array(bh), np.array(qi)
+
+
+# ----------------------------------------------------------------- attention --
+
+@pytest.mark.parametrize("name", ["attn_f32_B1H1N128d64", "attn_bf16_B2H8N1024d64"])
+def test_attn_workload_full(osm, name):
+    w = inputs.ATTN[name]
+    q, k, v = inputs.attn_inputs(w)
+    print(w.describe(), flush=True)
+    _check_full(osm, q, k, v, w.causal, w.dtype, name)
+
+
+@pytest.mark.parametrize("name", ["attn_bf16_B4H16N2048d128",
+                                  "attn_bf16_B2H16N4096d128_causal_x8rows",
+                                  "attn_bf16_B1H32N8192d128_causal"])
+def test_attn_workload_sampled(osm, name):
+    w = inputs.ATTN[name]
+    print(w.describe(), flush=True)
+    q, k, v = inputs.attn_inputs(w)
+    O, lse = _gpu_attn(osm, q, k, v, w.causal, w.scale)
+    # Properties at full size: finite everywhere; every output row is a convex
+    # combination of value rows, so it lies within each column's [min, max].
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse))
+    vf = v.to(torch.float32)
+    lo = vf.amin(dim=2, keepdim=True).numpy() - 2e-2
+    hi = vf.amax(dim=2, keepdim=True).numpy() + 2e-2
+    assert np.all(O >= lo) and np.all(O <= hi)
+    # Sampled rows against the oracle, including the x8 rows (multiples of 64).
+    rng = np.random.default_rng(w.seed)
+    bh, qi = _sample_rows(w, rng)
+    Oref, lref = oracle.attn_rows(q, k, v, w.scale, w.causal, bh, qi)
+    Og = O.reshape(w.B * w.H, w.N, w.d)[bh, qi]
+    lg = lse.reshape(w.B * w.H, w.N)[bh, qi]
+    eo, el = _maxabs(Og, Oref), _maxabs(lg, lref)
+    print(f"{name}: {len(qi)} sampled rows max|dO|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    to, tl = TOL[w.dtype]
+    assert eo <= to and el <= tl
+
+
+EDGE_N = [1, 2, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_attn_edge_shapes(osm, dtype, d, causal):
+    base = inputs.ATTN["attn_bf16_B2H8N1024d64" if dtype == "bf16" else "attn_f32_B1H1N128d64"]
+    for N in EDGE_N:
+        q, k, v = inputs.attn_inputs(base, B=1, H=2, N=N, d=d, seed=base.seed + 1000 + N)
+        _check_full(osm, q, k, v, causal, dtype, f"{dtype} d={d} causal={causal} N={N}")
+
+
+def test_attn_multi_batch_head_slices(osm):
+    # Odd B and H; each slice must match the oracle (no cross-slice mixing).
+    base = inputs.ATTN["attn_bf16_B2H8N1024d64"]
+    for d in (64, 128):
+        q, k, v = inputs.attn_inputs(base, B=3, H=5, N=200, d=d, seed=77)
+        for causal in (False, True):
+            _check_full(osm, q, k, v, causal, "bf16", f"B3H5N200 d={d} causal={causal}")
+
+
+def test_attn_rescale_stress(osm):
+    # Scores that rise along the keys force the running maximum to move on every
+    # tile (the rescale path); the first query row's boosted copy gives huge
+    # logits.  Built from grid values so the bf16 inputs are exact.
+    N, d = 700, 128
+    q = torch.zeros(1, 2, N, d)
+    k = torch.zeros(1, 2, N, d)
+    q[..., 0] = 1.0
+    q[:, 1, ::7, 0] = 16.0
+    k[..., 0] = torch.arange(N, dtype=torch.float32) / 32.0
+    g = torch.Generator().manual_seed(5)
+    v = torch.randn(1, 2, N, d, generator=g)
+    q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
+    for causal in (False, True):
+        _check_full(osm, q, k, v, causal, "bf16", f"rising scores causal={causal}")
+        _check_full(osm, q.float(), k.float(), v.float(), causal, "f32",
+                    f"rising scores f32 causal={causal}")
+
+
+def test_attn_constant_values(osm):
+    # All value rows equal to c: O must equal c (up to bf16 rounding of c's
+    # products, here exact because p sums to 1 and c is a small grid value).
+    base = inputs.ATTN["attn_bf16_B2H8N1024d64"]
+    q, k, _ = inputs.attn_inputs(base, B=1, H=2, N=333, d=128, seed=9)
+    c = torch.linspace(-2, 2, 128).bfloat16().float()
+    v = c.expand(1, 2, 333, 128).contiguous().bfloat16()
+    O, _ = _gpu_attn(osm, q, k, v, True, 1.0 / math.sqrt(128))
+    assert _maxabs(O, np.broadcast_to(c.numpy(), O.shape)) <= 2e-2
+
+
+def test_attn_deterministic(osm):
+    w = inputs.ATTN["attn_bf16_B2H16N4096d128_causal_x8rows"]
+    q, k, v = inputs.attn_inputs(w, B=1, H=4, N=1500)
+    dev = torch.device("cuda:0")
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    O1, l1 = osm.attention(q, k, v, causal=True)
+    O2, l2 = osm.attention(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(l1, l2)
+
+
+def test_attn_custom_scale(osm):
+    base = inputs.ATTN["attn_bf16_B2H8N1024d64"]
+    q, k, v = inputs.attn_inputs(base, B=1, H=2, N=190, d=64, seed=3)
+    for causal in (False, True):
+        _check_full(osm, q, k, v, causal, "bf16", f"scale=0.3 causal={causal}", scale=0.3)
+
+
+# ------------------------------------------------------------------- softmax --
+
+def _gpu_softmax(osm, x, inplace=False, offset=0):
+    dev = torch.device("cuda:0")
+    if offset:
+        # Shift the data by `offset` floats inside a larger buffer (misaligned rows).
+        buf = torch.empty(x.numel() + offset, dtype=torch.float32, device=dev)
+        xd = buf[offset:].view(x.shape)
+        xd.copy_(x.to(dev))
+    else:
+        xd = x.to(dev)
+    y = osm.softmax(xd, out=xd if inplace else None)
+    torch.cuda.synchronize()
+    return y.to(torch.float64).cpu().numpy()
+
+
+def test_softmax_small_workload(osm):
+    w = inputs.SOFTMAX["softmax_f32_4x128"]
+    x = inputs.softmax_inputs(w)
+    y = _gpu_softmax(osm, x)
+    e = _maxabs(y, oracle.row_softmax(x))
+    print(f"{w.describe()}: max|dy|={e:.3e}", flush=True)
+    assert np.all(np.isfinite(y)) and e <= 1e-5
+
+
+def test_softmax_large_workload(osm):
+    w = inputs.SOFTMAX["softmax_f32_32768x8192"]
+    x = inputs.softmax_inputs(w)
+    dev = torch.device("cuda:0")
+    y = osm.softmax(x.to(dev))
+    torch.cuda.synchronize()
+    s = y.double().sum(dim=1)
+    assert torch.all(torch.isfinite(y)) and float((s - 1).abs().max()) <= 1e-5
+    rng = np.random.default_rng(w.seed)
+    rows = np.unique(np.concatenate([[0, 1, w.B - 1], rng.choice(w.B, 509, replace=False)]))
+    ys = y[torch.from_numpy(rows).to(dev)].double().cpu().numpy()
+    e = _maxabs(ys, oracle.row_softmax(x[torch.from_numpy(rows)]))
+    print(f"{w.describe()}: {len(rows)} sampled rows max|dy|={e:.3e}", flush=True)
+    assert e <= 1e-5
+
+
+SOFTMAX_N = [1, 2, 3, 4, 5, 63, 64, 65, 127, 128, 129, 1000, 1023, 1024, 1025, 2048, 3001,
+             4096, 4097, 8192, 8193, 12000, 16384, 20000, 32768, 32769, 65536, 100003]
+
+
+@pytest.mark.parametrize("N", SOFTMAX_N)
+def test_softmax_edge_widths(osm, N):
+    w = inputs.SOFTMAX["softmax_f32_4x128"]
+    B = 5 if N <= 65536 else 2
+    x = inputs.softmax_inputs(w, B=B, N=N, seed=w.seed + N)
+    ref = oracle.row_softmax(x)
+    for inplace, offset in ((False, 0), (True, 0), (False, 1)):
+        y = _gpu_softmax(osm, x, inplace=inplace, offset=offset)
+        e = _maxabs(y, ref)
+        assert np.all(np.isfinite(y)) and e <= 1e-5, (N, inplace, offset, e)
+
+
+def test_softmax_extreme_rows(osm):
+    # Huge common offsets, a single dominant element, constant rows.
+    N = 2000
+    x = torch.zeros(4, N)
+    x[0] = 1000.0 - torch.arange(N, dtype=torch.float32)
+    x[1] = -1000.0 + torch.arange(N, dtype=torch.float32) * 0.5
+    x[2, 123] = 80.0
+    x[3] = 3.25
+    y = _gpu_softmax(osm, x)
+    e = _maxabs(y, oracle.row_softmax(x))
+    assert np.all(np.isfinite(y)) and e <= 1e-5

@@ -3,7 +3,8 @@
 hipcc compiles every source in csrc/ for --offload-arch=gfx950 into one
 shared object next to this file.  Packed fp32 VALU instructions are switched
 off for the device code (``-packed-fp32-ops``); the host pass warns that it
-does not know that feature, which is harmless.
+does not know that feature, which is harmless.  ``-fno-honor-nans``: the C ABI
+requires finite inputs, so max operations need not quiet NaN operands.
 """
 from __future__ import annotations
 
@@ -19,6 +20,9 @@ LIB_PATH = os.path.join(_HERE, "libosm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # Inputs are finite by contract; without NaN semantics fmaxf maps straight
+    # to v_max/v_max3 instead of first quieting each operand.
+    "-fno-honor-nans",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]

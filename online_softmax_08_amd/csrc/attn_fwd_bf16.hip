@@ -6,36 +6,51 @@
 //
 // Method: the tiled online softmax of "Lesson 22: why softmax is hard to make
 // efficient, and how FlashAttention reduces memory traffic", sections 21-24
-// and 32 (the update rule of section 22, the causal tile skipping of section
+// and 32 (the merge rule of section 22, the causal tile skipping of section
 // 34), with the refinements of "Moving less: four generations of
-// FlashAttention", chapter 3: the output stays unnormalised until the end
-// (3.2), the grid runs over query-row blocks (3.3), and query rows are split
-// across waves so waves never exchange partial outputs (3.4).  lse = m + ln l
-// is the statistic of section 2.4 of the same page.
+// FlashAttention": the output stays unnormalised until the end (3.2), the
+// grid runs over query-row blocks (3.3), query rows are split across waves so
+// waves never exchange partial outputs (3.4), and the running maximum used as
+// the exponent reference is only moved when it has grown by more than a fixed
+// margin (5.4).  lse = m + ln l is the statistic of section 2.4.
 //
 // gfx950 design:
 //  * Work: one workgroup per (batch*head, block of BR query rows); a wave owns
 //    QT x 32 query rows.  Under the causal mask workgroups are issued longest
 //    first.  Consecutive workgroup ids walk the batch*head index, so when
-//    batch*head is a multiple of 8 every query block of one head lands on the
-//    same XCD (ids are dealt round-robin over the 8 XCDs) and shares its L2.
+//    batch*head is a multiple of 8 all query blocks of one head land on the
+//    same XCD (ids are dealt round-robin over the 8 XCDs) and share its L2.
+//  * Global memory goes through buffer resources: rows past N read as zero
+//    and stores past N are dropped by the hardware range check, so ragged
+//    tails need no branches.
 //  * Q stays in VGPRs as the B operand of S^T = K Q^T for the whole kernel.
-//  * K and V tiles of 64 keys are staged through LDS, double-buffered: the
-//    global loads of tile j+1 are issued before tile j is computed and written
-//    to the other LDS buffer after it, with one barrier per tile.  K rows are
-//    stored with an XOR swizzle of their 16-byte chunks; V is stored
-//    transposed (V^T, keys contiguous) with its own swizzle, so both MFMA A
-//    operands are single 16-byte LDS reads.
+//  * K and V tiles of 64 keys move HBM -> LDS by buffer loads that write LDS
+//    directly (no VGPR staging), double-buffered: tile j+1 is in flight while
+//    tile j is computed, one barrier per tile.  Both tiles stay row-major with
+//    padded rows; each wave load instruction fills 1 KiB of LDS, and every
+//    lane picks the global 16 bytes that belong at its LDS position (lanes
+//    landing on row padding fetch a harmless duplicate).  The tile loop is
+//    unrolled by two, so every LDS read address is a loop-invariant register
+//    plus an immediate.
 //  * S^T puts one query per lane (lane % 32) and 16 keys per lane in each
 //    32x32 accumulator, so the row max and row sum are in-lane reductions plus
-//    one v_permlane32_swap; the row sum is kept per lane and the two halves
-//    are added once at the end.  The K rows are permuted inside each 32-row
-//    MFMA tile so that every accumulator register group of 8 holds 8
-//    consecutive keys: the bf16 probabilities then are, register for
-//    register, the B operand of O^T += V^T P^T -- no shuffles.
-//  * p = 2^(s c - m c) with c = scale log2(e): one FMA and one v_exp_f32.
-//    The accumulator rescale by exp(m_old - m_new) is skipped when no row of
-//    the wave changed its maximum (the factor is then exactly 1).
+//    one v_permlane32_swap; the row sum is kept per lane and the halves are
+//    added once at the end.  K rows are placed in LDS so that each group of 8
+//    accumulator registers holds 8 consecutive keys: the bf16 probabilities
+//    are, register for register, the B operand of O^T += V^T P^T.
+//  * The V^T A operand (8 consecutive keys of one column per lane) comes from
+//    the row-major V tile through ds_read_b64_tr_b16, the gfx950 transposing
+//    LDS read: in each group of 16 lanes, lane 4a + b receives element b of
+//    the 8-byte reads of lanes a, a + 4, a + 8 and a + 12.
+//  * Row pitches (K: d + 8, V: d + 16 elements) make both LDS read patterns
+//    bank-conflict free.
+//  * p = 2^(s c - m c) with c = scale log2(e): one FMA and one v_exp_f32 per
+//    score.  The reference m only moves when some row of the wave has a tile
+//    maximum more than 8 (in log2 units) above it; otherwise every p <= 2^8
+//    and neither l nor the accumulators are touched.  The result is the same
+//    exact quantity: l and the accumulators share the reference.
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -43,46 +58,68 @@
 namespace osm {
 namespace {
 
-constexpr int BC = 64;  // keys per tile
+constexpr int BC = 64;                // keys per tile
+constexpr float kRescaleLog2 = 8.0f;  // move the reference beyond 2^8 growth
 
 typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-// Key row (inside a 32-row MFMA tile) that A-operand row i reads, chosen so
-// that accumulator register r of lane half h ends up holding key
-// 16*(r/8) + 8*h + r%8.  With i = 8g + 4h + t the 32x32 accumulator layout
-// places row i in register 4g + t of half h.
-__device__ __forceinline__ int key_of_row(int i)
+// Inside a 32-key MFMA tile, LDS row i holds key swap_bits23(i) (bits 2 and 3
+// exchanged; the map is its own inverse).  With A-operand row i read by lane
+// i, the 32x32 accumulator layout (row 8g + 4h + t lands in register 4g + t
+// of lane half h) then leaves key 16*(r/8) + 8*h + r%8 in register r of half h.
+__device__ __forceinline__ int swap_bits23(int i)
 {
-    return 16 * (i >> 4) + 8 * ((i >> 2) & 1) + 4 * ((i >> 3) & 1) + (i & 3);
+    return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
-// Swizzle (XOR on 16-byte chunks) of K row r: the 8 lanes that read one
-// column of chunks together see 8 different chunk positions.
-__device__ __forceinline__ int kswz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
-// Swizzle of V^T row d (chunks of 8 keys): consecutive rows, and rows 8 apart,
-// fall on different chunk positions.
-__device__ __forceinline__ int vswz(int d) { return (d + (d >> 3)) & 7; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    // Raw buffer (stride 0): loads at offsets >= bytes return 0, stores there
+    // are dropped.  0x00020000 selects 32-bit data format for untyped access.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane L of the wave writes
+// dst + 16 L.  The builtin sits in a device-only body because clang's host pass
+// otherwise drops the launch stubs of kernels that contain it.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, lds_void_t* dst, uint32_t voff)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
+#endif
+}
 
 template <int D, int QT, int NW>
 struct Cfg {
-    static constexpr int T = NW * 64;           // threads per workgroup
-    static constexpr int BR = NW * QT * 32;     // query rows per workgroup
-    static constexpr int KCH = D / 8;           // 16-byte chunks per K row
-    static constexpr int KPT = BC * KCH / T;    // K chunks staged per thread
-    static constexpr int NVB = (BC / 4) * KCH;  // V blocks of 4 keys x 8 columns
-    static constexpr int VPT = (NVB + T - 1) / T;
-    static constexpr int TILE = BC * D;         // elements of one K (or V) tile
-    static_assert(BC * KCH % T == 0, "K staging must divide evenly");
+    static constexpr int T = NW * 64;         // threads per workgroup
+    static constexpr int BR = NW * QT * 32;   // query rows per workgroup
+    static constexpr int KP = D + 8;          // K row pitch in LDS (elements)
+    static constexpr int VP = D + 16;         // V row pitch in LDS (elements)
+    static constexpr int KCPR = KP / 8;       // 16-byte chunks per K row (last is padding)
+    static constexpr int VCPR = VP / 8;       // 16-byte chunks per V row (last two padding)
+    static constexpr int KTILE_B = BC * KP * 2;
+    static constexpr int VTILE_B = BC * VP * 2;
+    static constexpr int KINST = KTILE_B / 1024;  // 1 KiB wave loads per K tile
+    static constexpr int VINST = VTILE_B / 1024;
+    static constexpr int KPW = (KINST + NW - 1) / NW;  // K loads issued per wave
+    static constexpr int VPW = (VINST + NW - 1) / NW;
+    static constexpr int LDS_B = 2 * (KTILE_B + VTILE_B);
+    static_assert(KTILE_B % 1024 == 0 && VTILE_B % 1024 == 0, "tiles are whole wave loads");
 };
 
-template <int D, int QT, int NW, bool CAUSAL>
-__global__ void __launch_bounds__(NW * 64)
+template <int D, int QT, int NW, int WPE, bool CAUSAL>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, __bf16* __restrict__ O,
                      float* __restrict__ lse, int N, int BH, int nqt, float scale)
 {
     using C = Cfg<D, QT, NW>;
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C::TILE];
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[2][C::TILE];
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_B];
+    // Buffer b: K tile at b * KTILE_B, V tile at 2 * KTILE_B + b * VTILE_B.
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -91,21 +128,22 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int qt = CAUSAL ? nqt - 1 - t : t;
     const int q0 = qt * C::BR;
     const size_t base = (size_t)bh * N * D;
-    const __bf16* Qb = Q + base;
-    const __bf16* Kb = K + base;
-    const __bf16* Vb = V + base;
+    const uint32_t slice_b = (uint32_t)N * D * 2;
     const int qw0 = q0 + wave * QT * 32;  // first query row of this wave
 
     // Q as the B operand of S^T = K Q^T: lane (j, h), k-step kk holds
-    // Q[row][16 kk + 8 h .. +7] of row qw0 + 32 nt + j.
+    // Q[row][16 kk + 8 h .. +7] of row qw0 + 32 nt + j (zero past N).
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, slice_b);
     bf16x8 qf[QT][D / 16];
 #pragma unroll
     for (int nt = 0; nt < QT; ++nt) {
         const int q = qw0 + nt * 32 + j;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            qf[nt][kk] = q < N ? *reinterpret_cast<const bf16x8*>(Qb + (size_t)q * D + kk * 16 + 8 * h)
-                               : bf16x8{};
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(
+                qrs, (uint32_t)(q * D + kk * 16 + 8 * h) * 2, 0, 0);
+            qf[nt][kk] = __builtin_bit_cast(bf16x8, raw);
+        }
     }
 
     f32x16 acc[QT][D / 32];
@@ -113,7 +151,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int nt = 0; nt < QT; ++nt)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) acc[nt][dt] = f32x16{};
-    float m[QT], l[QT];
+    float m[QT], l[QT];  // exponent reference (raw score units) and lane's share of the sum
 #pragma unroll
     for (int nt = 0; nt < QT; ++nt) {
         m[nt] = kNegInf;
@@ -121,219 +159,232 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
     const float c = scale * kLog2e;
 
-    // ---- staging of one K/V tile: global -> registers -> LDS ----
-    u32x4 kreg[C::KPT];
-    u32x4 vreg[C::VPT][4];
-    auto gload = [&](int kt) {
+    // ---- HBM -> LDS tile loads (loop-invariant per-lane source offsets) ----
+    // Wave load i writes LDS chunk positions 64 i .. 64 i + 63 of a tile; the
+    // lane at position p fetches row p / CPR, column chunk p % CPR (padding
+    // chunks re-fetch the row's last real chunk).  K rows are permuted inside
+    // each 32-row group (swap_bits23); V rows keep key order.
+    uint32_t ksrc[C::KPW], vsrc[C::VPW];
+#pragma unroll
+    for (int u = 0; u < C::KPW; ++u) {
+        const int p = (wave + u * NW) * 64 + lane;
+        const int lrow = p / C::KCPR, ch = min(p % C::KCPR, D / 8 - 1);
+        const int row = (lrow & ~31) | swap_bits23(lrow & 31);
+        ksrc[u] = (uint32_t)(row * D + ch * 8) * 2;
+    }
+#pragma unroll
+    for (int u = 0; u < C::VPW; ++u) {
+        const int p = (wave + u * NW) * 64 + lane;
+        const int row = p / C::VCPR, ch = min(p % C::VCPR, D / 8 - 1);
+        vsrc[u] = (uint32_t)(row * D + ch * 8) * 2;
+    }
+    const __bf16* Kb = K + base;
+    const __bf16* Vb = V + base;
+    auto issue = [&](auto bufc, int kt) {
+        constexpr int BUF = decltype(bufc)::value;
         const int kv0 = kt * BC;
+        const uint32_t left = (uint32_t)(N - kv0) * D * 2;  // bytes of this slice from kv0 on
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb + (size_t)kv0 * D, left);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb + (size_t)kv0 * D, left);
 #pragma unroll
-        for (int i = 0; i < C::KPT; ++i) {
-            const int cidx = tid + i * C::T, row = cidx / C::KCH, ch = cidx % C::KCH;
-            const int key = kv0 + row;
-            kreg[i] = key < N ? *reinterpret_cast<const u32x4*>(Kb + (size_t)key * D + ch * 8)
-                              : u32x4{};
+        for (int u = 0; u < C::KPW; ++u) {
+            const int i = wave + u * NW;
+            if (C::KINST % NW == 0 || i < C::KINST)
+                lds_dma16(krs, (lds_void_t*)(smem + BUF * C::KTILE_B + i * 1024), ksrc[u]);
         }
 #pragma unroll
-        for (int b = 0; b < C::VPT; ++b) {
-            const int blk = tid + b * C::T;
-            if (blk < C::NVB) {
-                const int kg = blk / C::KCH, dc = blk % C::KCH;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int key = kv0 + 4 * kg + e;
-                    vreg[b][e] = key < N ? *reinterpret_cast<const u32x4*>(Vb + (size_t)key * D + dc * 8)
-                                         : u32x4{};
-                }
-            }
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < C::KPT; ++i) {
-            const int cidx = tid + i * C::T, row = cidx / C::KCH, ch = cidx % C::KCH;
-            *reinterpret_cast<u32x4*>(&Ks[buf][row * D + ((ch ^ kswz(row)) * 8)]) = kreg[i];
-        }
-#pragma unroll
-        for (int b = 0; b < C::VPT; ++b) {
-            const int blk = tid + b * C::T;
-            if (blk < C::NVB) {
-                const int kg = blk / C::KCH, dc = blk % C::KCH;
-                // vreg[b][e] holds columns 8 dc .. 8 dc + 7 of key 4 kg + e; dword w
-                // packs columns 2w (low half) and 2w + 1 (high half).  Gather the
-                // four keys of one column into 8 bytes of the V^T row.
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t lo01 = __builtin_amdgcn_perm(vreg[b][1][w], vreg[b][0][w], 0x05040100u);
-                    const uint32_t lo23 = __builtin_amdgcn_perm(vreg[b][3][w], vreg[b][2][w], 0x05040100u);
-                    const uint32_t hi01 = __builtin_amdgcn_perm(vreg[b][1][w], vreg[b][0][w], 0x07060302u);
-                    const uint32_t hi23 = __builtin_amdgcn_perm(vreg[b][3][w], vreg[b][2][w], 0x07060302u);
-                    const int d0 = dc * 8 + 2 * w, d1 = d0 + 1;
-                    *reinterpret_cast<u32x2*>(&Vt[buf][d0 * BC + (((kg >> 1) ^ vswz(d0)) * 8) + (kg & 1) * 4]) =
-                        u32x2{lo01, lo23};
-                    *reinterpret_cast<u32x2*>(&Vt[buf][d1 * BC + (((kg >> 1) ^ vswz(d1)) * 8) + (kg & 1) * 4]) =
-                        u32x2{hi01, hi23};
-                }
-            }
+        for (int u = 0; u < C::VPW; ++u) {
+            const int i = wave + u * NW;
+            if (C::VINST % NW == 0 || i < C::VINST)
+                lds_dma16(vrs, (lds_void_t*)(smem + 2 * C::KTILE_B + BUF * C::VTILE_B + i * 1024),
+                          vsrc[u]);
         }
     };
 
-    const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
-    const int ntiles = (kv_end + BC - 1) / BC;
+    // Per-lane LDS read bases.  K A operand: row j of each 32-row group, half
+    // h of each 16-column step.  V^T A operand via the transposing read: in
+    // lane group g = lane / 16 the lane 16 g + 4 e + a reads 4 columns
+    // (16 (g % 2) + 4 a ..) of key row 8 (g / 2) + e (+ 4 for the second
+    // read); lane i of the group then holds column 16 (g % 2) + i for 4 keys.
+    const char* kread = smem + (j * C::KP + 8 * h) * 2;
+    const int g16 = lane >> 4, e4 = (lane >> 2) & 3, a4 = lane & 3;
+    const char* vread = smem + 2 * C::KTILE_B +
+                        ((8 * (g16 >> 1) + e4) * C::VP + 16 * (g16 & 1) + 4 * a4) * 2;
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int buf = kt & 1;
+    auto compute = [&](auto bufc, int kt) {
+        constexpr int BUF = decltype(bufc)::value;
         const int kv0 = kt * BC;
-        const bool more = kt + 1 < ntiles;
-        if (more) gload(kt + 1);
-
         // A wave whose rows all precede the tile's first key sees nothing in it.
-        const bool active = !CAUSAL || kv0 <= qw0 + QT * 32 - 1;
-        if (active) {
-            // ---- S^T = K Q^T for two 32-key MFMA tiles ----
-            f32x16 s[2][QT];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < QT; ++nt) s[mt][nt] = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    const int row = mt * 32 + key_of_row(j);
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        &Ks[buf][row * D + (((2 * kk + h) ^ kswz(row)) * 8)]);
-#pragma unroll
-                    for (int nt = 0; nt < QT; ++nt)
-                        s[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nt][kk], s[mt][nt], 0, 0, 0);
-                }
-            }
+        if (CAUSAL && kv0 > qw0 + QT * 32 - 1) return;
 
-            // ---- mask, online softmax statistics, probabilities ----
-            const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
-            float alpha[QT];
+        // ---- S^T = K Q^T for two 32-key MFMA tiles ----
+        f32x16 s[2][QT];
 #pragma unroll
-            for (int nt = 0; nt < QT; ++nt) {
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < QT; ++nt) s[mt][nt] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    kread + BUF * C::KTILE_B + (mt * 32 * C::KP + kk * 16) * 2);
+#pragma unroll
+                for (int nt = 0; nt < QT; ++nt)
+                    s[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nt][kk], s[mt][nt], 0, 0, 0);
+            }
+        }
+
+        // ---- mask (diagonal / tail tiles only) and tile row maxima ----
+        const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
+        float mx[QT];
+#pragma unroll
+        for (int nt = 0; nt < QT; ++nt) {
+            if (need_mask) {
                 const int q = qw0 + nt * 32 + j;
-                if (need_mask) {
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = kv0 + mt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
-                            if (key >= N || (CAUSAL && key > q)) s[mt][nt][r] = kNegInf;
-                        }
-                }
-                float mx = kNegInf;
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][nt][r]);
-                mx = combine_xor32(mx, MaxOp());
-                const float m_new = fmaxf(m[nt], mx);
-                // Tile 0 holds key 0, visible to every row, so m_new is finite from
-                // the first tile on; the guards only keep -inf - -inf out of exp2.
-                // alpha is exactly 1 when the maximum did not move and 0 for an
-                // empty history (m = -inf).
-                const float mc = (m_new == kNegInf) ? 0.f : m_new * c;
-                alpha[nt] = (m_new == kNegInf) ? 1.f : exp2_hw((m[nt] - m_new) * c);
-                float psum = 0.f;
+                // Keys visible to query q in this tile: kv0 .. lim - 1.
+                const int lim = CAUSAL ? min(N, q + 1) : N;
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float p = exp2_hw(fmaf(s[mt][nt][r], c, -mc));
-                        s[mt][nt][r] = p;
-                        psum += p;
+                        const int key = kv0 + mt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
+                        if (key >= lim) s[mt][nt][r] = kNegInf;
                     }
-                l[nt] = alpha[nt] * l[nt] + psum;
-                m[nt] = m_new;
             }
-            bool rescale = false;
+            float v = kNegInf;
 #pragma unroll
-            for (int nt = 0; nt < QT; ++nt) rescale |= alpha[nt] != 1.0f;
-            if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < QT; ++nt)
-#pragma unroll
-                    for (int dt = 0; dt < D / 32; ++dt) acc[nt][dt] *= alpha[nt];
-            }
+                for (int r = 0; r < 16; r += 2) v = fmaxf(v, fmaxf(s[mt][nt][r], s[mt][nt][r + 1]));
+            mx[nt] = combine_xor32(v, MaxOp());
+        }
 
-            // ---- O^T += V^T P^T over four 16-key steps ----
+        // ---- move the exponent reference only when some row grew past the margin ----
+        bool grow = false;
 #pragma unroll
-            for (int ks = 0; ks < BC / 16; ++ks) {
-                bf16x8 pf[QT];
+        for (int nt = 0; nt < QT; ++nt) grow |= (mx[nt] - m[nt]) * c > kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-                for (int nt = 0; nt < QT; ++nt) {
-                    const f32x16& sv = s[ks >> 1][nt];
-                    const f32x8 p8 = (ks & 1) ? __builtin_shufflevector(sv, sv, 8, 9, 10, 11, 12, 13, 14, 15)
-                                              : __builtin_shufflevector(sv, sv, 0, 1, 2, 3, 4, 5, 6, 7);
-                    pf[nt] = __builtin_convertvector(p8, bf16x8);
-                }
+            for (int nt = 0; nt < QT; ++nt) {
+                const float m_new = fmaxf(m[nt], mx[nt]);
+                // Tile 0 holds key 0, visible to every row, so m_new is finite;
+                // an empty history (m = -inf, l = acc = 0) gets factor 0.  The
+                // guard keeps -inf - -inf out of exp2 all the same.
+                const float alpha = (m_new == kNegInf) ? 1.f : exp2_hw((m[nt] - m_new) * c);
+                l[nt] *= alpha;
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const int d = dt * 32 + j;
-                    const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-                        &Vt[buf][d * BC + (((2 * ks + h) ^ vswz(d)) * 8)]);
-#pragma unroll
-                    for (int nt = 0; nt < QT; ++nt)
-                        acc[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[nt], acc[nt][dt], 0, 0, 0);
-                }
+                for (int dt = 0; dt < D / 32; ++dt) acc[nt][dt] *= alpha;
+                m[nt] = m_new;
             }
         }
 
-        if (more) lstore(buf ^ 1);
+        // ---- probabilities, row sums, O^T += V^T P^T over four 16-key steps ----
+        bf16x8 pf[BC / 16][QT];
+#pragma unroll
+        for (int nt = 0; nt < QT; ++nt) {
+            const float mc = m[nt] * c;
+            float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = exp2_hw(fmaf(s[mt][nt][r], c, -mc));
+                    s[mt][nt][r] = p;
+                    ps[r & 3] += p;
+                }
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const f32x16& sv = s[mt][nt];
+                    const f32x8 p8 = half ? __builtin_shufflevector(sv, sv, 8, 9, 10, 11, 12, 13, 14, 15)
+                                          : __builtin_shufflevector(sv, sv, 0, 1, 2, 3, 4, 5, 6, 7);
+                    pf[2 * mt + half][nt] = __builtin_convertvector(p8, bf16x8);
+                }
+            }
+            l[nt] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < BC / 16; ++ks) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const char* vp = vread + BUF * C::VTILE_B + (16 * ks * C::VP + 32 * dt) * 2;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)vp);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 4 * C::VP * 2));
+                const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int nt = 0; nt < QT; ++nt)
+                    acc[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks][nt], acc[nt][dt], 0, 0, 0);
+            }
+        }
+    };
+
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
+    const int ntiles = (kv_end + BC - 1) / BC;
+
+    issue(B0{}, 0);
+    __syncthreads();  // waits for the tile loads (vmcnt) before publishing
+    for (int kt = 0; kt < ntiles; kt += 2) {
+        // even tile: compute buffer 0 while tile kt + 1 streams into buffer 1
+        if (kt + 1 < ntiles) issue(B1{}, kt + 1);
+        compute(B0{}, kt);
+        __syncthreads();
+        if (kt + 1 >= ntiles) break;
+        // odd tile: compute buffer 1 while tile kt + 2 streams into buffer 0
+        if (kt + 2 < ntiles) issue(B0{}, kt + 2);
+        compute(B1{}, kt + 1);
         __syncthreads();
     }
 
-    // ---- epilogue: O = acc / l in bf16, lse = m scale + ln l ----
+    // ---- epilogue: O = acc / l in bf16 (rows past N dropped), lse = m scale + ln l ----
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(O + base, slice_b);
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lse + (size_t)bh * N, (uint32_t)N * 4);
 #pragma unroll
     for (int nt = 0; nt < QT; ++nt) {
         const int q = qw0 + nt * 32 + j;
         const float l_tot = combine_xor32(l[nt], SumOp());
-        if (q < N) {
-            const float inv = 1.0f / l_tot;
-            __bf16* orow = O + base + (size_t)q * D;
+        const float inv = 1.0f / l_tot;
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 o4 = {acc[nt][dt][4 * g] * inv, acc[nt][dt][4 * g + 1] * inv,
-                                      acc[nt][dt][4 * g + 2] * inv, acc[nt][dt][4 * g + 3] * inv};
-                    *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * g + 4 * h) =
-                        __builtin_convertvector(o4, bf16x4);
-                }
-            if (h == 0) lse[(size_t)bh * N + q] = m[nt] * scale + logf(l_tot);
-        }
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 o4 = {acc[nt][dt][4 * g] * inv, acc[nt][dt][4 * g + 1] * inv,
+                                  acc[nt][dt][4 * g + 2] * inv, acc[nt][dt][4 * g + 3] * inv};
+                const bf16x4 ob = __builtin_convertvector(o4, bf16x4);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ors,
+                                                      (uint32_t)(q * D + dt * 32 + 8 * g + 4 * h) * 2, 0, 0);
+            }
+        if (h == 0)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m[nt] * scale + logf(l_tot)), lrs,
+                                                  (uint32_t)q * 4, 0, 0);
     }
 }
 
-template <int D, int QT, int NW, bool CAUSAL>
+template <int D, int QT, int NW, int WPE, bool CAUSAL>
 hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
                   int N, float scale, hipStream_t stream)
 {
     using C = Cfg<D, QT, NW>;
     const int nqt = (N + C::BR - 1) / C::BR;
     const dim3 grid((unsigned)(nqt * BH)), block(C::T);
-    attn_fwd_bf16_kernel<D, QT, NW, CAUSAL><<<grid, block, 0, stream>>>(
+    attn_fwd_bf16_kernel<D, QT, NW, WPE, CAUSAL><<<grid, block, 0, stream>>>(
         static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
         static_cast<__bf16*>(O), lse, N, BH, nqt, scale);
     return hipGetLastError();
 }
 
-// d = 64: 4 waves x 64 query rows (one wave per SIMD, Q and the output
-// accumulators of 64 rows fit the registers).  d = 128: 8 waves x 32 rows
-// (two waves per SIMD) -- 64 rows per wave would exceed the register file.
+#ifndef OSM_ATTN_VARIANTS
+// 8 waves x 32 query rows per workgroup, two waves per SIMD.
 template <int D, bool CAUSAL>
 hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
                     int N, float scale, hipStream_t stream)
 {
-    if (D == 64) return launch<D, 2, 4, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
-    return launch<D, 1, 8, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
+    return launch<D, 1, 8, 2, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
 }
+#else
+#include OSM_ATTN_VARIANTS
+#endif
 
 }  // namespace
 

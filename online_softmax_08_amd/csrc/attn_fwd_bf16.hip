@@ -58,7 +58,6 @@
 namespace osm {
 namespace {
 
-constexpr int BC = 64;                // keys per tile
 constexpr float kRescaleLog2 = 8.0f;  // move the reference beyond 2^8 growth
 
 typedef __attribute__((ext_vector_type(8))) float f32x8;
@@ -93,8 +92,9 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, lds_void_t*
 #endif
 }
 
-template <int D, int QT, int NW>
+template <int D, int QT, int NW, int BC_>
 struct Cfg {
+    static constexpr int BC = BC_;            // keys per tile
     static constexpr int T = NW * 64;         // threads per workgroup
     static constexpr int BR = NW * QT * 32;   // query rows per workgroup
     static constexpr int KP = D + 8;          // K row pitch in LDS (elements)
@@ -107,19 +107,27 @@ struct Cfg {
     static constexpr int VINST = VTILE_B / 1024;
     static constexpr int KPW = (KINST + NW - 1) / NW;  // K loads issued per wave
     static constexpr int VPW = (VINST + NW - 1) / NW;
-    static constexpr int LDS_B = 2 * (KTILE_B + VTILE_B);
+    static constexpr int LDS_B2 = 2 * (KTILE_B + VTILE_B);      // 2 K + 2 V buffers
     static_assert(KTILE_B % 1024 == 0 && VTILE_B % 1024 == 0, "tiles are whole wave loads");
 };
 
-template <int D, int QT, int NW, int WPE, bool CAUSAL>
+template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, __bf16* __restrict__ O,
                      float* __restrict__ lse, int N, int BH, int nqt, float scale)
 {
-    using C = Cfg<D, QT, NW>;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_B];
-    // Buffer b: K tile at b * KTILE_B, V tile at 2 * KTILE_B + b * VTILE_B.
+    using C = Cfg<D, QT, NW, BC>;
+    constexpr int NMT = BC / 32;  // 32-key MFMA tiles per key tile
+    // Four separate LDS objects (not slices of one array): the compiler can
+    // then prove that the DMA filling one buffer does not alias reads of the
+    // other, and does not stall those reads on the DMA's completion.
+    __shared__ __attribute__((aligned(1024))) char kbuf0[C::KTILE_B];
+    __shared__ __attribute__((aligned(1024))) char kbuf1[C::KTILE_B];
+    __shared__ __attribute__((aligned(1024))) char vbuf0[C::VTILE_B];
+    __shared__ __attribute__((aligned(1024))) char vbuf1[C::VTILE_B];
+    auto kbuf = [&](auto bufc) -> char* { if constexpr (decltype(bufc)::value == 0) return kbuf0; else return kbuf1; };
+    auto vbuf = [&](auto bufc) -> char* { if constexpr (decltype(bufc)::value == 0) return vbuf0; else return vbuf1; };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -180,62 +188,65 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
     const __bf16* Kb = K + base;
     const __bf16* Vb = V + base;
-    auto issue = [&](auto bufc, int kt) {
-        constexpr int BUF = decltype(bufc)::value;
+    auto issue_k = [&](auto bufc, int kt) {
         const int kv0 = kt * BC;
         const uint32_t left = (uint32_t)(N - kv0) * D * 2;  // bytes of this slice from kv0 on
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb + (size_t)kv0 * D, left);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb + (size_t)kv0 * D, left);
 #pragma unroll
         for (int u = 0; u < C::KPW; ++u) {
             const int i = wave + u * NW;
             if (C::KINST % NW == 0 || i < C::KINST)
-                lds_dma16(krs, (lds_void_t*)(smem + BUF * C::KTILE_B + i * 1024), ksrc[u]);
+                lds_dma16(krs, (lds_void_t*)(kbuf(bufc) + i * 1024), ksrc[u]);
         }
+    };
+    auto issue_v = [&](auto bufc, int kt) {
+        const int kv0 = kt * BC;
+        const uint32_t left = (uint32_t)(N - kv0) * D * 2;
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb + (size_t)kv0 * D, left);
 #pragma unroll
         for (int u = 0; u < C::VPW; ++u) {
             const int i = wave + u * NW;
             if (C::VINST % NW == 0 || i < C::VINST)
-                lds_dma16(vrs, (lds_void_t*)(smem + 2 * C::KTILE_B + BUF * C::VTILE_B + i * 1024),
-                          vsrc[u]);
+                lds_dma16(vrs, (lds_void_t*)(vbuf(bufc) + i * 1024), vsrc[u]);
         }
     };
+    auto issue = [&](auto bufc, int kt) {
+        issue_k(bufc, kt);
+        issue_v(bufc, kt);
+    };
+
 
     // Per-lane LDS read bases.  K A operand: row j of each 32-row group, half
     // h of each 16-column step.  V^T A operand via the transposing read: in
     // lane group g = lane / 16 the lane 16 g + 4 e + a reads 4 columns
     // (16 (g % 2) + 4 a ..) of key row 8 (g / 2) + e (+ 4 for the second
     // read); lane i of the group then holds column 16 (g % 2) + i for 4 keys.
-    const char* kread = smem + (j * C::KP + 8 * h) * 2;
+    const int kread = (j * C::KP + 8 * h) * 2;
     const int g16 = lane >> 4, e4 = (lane >> 2) & 3, a4 = lane & 3;
-    const char* vread = smem + 2 * C::KTILE_B +
-                        ((8 * (g16 >> 1) + e4) * C::VP + 16 * (g16 & 1) + 4 * a4) * 2;
+    const int vread = ((8 * (g16 >> 1) + e4) * C::VP + 16 * (g16 & 1) + 4 * a4) * 2;
 
-    auto compute = [&](auto bufc, int kt) {
-        constexpr int BUF = decltype(bufc)::value;
-        const int kv0 = kt * BC;
-        // A wave whose rows all precede the tile's first key sees nothing in it.
-        if (CAUSAL && kv0 > qw0 + QT * 32 - 1) return;
-
-        // ---- S^T = K Q^T for two 32-key MFMA tiles ----
-        f32x16 s[2][QT];
+    // S^T = K Q^T of the K tile in LDS buffer KB, two 32-key MFMA tiles.
+    auto qk = [&](auto kbc, f32x16 (&s)[NMT][QT]) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < QT; ++nt) s[mt][nt] = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
+            for (int mt = 0; mt < NMT; ++mt) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    kread + BUF * C::KTILE_B + (mt * 32 * C::KP + kk * 16) * 2);
+                    kbuf(kbc) + kread + (mt * 32 * C::KP + kk * 16) * 2);
 #pragma unroll
                 for (int nt = 0; nt < QT; ++nt)
                     s[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nt][kk], s[mt][nt], 0, 0, 0);
             }
         }
+    };
 
-        // ---- mask (diagonal / tail tiles only) and tile row maxima ----
+    // Mask (diagonal / tail tiles only), tile row maxima, and the rare move of
+    // the exponent reference.
+    auto stats = [&](f32x16 (&s)[NMT][QT], int kv0) {
         const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
         float mx[QT];
 #pragma unroll
@@ -245,7 +256,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 // Keys visible to query q in this tile: kv0 .. lim - 1.
                 const int lim = CAUSAL ? min(N, q + 1) : N;
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
+                for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kv0 + mt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
@@ -254,13 +265,11 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             }
             float v = kNegInf;
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) v = fmaxf(v, fmaxf(s[mt][nt][r], s[mt][nt][r + 1]));
             mx[nt] = combine_xor32(v, MaxOp());
         }
-
-        // ---- move the exponent reference only when some row grew past the margin ----
         bool grow = false;
 #pragma unroll
         for (int nt = 0; nt < QT; ++nt) grow |= (mx[nt] - m[nt]) * c > kRescaleLog2;
@@ -278,15 +287,16 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 m[nt] = m_new;
             }
         }
+    };
 
-        // ---- probabilities, row sums, O^T += V^T P^T over four 16-key steps ----
-        bf16x8 pf[BC / 16][QT];
+    // Probabilities of the scores in s (bf16 B fragments, row sums into l).
+    auto probs = [&](f32x16 (&s)[NMT][QT], bf16x8 (&pf)[BC / 16][QT]) {
 #pragma unroll
         for (int nt = 0; nt < QT; ++nt) {
             const float mc = m[nt] * c;
             float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
+            for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float p = exp2_hw(fmaf(s[mt][nt][r], c, -mc));
@@ -303,11 +313,15 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             }
             l[nt] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
         }
+    };
+
+    // O^T += V^T P^T over four 16-key steps, V from LDS buffer VB.
+    auto pv = [&](auto vbc, bf16x8 (&pf)[BC / 16][QT]) {
 #pragma unroll
         for (int ks = 0; ks < BC / 16; ++ks) {
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-                const char* vp = vread + BUF * C::VTILE_B + (16 * ks * C::VP + 32 * dt) * 2;
+                const char* vp = vbuf(vbc) + vread + (16 * ks * C::VP + 32 * dt) * 2;
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)vp);
                 const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 4 * C::VP * 2));
                 const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -322,7 +336,19 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     using B1 = std::integral_constant<int, 1>;
     const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
     const int ntiles = (kv_end + BC - 1) / BC;
+    // Tiles this wave computes: 0 .. wt - 1 (under the causal mask the later
+    // tiles of the workgroup lie wholly in this wave's future).
+    const int wt = CAUSAL ? min(ntiles, (qw0 + QT * 32 - 1) / BC + 1) : ntiles;
 
+    auto compute = [&](auto bufc, int kt) {
+        if (kt >= wt) return;
+        f32x16 s[NMT][QT];
+        qk(bufc, s);
+        stats(s, kt * BC);
+        bf16x8 pf[BC / 16][QT];
+        probs(s, pf);
+        pv(bufc, pf);
+    };
     issue(B0{}, 0);
     __syncthreads();  // waits for the tile loads (vmcnt) before publishing
     for (int kt = 0; kt < ntiles; kt += 2) {
@@ -361,30 +387,26 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
 }
 
-template <int D, int QT, int NW, int WPE, bool CAUSAL>
+template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL>
 hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
                   int N, float scale, hipStream_t stream)
 {
-    using C = Cfg<D, QT, NW>;
+    using C = Cfg<D, QT, NW, BC>;
     const int nqt = (N + C::BR - 1) / C::BR;
     const dim3 grid((unsigned)(nqt * BH)), block(C::T);
-    attn_fwd_bf16_kernel<D, QT, NW, WPE, CAUSAL><<<grid, block, 0, stream>>>(
+    attn_fwd_bf16_kernel<D, QT, NW, WPE, BC, CAUSAL><<<grid, block, 0, stream>>>(
         static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
         static_cast<__bf16*>(O), lse, N, BH, nqt, scale);
     return hipGetLastError();
 }
 
-#ifndef OSM_ATTN_VARIANTS
-// 8 waves x 32 query rows per workgroup, two waves per SIMD.
+// 8 waves x 32 query rows per workgroup (two waves per SIMD), 64-key tiles.
 template <int D, bool CAUSAL>
 hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
                     int N, float scale, hipStream_t stream)
 {
-    return launch<D, 1, 8, 2, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
+    return launch<D, 1, 8, 2, 64, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
 }
-#else
-#include OSM_ATTN_VARIANTS
-#endif
 
 }  // namespace
 

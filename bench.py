@@ -166,7 +166,7 @@ def main() -> int:
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_attn,
-                     "kernel": "attn_fwd_bf16_kernel", "kernel_ms": round(attn_ms, 4),
+                     "kernel": "attn_fwd_bf16_pp_kernel", "kernel_ms": round(attn_ms, 4),
                      "flops_per_launch": wa.flops, "algorithmic_bytes": attn_bytes},
         "softmax": {"value": round(sm_gbs, 1), "unit": "GB/s", "kernel_ms": round(sm_ms, 4)},
         "roofline_softmax": {"bound": "hbm", "achieved": round(sm_gbs, 1), "peak": PEAK_HBM_GBS,

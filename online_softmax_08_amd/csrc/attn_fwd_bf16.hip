@@ -49,6 +49,12 @@
 //    maximum more than 8 (in log2 units) above it; otherwise every p <= 2^8
 //    and neither l nor the accumulators are touched.  The result is the same
 //    exact quantity: l and the accumulators share the reference.
+//  * Two schedules share these pieces.  attn_fwd_bf16_kernel runs each tile
+//    as S^T, softmax, P V in every wave; the two waves of a SIMD then mostly
+//    use the matrix core and the vector unit at the same time and wait for
+//    each other.  attn_fwd_bf16_pp_kernel (used under the causal mask, where
+//    it measures faster) staggers the two waves of each SIMD by half a tile
+//    step, so that one issues only MFMAs while the other runs the softmax.
 
 #include <type_traits>
 
@@ -387,6 +393,283 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
 }
 
+// Phase-staggered variant: 8 waves of 32 query rows, two per SIMD (waves w
+// and w + 4 share one).  Each tile step of a wave is split into a matrix
+// phase, P V of the previous tile and S^T = K Q^T of this one, and a vector
+// phase, the tile's mask, maxima, reference move and exponentials.  Waves
+// 0-3 run their matrix phase while waves 4-7 run their vector phase and vice
+// versa, with a workgroup barrier between phases: the matrix core of every
+// SIMD is fed by one wave while the vector unit serves the other.
+// Tile i is read in phases 2i (waves 0-3) and 2i + 1 (waves 4-7); the loads
+// of K(i + 1) and V(i) start in phase 2i and are waited for before the
+// barrier that ends phase 2i + 1.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                        const __bf16* __restrict__ V, __bf16* __restrict__ O,
+                        float* __restrict__ lse, int N, int BH, int nqt, float scale)
+{
+    constexpr int NW = 8, BC = 64;
+    using C = Cfg<D, 1, NW, BC>;
+    __shared__ __attribute__((aligned(1024))) char kbuf0[C::KTILE_B];
+    __shared__ __attribute__((aligned(1024))) char kbuf1[C::KTILE_B];
+    __shared__ __attribute__((aligned(1024))) char vbuf0[C::VTILE_B];
+    __shared__ __attribute__((aligned(1024))) char vbuf1[C::VTILE_B];
+    auto kbuf = [&](auto bufc) -> char* { if constexpr (decltype(bufc)::value == 0) return kbuf0; else return kbuf1; };
+    auto vbuf = [&](auto bufc) -> char* { if constexpr (decltype(bufc)::value == 0) return vbuf0; else return vbuf1; };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool late = wave >= NW / 2;  // runs each phase one step after its SIMD partner
+    const int j = lane & 31, h = lane >> 5;
+    const int t = blockIdx.x / BH, bh = blockIdx.x - t * BH;
+    const int qt = CAUSAL ? nqt - 1 - t : t;
+    const int q0 = qt * C::BR;
+    const size_t base = (size_t)bh * N * D;
+    const uint32_t slice_b = (uint32_t)N * D * 2;
+    const int qw0 = q0 + wave * 32;
+    const int qrow = qw0 + j;
+
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, slice_b);
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        qf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+            qrs, (uint32_t)(qrow * D + kk * 16 + 8 * h) * 2, 0, 0));
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+    float m = kNegInf, l = 0.f;
+    const float c = scale * kLog2e;
+
+    const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
+    const int ntiles = (kv_end + BC - 1) / BC;
+    // This wave computes tiles 0 .. T - 1; only tile T - 1 can need a mask.
+    const int T = CAUSAL ? min(ntiles, qw0 / BC + 1) : ntiles;
+    const int kvm = (T - 1) * BC;
+    const bool mask_last = (kvm + BC > N) || (CAUSAL && kvm + BC - 1 > qw0);
+
+    // Per-lane source offsets of this wave's 1 KiB tile loads: load i fills
+    // LDS chunk positions 64 i .. 64 i + 63 of a tile, and the lane at
+    // position p fetches row p / CPR, column chunk p % CPR (padding chunks
+    // re-fetch the row's last real chunk).  K rows are permuted inside each
+    // 32-row group (swap_bits23); V rows keep key order.
+    uint32_t ksrc[C::KPW], vsrc[C::VPW];
+#pragma unroll
+    for (int u = 0; u < C::KPW; ++u) {
+        const int p = (wave + u * NW) * 64 + lane;
+        const int lrow = p / C::KCPR, ch = min(p % C::KCPR, D / 8 - 1);
+        const int row = (lrow & ~31) | swap_bits23(lrow & 31);
+        ksrc[u] = (uint32_t)(row * D + ch * 8) * 2;
+    }
+#pragma unroll
+    for (int u = 0; u < C::VPW; ++u) {
+        const int p = (wave + u * NW) * 64 + lane;
+        const int row = p / C::VCPR, ch = min(p % C::VCPR, D / 8 - 1);
+        vsrc[u] = (uint32_t)(row * D + ch * 8) * 2;
+    }
+    const __bf16* Kb = K + base;
+    const __bf16* Vb = V + base;
+    auto issue_k = [&](auto bufc, int kt) {
+        const int kv0 = kt * BC;
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb + (size_t)kv0 * D, (uint32_t)(N - kv0) * D * 2);
+#pragma unroll
+        for (int u = 0; u < C::KPW; ++u) {
+            const int i = wave + u * NW;
+            if (C::KINST % NW == 0 || i < C::KINST)
+                lds_dma16(krs, (lds_void_t*)(kbuf(bufc) + i * 1024), ksrc[u]);
+        }
+    };
+    auto issue_v = [&](auto bufc, int kt) {
+        const int kv0 = kt * BC;
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb + (size_t)kv0 * D, (uint32_t)(N - kv0) * D * 2);
+#pragma unroll
+        for (int u = 0; u < C::VPW; ++u) {
+            const int i = wave + u * NW;
+            if (C::VINST % NW == 0 || i < C::VINST)
+                lds_dma16(vrs, (lds_void_t*)(vbuf(bufc) + i * 1024), vsrc[u]);
+        }
+    };
+
+    const int kread = (j * C::KP + 8 * h) * 2;
+    const int g16 = lane >> 4, e4 = (lane >> 2) & 3, a4 = lane & 3;
+    const int vread = ((8 * (g16 >> 1) + e4) * C::VP + 16 * (g16 & 1) + 4 * a4) * 2;
+
+    f32x16 s[2];    // scores of the current tile, 32 keys each
+    bf16x8 pf[4];   // its probabilities, bf16, 16 keys each
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pf[ks] = bf16x8{};
+
+    auto qk = [&](auto kbc) {
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    kbuf(kbc) + kread + (mt * 32 * C::KP + kk * 16) * 2);
+                s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mt], 0, 0, 0);
+            }
+    };
+    auto pv = [&](auto vbc) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const char* vp = vbuf(vbc) + vread + (16 * ks * C::VP + 32 * dt) * 2;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)vp);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 4 * C::VP * 2));
+                const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], acc[dt], 0, 0, 0);
+            }
+    };
+
+
+    // Matrix phase of step i: P V of tile i - 1, then S^T of tile i, as one
+    // block whose LDS reads the scheduler keeps several MFMAs ahead of their
+    // use (48 reads feed 32 MFMAs).  One code path for steps 0 .. T keeps
+    // the accumulators in fixed registers: step 0 multiplies P = 0 with the
+    // zeroed V buffer (adds exactly 0), and the scores step T computes are
+    // never used.
+    auto matrix_phase = [&](auto kbc, auto vbc, int i) {
+        if (i > T) return;
+        pv(vbc);
+        qk(kbc);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
+#pragma unroll
+        for (int u = 0; u < 20; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    };
+    // Vector phase of step i: mask (last tile only), row maxima, the rare
+    // move of the exponent reference, probabilities and row sums.
+    auto vector_phase = [&](int i) {
+        if (i < 0 || i >= T) return;
+        if (i == T - 1 && mask_last) {
+            // Key kvm + o of register r (o below) is hidden when o >= thr.
+            // The empty asm keeps the 32 comparisons inside this rarely
+            // taken branch instead of letting them be hoisted out of the loop.
+            int thr = (CAUSAL ? min(N, qrow + 1) : N) - kvm - 8 * h;
+            asm volatile("" : "+v"(thr));
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (mt * 32 + 16 * (r >> 3) + (r & 7) >= thr) s[mt][r] = kNegInf;
+        }
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = fmaxf(s[0][u], s[0][u + 4]);
+#pragma unroll
+        for (int r = 8; r < 16; ++r) v[r & 3] = fmaxf(v[r & 3], s[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r & 3] = fmaxf(v[r & 3], s[1][r]);
+        const float mx = combine_xor32(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), MaxOp());
+        if (__builtin_amdgcn_ballot_w64((mx - m) * c > kRescaleLog2) != 0) {
+            // Tile 0 holds key 0, visible to every row, so m_new is finite;
+            // an empty history (m = -inf, l = acc = 0) gets factor 0.
+            const float m_new = fmaxf(m, mx);
+            const float alpha = (m_new == kNegInf) ? 1.f : exp2_hw((m - m_new) * c);
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+            m = m_new;
+        }
+        const float mc = m * c;
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = exp2_hw(fmaf(s[mt][r], c, -mc));
+                s[mt][r] = p;
+                ps[r & 3] += p;
+            }
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const f32x16& sv = s[mt];
+                const f32x8 p8 = half ? __builtin_shufflevector(sv, sv, 8, 9, 10, 11, 12, 13, 14, 15)
+                                      : __builtin_shufflevector(sv, sv, 0, 1, 2, 3, 4, 5, 6, 7);
+                pf[2 * mt + half] = __builtin_convertvector(p8, bf16x8);
+            }
+        }
+        l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    };
+
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    // Prologue: K(0), and zeros into vbuf1 (V(-1), read by step 0, so that
+    // 0 * V stays 0).
+    issue_k(B0{}, 0);
+    for (int o = tid * 16; o < C::VTILE_B; o += NW * 64 * 16)
+        *reinterpret_cast<u32x4*>(vbuf1 + o) = u32x4{};
+    __syncthreads();
+    // Steps i = 0 .. ntiles (step ntiles only finishes P V); two steps per
+    // loop trip so every LDS buffer is a compile-time choice: K(i) sits in
+    // kbuf[i % 2], V(i - 1) in vbuf[(i - 1) % 2].  K(i + 1) and V(i) are
+    // issued at the start of phase 2i and waited for at the barrier that
+    // ends phase 2i + 1.  The two wave groups run separate copies of the
+    // loop (same barriers, phases swapped), which keeps each copy's live
+    // registers to those of one phase order.
+    auto steps = [&](auto latec) {
+        constexpr bool LATE = decltype(latec)::value;
+        for (int i = 0; i <= ntiles; i += 2) {
+            if (i + 1 < ntiles) issue_k(B1{}, i + 1);
+            if (i < ntiles) issue_v(B0{}, i);
+            if constexpr (!LATE) matrix_phase(B0{}, B1{}, i); else vector_phase(i - 1);
+            __builtin_amdgcn_s_barrier();
+            if constexpr (!LATE) vector_phase(i); else matrix_phase(B0{}, B1{}, i);
+            if (i + 1 > ntiles) break;
+            __syncthreads();  // K(i + 1) and V(i) have landed
+            if (i + 2 < ntiles) issue_k(B0{}, i + 2);
+            if (i + 1 < ntiles) issue_v(B1{}, i + 1);
+            if constexpr (!LATE) matrix_phase(B1{}, B0{}, i + 1); else vector_phase(i);
+            __builtin_amdgcn_s_barrier();
+            if constexpr (!LATE) vector_phase(i + 1); else matrix_phase(B1{}, B0{}, i + 1);
+            __syncthreads();  // K(i + 2) and V(i + 1) have landed
+        }
+    };
+    if (late)
+        steps(std::true_type{});
+    else
+        steps(std::false_type{});
+
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(O + base, slice_b);
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lse + (size_t)bh * N, (uint32_t)N * 4);
+    const float l_tot = combine_xor32(l, SumOp());
+    const float inv = 1.0f / l_tot;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 o4 = {acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv,
+                              acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv};
+            const bf16x4 ob = __builtin_convertvector(o4, bf16x4);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ors,
+                                                  (uint32_t)(qrow * D + dt * 32 + 8 * g + 4 * h) * 2, 0, 0);
+        }
+    if (h == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m * scale + logf(l_tot)), lrs,
+                                              (uint32_t)qrow * 4, 0, 0);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_pp(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
+                     int N, float scale, hipStream_t stream)
+{
+    constexpr int BR = 256;
+    const int nqt = (N + BR - 1) / BR;
+    const dim3 grid((unsigned)(nqt * BH)), block(512);
+    attn_fwd_bf16_pp_kernel<D, CAUSAL><<<grid, block, 0, stream>>>(
+        static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
+        static_cast<__bf16*>(O), lse, N, BH, nqt, scale);
+    return hipGetLastError();
+}
+
 template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL>
 hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
                   int N, float scale, hipStream_t stream)
@@ -401,11 +684,16 @@ hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* l
 }
 
 // 8 waves x 32 query rows per workgroup (two waves per SIMD), 64-key tiles.
+// Under the causal mask the phase-staggered kernel is faster; without it the
+// two measure alike and the plain kernel is kept.
 template <int D, bool CAUSAL>
 hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
                     int N, float scale, hipStream_t stream)
 {
-    return launch<D, 1, 8, 2, 64, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
+    if constexpr (CAUSAL)
+        return launch_pp<D, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
+    else
+        return launch<D, 1, 8, 2, 64, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
 }
 
 }  // namespace

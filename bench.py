@@ -4,10 +4,9 @@ One step = one fused attention forward on the causal bf16 workload
 (B=2, H=16 -> B*H = 32, N=4096, d=128, every 64th query row x8) followed by
 one stable row softmax over fp32 [32768, 8192].  Inputs are seeded synthetic
 tensors already resident in HBM.  W untimed warm-up steps, then K timed steps
-between device synchronisations: the K attention launches run back to back,
-then the K softmax launches, and HIP events recorded on the launch stream
-(torch's current stream) around each group give each kernel's average
-launch duration.
+between device synchronisations; HIP events recorded on the launch stream
+(torch's current stream) around each launch give each kernel's mean launch
+duration.
 
 Prints one JSON line:
   value             attention TFLOPS, counted FLOPs 4*B*H*N^2*d / 2 (causal)
@@ -113,22 +112,22 @@ def main() -> int:
             cdst.copy_(csrc)
     torch.cuda.synchronize()
 
-    # Timed region: the K steps' attention launches back to back, then their K
-    # row-softmax launches, bracketed by three HIP events on the launch stream
-    # (torch's current stream) so each kernel's average launch duration is one
-    # bracket divided by K; the wall clock between the synchronisations gives
-    # the time per step.
+    # Timed region: K steps, each one attention launch followed by one row
+    # softmax launch, between two device synchronisations (wall clock per
+    # step).  HIP events recorded on the launch stream (torch's current
+    # stream) before the attention, between the two launches and after the
+    # softmax give each kernel's launch duration; their means over the K
+    # steps are the per-kernel figures.
     K = args.steps
-    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(K):
+    for e in ev:
+        e[0].record()
         osm.attention(q, k, v, causal=wa.causal, out=O, lse=lse)
-    e1.record()
-    for _ in range(K):
+        e[1].record()
         osm.softmax(x, out=y)
-    e2.record()
+        e[2].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if args.copy_probe:
@@ -136,8 +135,8 @@ def main() -> int:
             cdst.copy_(csrc)
         torch.cuda.synchronize()
 
-    attn_ms = e0.elapsed_time(e1) / K
-    sm_ms = e1.elapsed_time(e2) / K
+    attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    sm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
     attn_tflops = wa.flops / (attn_ms * 1e-3) / 1e12
     sm_gbs = ws.bytes / (sm_ms * 1e-3) / 1e9
     # Algorithmic HBM bytes of the attention kernel: Q, K, V read once, O and

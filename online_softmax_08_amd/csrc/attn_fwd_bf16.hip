@@ -450,45 +450,44 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     const int kvm = (T - 1) * BC;
     const bool mask_last = (kvm + BC > N) || (CAUSAL && kvm + BC - 1 > qw0);
 
-    // Per-lane source offsets of this wave's 1 KiB tile loads: load i fills
-    // LDS chunk positions 64 i .. 64 i + 63 of a tile, and the lane at
-    // position p fetches row p / CPR, column chunk p % CPR (padding chunks
-    // re-fetch the row's last real chunk).  K rows are permuted inside each
-    // 32-row group (swap_bits23); V rows keep key order.
-    uint32_t ksrc[C::KPW], vsrc[C::VPW];
+    // Tile loads.  The four waves that are about to run their matrix phase
+    // load one part of a tile right before it: waves 0-3 load K(i + 1) at
+    // the start of phase 2i, waves 4-7 load V(i) at the start of phase
+    // 2i + 1 (each part 17 or 18 1 KiB loads, about five per wave).  An
+    // LDS-bound load costs its wave some 30 cycles of issue and the CU
+    // accepts about one per 10 cycles, so four waves issuing one part cost
+    // half of what all eight waves issuing both parts at once would.  Load n
+    // of a part fills LDS positions 64 n .. 64 n + 63; the lane at position p
+    // fetches row p / CPR, column chunk p % CPR (padding chunks re-fetch the
+    // row's last real chunk).  K rows are permuted inside each 32-row group
+    // (swap_bits23); V rows keep key order.
+    constexpr int NG = NW / 2;  // waves per group
+    constexpr int LPW = ((C::KINST > C::VINST ? C::KINST : C::VINST) + NG - 1) / NG;
+    const int g = wave % NG;
+    const int ninst = late ? C::VINST : C::KINST;
+    uint32_t src[LPW];
 #pragma unroll
-    for (int u = 0; u < C::KPW; ++u) {
-        const int p = (wave + u * NW) * 64 + lane;
-        const int lrow = p / C::KCPR, ch = min(p % C::KCPR, D / 8 - 1);
-        const int row = (lrow & ~31) | swap_bits23(lrow & 31);
-        ksrc[u] = (uint32_t)(row * D + ch * 8) * 2;
-    }
-#pragma unroll
-    for (int u = 0; u < C::VPW; ++u) {
-        const int p = (wave + u * NW) * 64 + lane;
-        const int row = p / C::VCPR, ch = min(p % C::VCPR, D / 8 - 1);
-        vsrc[u] = (uint32_t)(row * D + ch * 8) * 2;
-    }
-    const __bf16* Kb = K + base;
-    const __bf16* Vb = V + base;
-    auto issue_k = [&](auto bufc, int kt) {
-        const int kv0 = kt * BC;
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb + (size_t)kv0 * D, (uint32_t)(N - kv0) * D * 2);
-#pragma unroll
-        for (int u = 0; u < C::KPW; ++u) {
-            const int i = wave + u * NW;
-            if (C::KINST % NW == 0 || i < C::KINST)
-                lds_dma16(krs, (lds_void_t*)(kbuf(bufc) + i * 1024), ksrc[u]);
+    for (int u = 0; u < LPW; ++u) {
+        const int p = (g + u * NG) * 64 + lane;
+        if (!late) {
+            const int lrow = p / C::KCPR, ch = min(p % C::KCPR, D / 8 - 1);
+            const int row = (lrow & ~31) | swap_bits23(lrow & 31);
+            src[u] = (uint32_t)(row * D + ch * 8) * 2;
+        } else {
+            const int row = p / C::VCPR, ch = min(p % C::VCPR, D / 8 - 1);
+            src[u] = (uint32_t)(row * D + ch * 8) * 2;
         }
-    };
-    auto issue_v = [&](auto bufc, int kt) {
+    }
+    // This wave's share of tile kt of its group's part into buffer BUFC.
+    auto load_part = [&](auto bufc, int kt) {
         const int kv0 = kt * BC;
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb + (size_t)kv0 * D, (uint32_t)(N - kv0) * D * 2);
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc((late ? V : K) + base + (size_t)kv0 * D, (uint32_t)(N - kv0) * D * 2);
+        char* dst = late ? vbuf(bufc) : kbuf(bufc);
 #pragma unroll
-        for (int u = 0; u < C::VPW; ++u) {
-            const int i = wave + u * NW;
-            if (C::VINST % NW == 0 || i < C::VINST)
-                lds_dma16(vrs, (lds_void_t*)(vbuf(bufc) + i * 1024), vsrc[u]);
+        for (int u = 0; u < LPW; ++u) {
+            const int n = g + u * NG;
+            if (n < ninst) lds_dma16(rs, (lds_void_t*)(dst + n * 1024), src[u]);
         }
     };
 
@@ -602,34 +601,50 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    // Prologue: K(0), and zeros into vbuf1 (V(-1), read by step 0, so that
-    // 0 * V stays 0).
-    issue_k(B0{}, 0);
+    // Prologue: K(0) (waves 0-3), and zeros into vbuf1 (V(-1), read by step
+    // 0, so that 0 * V stays 0).
+    if (!late) load_part(B0{}, 0);
     for (int o = tid * 16; o < C::VTILE_B; o += NW * 64 * 16)
         *reinterpret_cast<u32x4*>(vbuf1 + o) = u32x4{};
     __syncthreads();
     // Steps i = 0 .. ntiles (step ntiles only finishes P V); two steps per
     // loop trip so every LDS buffer is a compile-time choice: K(i) sits in
-    // kbuf[i % 2], V(i - 1) in vbuf[(i - 1) % 2].  K(i + 1) and V(i) are
-    // issued at the start of phase 2i and waited for at the barrier that
-    // ends phase 2i + 1.  The two wave groups run separate copies of the
-    // loop (same barriers, phases swapped), which keeps each copy's live
-    // registers to those of one phase order.
+    // kbuf[i % 2], V(i) in vbuf[i % 2].  K(i + 1) (loaded at the start of
+    // phase 2i) and V(i) (start of phase 2i + 1) are waited for at the
+    // barrier that ends phase 2i + 1.  The two wave groups run separate
+    // copies of the loop (same barriers, phases swapped), which keeps each
+    // copy's live registers to those of one phase order.
     auto steps = [&](auto latec) {
         constexpr bool LATE = decltype(latec)::value;
         for (int i = 0; i <= ntiles; i += 2) {
-            if (i + 1 < ntiles) issue_k(B1{}, i + 1);
-            if (i < ntiles) issue_v(B0{}, i);
-            if constexpr (!LATE) matrix_phase(B0{}, B1{}, i); else vector_phase(i - 1);
+            if constexpr (!LATE) {
+                if (i + 1 < ntiles) load_part(B1{}, i + 1);
+                matrix_phase(B0{}, B1{}, i);
+            } else {
+                vector_phase(i - 1);
+            }
             __builtin_amdgcn_s_barrier();
-            if constexpr (!LATE) vector_phase(i); else matrix_phase(B0{}, B1{}, i);
+            if constexpr (!LATE) {
+                vector_phase(i);
+            } else {
+                if (i < ntiles) load_part(B0{}, i);
+                matrix_phase(B0{}, B1{}, i);
+            }
             if (i + 1 > ntiles) break;
             __syncthreads();  // K(i + 1) and V(i) have landed
-            if (i + 2 < ntiles) issue_k(B0{}, i + 2);
-            if (i + 1 < ntiles) issue_v(B1{}, i + 1);
-            if constexpr (!LATE) matrix_phase(B1{}, B0{}, i + 1); else vector_phase(i);
+            if constexpr (!LATE) {
+                if (i + 2 < ntiles) load_part(B0{}, i + 2);
+                matrix_phase(B1{}, B0{}, i + 1);
+            } else {
+                vector_phase(i);
+            }
             __builtin_amdgcn_s_barrier();
-            if constexpr (!LATE) vector_phase(i + 1); else matrix_phase(B1{}, B0{}, i + 1);
+            if constexpr (!LATE) {
+                vector_phase(i + 1);
+            } else {
+                if (i + 1 < ntiles) load_part(B1{}, i + 1);
+                matrix_phase(B1{}, B0{}, i + 1);
+            }
             __syncthreads();  // K(i + 2) and V(i + 1) have landed
         }
     };
@@ -683,17 +698,26 @@ hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* l
     return hipGetLastError();
 }
 
-// 8 waves x 32 query rows per workgroup (two waves per SIMD), 64-key tiles.
-// Under the causal mask the phase-staggered kernel is faster; without it the
-// two measure alike and the plain kernel is kept.
+// Workgroups of 8 waves x 32 query rows (two waves per SIMD), 64-key tiles,
+// while that still gives one workgroup per CU (256) or more; smaller problems
+// use workgroups of 4 or 2 waves so that the grid still covers the chip.
+// With 8 waves the phase-staggered kernel serves the causal case (it
+// measures faster there); without the mask the two measure alike and the
+// plain kernel is kept.
 template <int D, bool CAUSAL>
 hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
                     int N, float scale, hipStream_t stream)
 {
-    if constexpr (CAUSAL)
-        return launch_pp<D, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
-    else
-        return launch<D, 1, 8, 2, 64, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
+    constexpr long long kCUs = 256;
+    if ((long long)((N + 255) / 256) * BH >= kCUs) {
+        if constexpr (CAUSAL)
+            return launch_pp<D, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
+        else
+            return launch<D, 1, 8, 2, 64, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
+    }
+    if ((long long)((N + 127) / 128) * BH >= kCUs)
+        return launch<D, 1, 4, 2, 64, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
+    return launch<D, 1, 2, 2, 64, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
 }
 
 }  // namespace

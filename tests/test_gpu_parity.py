@@ -171,6 +171,29 @@ def test_attn_deterministic(osm):
     assert torch.equal(O1, O2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 8, 2048, 64), (2, 8, 4096, 128), (1, 2, 4096, 128)])
+def test_attn_workgroup_sizes(osm, shape, causal):
+    # The launch uses workgroups of 2, 4 or 8 waves depending on how many
+    # it takes to cover the chip; these shapes reach the 4-wave size (first),
+    # the 8-wave kernels (second) and the 2-wave size at long N (third) for
+    # both masks.  Sampled rows against the oracle, every row finite.
+    B, H, N, d = shape
+    base = inputs.ATTN["attn_bf16_B2H8N1024d64" if d == 64 else "attn_bf16_B4H16N2048d128"]
+    q, k, v = inputs.attn_inputs(base, B=B, H=H, N=N, d=d, seed=base.seed + 7 * N + d)
+    scale = 1.0 / math.sqrt(d)
+    O, lse = _gpu_attn(osm, q, k, v, causal, scale)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse))
+    w = inputs.AttnWorkload(name="wg", dtype="bf16", B=B, H=H, N=N, d=d, causal=causal, seed=base.seed)
+    rng = np.random.default_rng(N + d + causal)
+    bh, qi = _sample_rows(w, rng, n_slices=4, n_random=12)
+    Oref, lref = oracle.attn_rows(q, k, v, scale, causal, bh, qi)
+    eo = _maxabs(O.reshape(B * H, N, d)[bh, qi], Oref)
+    el = _maxabs(lse.reshape(B * H, N)[bh, qi], lref)
+    print(f"B{B}H{H}N{N}d{d} causal={causal}: {len(qi)} rows max|dO|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1]
+
+
 def test_attn_custom_scale(osm):
     base = inputs.ATTN["attn_bf16_B2H8N1024d64"]
     q, k, v = inputs.attn_inputs(base, B=1, H=2, N=190, d=64, seed=3)

@@ -16,6 +16,10 @@ Prints one JSON line:
   roofline_softmax  softmax kernel against the HBM peak
   cpu_baseline      the fp64 oracle on the host cores, on a bounded sample
                     of the same workload (and its parity on that sample)
+  supplementary     measured after the timed region: the attention shape
+                    without the mask, a plain device copy of the softmax
+                    input as the practical HBM ceiling, and the split-KV
+                    forward beside the single pass on long rows / few heads
 """
 from __future__ import annotations
 
@@ -176,8 +180,64 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wa, ws, q_cpu, k_cpu, v_cpu, x_cpu, O, lse, y)
+    out["supplementary"] = supplementary(osm, wa, ws, q, k, v, x)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def supplementary(osm, wa, ws, q, k, v, x, reps=10):
+    """Figures measured after the timed region, not part of a step: the same
+    attention shape without the causal mask, and a plain device copy of the
+    softmax input (the practical ceiling for a read-once / write-once
+    kernel on this GPU)."""
+    import torch
+
+    def per_launch_ms(fn):
+        for _ in range(2):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / reps
+
+    O2 = torch.empty_like(q)
+    lse2 = torch.empty((wa.B, wa.H, wa.N), dtype=torch.float32, device=q.device)
+    nc_ms = per_launch_ms(lambda: osm.attention(q, k, v, causal=False, out=O2, lse=lse2))
+    nc_flops = 4.0 * wa.B * wa.H * wa.N * wa.N * wa.d
+    dst = torch.empty_like(x)
+    cp_ms = per_launch_ms(lambda: dst.copy_(x))
+    # Split-KV on long rows and few heads (256-row query blocks alone would
+    # cover an eighth of the CUs), next to the single pass on the same input.
+    B, H, N, d = 1, 2, 8192, 128
+    g = torch.Generator().manual_seed(5)
+    qs, ks, vs = (torch.randn((B, H, N, d), generator=g).to(torch.bfloat16).to(q.device)
+                  for _ in range(3))
+    split = {"workload": f"bf16 B={B} H={H} N={N} d={d}"}
+    for causal in (False, True):
+        ns, ws_bytes = osm.attn_fwd_splitkv_plan(B, H, N, d, causal, 0)
+        wsp = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        flops = 4.0 * B * H * N * N * d / (2 if causal else 1)
+        t_split = per_launch_ms(lambda: osm.attention_splitkv(qs, ks, vs, causal=causal,
+                                                              nsplit=ns, workspace=wsp))
+        t_one = per_launch_ms(lambda: osm.attention(qs, ks, vs, causal=causal))
+        split["causal" if causal else "noncausal"] = {
+            "nsplit": ns, "split_tflops": round(flops / (t_split * 1e-3) / 1e12, 1),
+            "single_pass_tflops": round(flops / (t_one * 1e-3) / 1e12, 1),
+            "split_ms": round(t_split, 4), "single_pass_ms": round(t_one, 4)}
+    return {
+        "attn_noncausal": {"workload": f"bf16 B={wa.B} H={wa.H} N={wa.N} d={wa.d}, no mask",
+                           "value": round(nc_flops / (nc_ms * 1e-3) / 1e12, 2), "unit": "TFLOPS",
+                           "kernel_ms": round(nc_ms, 4)},
+        "hbm_copy": {"workload": f"device copy of the fp32 [{ws.B}, {ws.N}] softmax input",
+                     "value": round(ws.bytes / (cp_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                     "kernel_ms": round(cp_ms, 4)},
+        "attn_splitkv": split,
+    }
 
 
 def cpu_baseline(wa, ws, q_cpu, k_cpu, v_cpu, x_cpu, O, lse, y):

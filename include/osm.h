@@ -1,7 +1,7 @@
 /*
  * osm.h -- C ABI of the MI355X (gfx950) online-softmax attention library.
  *
- * Two operations, both defined on the source pages:
+ * The operations, all defined on the source pages:
  *
  *  attn_fwd / attn_fwd_f32
  *    Exact attention forward O = softmax(scale * Q K^T) V for every
@@ -14,6 +14,15 @@
  *    (the row statistic L = m + log l, natural log, of the scaled scores).
  *    The computation is the fused, tiled online softmax of Lesson 22,
  *    sections 21-24 and 32: S and P are never written to memory.
+ *
+ *  attn_fwd_splitkv / attn_combine
+ *    The same attention with the keys of each query block divided into
+ *    several ranges computed in parallel, each yielding a normalised partial
+ *    output and a partial logsumexp, which a second kernel merges.  The
+ *    split is the occupancy device of "Operator fusion seen through
+ *    FlashAttention", the list of risks, item 6 (split-KV with accumulated
+ *    lse and output partials, then a combine); the merge is the rule for
+ *    joining two partial softmax states of Lesson 22, section 22.
  *
  *  row_softmax
  *    Numerically stable softmax of each row of x [B][N]:
@@ -40,6 +49,8 @@
 #ifndef OSM_H
 #define OSM_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -53,7 +64,9 @@ typedef enum {
     OSM_ERR_ALIAS = 5,    /* an output overlaps an input or the other output   */
     OSM_ERR_ALIGN = 6,    /* a pointer is not aligned as required              */
     OSM_ERR_DEVICE = 7,   /* the current device is not a gfx950 GPU            */
-    OSM_ERR_HIP = 8       /* the HIP runtime reported an error at launch       */
+    OSM_ERR_HIP = 8,      /* the HIP runtime reported an error at launch       */
+    OSM_ERR_SPLITS = 9,   /* a split count is outside its documented range     */
+    OSM_ERR_WORKSPACE = 10 /* workspace_bytes is below what the plan requires  */
 } osm_status;
 
 /*
@@ -79,6 +92,62 @@ int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* lse,
  */
 int attn_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* lse,
                  int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * attn_fwd_splitkv_plan -- resolve a split count and size its workspace.
+ *   B, H, N, d, causal : as for attn_fwd (d must be 64 or 128)
+ *   nsplit             : 1 .. 64 key ranges, or 0 to let the library choose
+ *                        (it splits only when 256-row query blocks alone
+ *                        would leave compute units idle)
+ *   *nsplit_out        : the count attn_fwd_splitkv will use for nsplit
+ *   *workspace_bytes   : device bytes attn_fwd_splitkv needs for it:
+ *                        nsplit * B * H * N * (d + 1) * 4, or 0 when the
+ *                        count is 1 (then the call is exactly attn_fwd)
+ * Host only; touches no device.  Returns OSM_ERR_NULL for NULL out pointers,
+ * OSM_ERR_SIZE, OSM_ERR_HEAD_DIM or OSM_ERR_SPLITS for bad sizes.
+ */
+int attn_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int nsplit,
+                          int* nsplit_out, size_t* workspace_bytes);
+
+/*
+ * attn_fwd_splitkv -- attn_fwd computed as nsplit parallel key ranges plus a
+ * merge.  Q, K, V, O, lse, B, H, N, d, scale, causal, stream as for attn_fwd.
+ *   nsplit          : 0 (library's choice) or 1 .. 64.  Each 256-row query
+ *                     block divides its visible key tiles (64 keys each)
+ *                     into nsplit near-equal contiguous ranges; ranges past
+ *                     the last visible tile are empty.
+ *   workspace       : device memory of at least workspace_bytes as returned
+ *                     by attn_fwd_splitkv_plan for the same arguments,
+ *                     16-byte aligned, not overlapping any other argument;
+ *                     may be NULL when the resolved count is 1.  The caller
+ *                     owns it; its contents on entry do not matter and on
+ *                     return are unspecified.  Calls that share a workspace
+ *                     must be ordered on one stream.
+ * O and lse satisfy attn_fwd's tolerance against the exact result; they are
+ * not bitwise equal to attn_fwd's (the partials are merged in fp32).
+ * Returns an osm_status (OSM_ERR_WORKSPACE if workspace_bytes is too small,
+ * OSM_ERR_SIZE if N * d * 4 does not fit in 32 bits).
+ */
+int attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* lse,
+                     int B, int H, int N, int d, float scale, int causal, int nsplit,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_combine -- merge S partial attention results over disjoint key sets.
+ *   O_part   : const fp32 [S][B][H][N][d], partial s normalised over its keys
+ *   lse_part : const fp32 [S][B][H][N], the partial logsumexps (finite, or -inf
+ *              for a row of a partial that saw no key: its O_part row is then
+ *              not read)
+ *   O        : bf16 [B][H][N][d] = sum_s e^(lse_s - lse) O_s
+ *   lse      : fp32 [B][H][N] = ln sum_s e^(lse_s); -inf (and O = 0) for a
+ *              row whose every partial is -inf
+ *   S        : 1 .. 64
+ * Alignment: O_part 16 bytes, O 8, lse_part and lse 4.  Outputs may not
+ * overlap the inputs or each other.  This is the merge step of attn_fwd_splitkv
+ * and of attention whose keys are held in shards.  Returns an osm_status.
+ */
+int attn_combine(const float* O_part, const float* lse_part, void* O, float* lse, int S,
+                 int B, int H, int N, int d, void* stream);
 
 /*
  * row_softmax -- stable softmax of each fp32 row.

@@ -31,10 +31,20 @@ _lib.attn_fwd_f32.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _
 _lib.attn_fwd_f32.restype = _i
 _lib.row_softmax.argtypes = [_vp, _vp, _i, _i, _vp]
 _lib.row_softmax.restype = _i
+_sz = ctypes.c_size_t
+_lib.attn_fwd_splitkv_plan.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(_i),
+                                       ctypes.POINTER(_sz)]
+_lib.attn_fwd_splitkv_plan.restype = _i
+_lib.attn_fwd_splitkv.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp, _sz,
+                                  _vp]
+_lib.attn_fwd_splitkv.restype = _i
+_lib.attn_combine.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
+_lib.attn_combine.restype = _i
 _lib.osm_status_str.argtypes = [_i]
 _lib.osm_status_str.restype = ctypes.c_char_p
 
-EXPORTS = ("attn_fwd", "attn_fwd_f32", "row_softmax", "osm_status_str")
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_splitkv_plan", "attn_fwd_splitkv",
+           "attn_combine", "row_softmax", "osm_status_str")
 
 OSM_OK = 0
 OSM_ERR_NULL = 1
@@ -45,6 +55,8 @@ OSM_ERR_ALIAS = 5
 OSM_ERR_ALIGN = 6
 OSM_ERR_DEVICE = 7
 OSM_ERR_HIP = 8
+OSM_ERR_SPLITS = 9
+OSM_ERR_WORKSPACE = 10
 
 
 class OsmError(RuntimeError):
@@ -82,3 +94,27 @@ def attn_fwd_f32(Q: int, K: int, V: int, O: int, lse: int, B: int, H: int, N: in
 def row_softmax(x: int, y: int, B: int, N: int, stream: int = 0) -> None:
     """Stable row softmax of fp32 [B, N]; see include/osm.h."""
     _call("row_softmax", x, y, B, N, stream)
+
+
+def attn_fwd_splitkv_plan(B: int, H: int, N: int, d: int, causal: bool,
+                          nsplit: int = 0) -> tuple[int, int]:
+    """(resolved split count, workspace bytes) for attn_fwd_splitkv; see include/osm.h."""
+    n_out = _i(0)
+    ws = _sz(0)
+    _call("attn_fwd_splitkv_plan", B, H, N, d, int(bool(causal)), nsplit, ctypes.byref(n_out),
+          ctypes.byref(ws))
+    return n_out.value, ws.value
+
+
+def attn_fwd_splitkv(Q: int, K: int, V: int, O: int, lse: int, B: int, H: int, N: int, d: int,
+                     scale: float, causal: bool, nsplit: int, workspace: int,
+                     workspace_bytes: int, stream: int = 0) -> None:
+    """bf16 attention forward over nsplit parallel key ranges; see include/osm.h."""
+    _call("attn_fwd_splitkv", Q, K, V, O, lse, B, H, N, d, scale, int(bool(causal)), nsplit,
+          workspace, workspace_bytes, stream)
+
+
+def attn_combine(O_part: int, lse_part: int, O: int, lse: int, S: int, B: int, H: int, N: int,
+                 d: int, stream: int = 0) -> None:
+    """Merge of S partial attention results; see include/osm.h."""
+    _call("attn_combine", O_part, lse_part, O, lse, S, B, H, N, d, stream)

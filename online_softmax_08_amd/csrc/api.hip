@@ -69,6 +69,13 @@ int validate_attn(const void* Q, const void* K, const void* V, const void* O, co
     return OSM_OK;
 }
 
+// Bytes of the split-KV workspace: fp32 partial outputs [nsplit][bh][N][d],
+// then the fp32 partial logsumexps [nsplit][bh][N].
+size_t splitkv_workspace(int nsplit, long long bh, int N, int d)
+{
+    return (size_t)nsplit * bh * N * ((size_t)d + 1) * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -108,6 +115,83 @@ int row_softmax(const float* x, float* y, int B, int N, void* stream)
     return finish(osm::launch_row_softmax(x, y, B, N, static_cast<hipStream_t>(stream)));
 }
 
+int attn_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int nsplit, int* nsplit_out,
+                          size_t* workspace_bytes)
+{
+    if (!nsplit_out || !workspace_bytes) return OSM_ERR_NULL;
+    if (B < 0 || H < 0 || N < 0) return OSM_ERR_SIZE;
+    if (d != 64 && d != 128) return OSM_ERR_HEAD_DIM;
+    if (nsplit < 0 || nsplit > osm::kMaxSplits) return OSM_ERR_SPLITS;
+    const long long bh = (long long)B * H;
+    if (bh > INT_MAX) return OSM_ERR_SIZE;
+    if (nsplit == 0) nsplit = (bh == 0 || N == 0) ? 1 : osm::attn_splitkv_auto((int)bh, N, d, causal != 0);
+    *nsplit_out = nsplit;
+    *workspace_bytes = nsplit == 1 ? 0 : splitkv_workspace(nsplit, bh, N, d);
+    return OSM_OK;
+}
+
+int attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* lse, int B,
+                     int H, int N, int d, float scale, int causal, int nsplit, void* workspace,
+                     size_t workspace_bytes, void* stream)
+{
+    bool work = false;
+    int st = validate_attn(Q, K, V, O, lse, B, H, N, d, scale, 2, &work);
+    if (st != OSM_OK) return st;
+    if (nsplit < 0 || nsplit > osm::kMaxSplits) return OSM_ERR_SPLITS;
+    if (!work) return OSM_OK;
+    const long long bh = (long long)B * H;
+    if (nsplit == 0) nsplit = osm::attn_splitkv_auto((int)bh, N, d, causal != 0);
+    if (nsplit == 1) {
+        if ((st = check_device()) != OSM_OK) return st;
+        return finish(osm::launch_attn_fwd_bf16(Q, K, V, O, lse, (int)bh, N, d, scale, causal != 0,
+                                                static_cast<hipStream_t>(stream)));
+    }
+    // The partial pass launches bh * ceil(N / 256) * nsplit workgroups of 512
+    // work-items, and a dispatch counts at most 2^32 - 1 work-items; offsets
+    // into one fp32 partial slice are 32-bit.
+    if (bh * ((N + 255) / 256) * nsplit * 512 > UINT32_MAX || (long long)N * d * 4 > UINT32_MAX)
+        return OSM_ERR_SIZE;
+    const size_t need = splitkv_workspace(nsplit, bh, N, d);
+    if (!workspace) return OSM_ERR_NULL;
+    if (workspace_bytes < need) return OSM_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return OSM_ERR_ALIGN;
+    const size_t tbytes = (size_t)bh * N * d * 2, lbytes = (size_t)bh * N * sizeof(float);
+    if (overlaps(workspace, need, Q, tbytes) || overlaps(workspace, need, K, tbytes) ||
+        overlaps(workspace, need, V, tbytes) || overlaps(workspace, need, O, tbytes) ||
+        overlaps(workspace, need, lse, lbytes))
+        return OSM_ERR_ALIAS;
+    if ((st = check_device()) != OSM_OK) return st;
+    float* opart = static_cast<float*>(workspace);
+    float* lpart = opart + (size_t)nsplit * bh * N * d;
+    return finish(osm::launch_attn_fwd_bf16_split(Q, K, V, O, lse, (int)bh, N, d, scale,
+                                                  causal != 0, nsplit, opart, lpart,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int attn_combine(const float* O_part, const float* lse_part, void* O, float* lse, int S, int B,
+                 int H, int N, int d, void* stream)
+{
+    if (B < 0 || H < 0 || N < 0) return OSM_ERR_SIZE;
+    if (d != 64 && d != 128) return OSM_ERR_HEAD_DIM;
+    if (S < 1 || S > osm::kMaxSplits) return OSM_ERR_SPLITS;
+    if (B == 0 || H == 0 || N == 0) return OSM_OK;
+    const long long rows = (long long)B * H * N;
+    if ((long long)B * H > INT_MAX) return OSM_ERR_SIZE;
+    if (!O_part || !lse_part || !O || !lse) return OSM_ERR_NULL;
+    if (!aligned(O_part, 16) || !aligned(lse_part, 4) || !aligned(O, 8) || !aligned(lse, 4))
+        return OSM_ERR_ALIGN;
+    const size_t pbytes = (size_t)S * rows * d * 4, plbytes = (size_t)S * rows * 4;
+    const size_t obytes = (size_t)rows * d * 2, lbytes = (size_t)rows * 4;
+    if (overlaps(O, obytes, O_part, pbytes) || overlaps(O, obytes, lse_part, plbytes) ||
+        overlaps(lse, lbytes, O_part, pbytes) || overlaps(lse, lbytes, lse_part, plbytes) ||
+        overlaps(lse, lbytes, O, obytes))
+        return OSM_ERR_ALIAS;
+    int st = check_device();
+    if (st != OSM_OK) return st;
+    return finish(osm::launch_attn_combine(O_part, lse_part, O, lse, S, rows, d,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 const char* osm_status_str(int status)
 {
     switch (status) {
@@ -120,6 +204,8 @@ const char* osm_status_str(int status)
     case OSM_ERR_ALIGN: return "a pointer is not aligned as required";
     case OSM_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
     case OSM_ERR_HIP: return "the HIP runtime reported an error";
+    case OSM_ERR_SPLITS: return "the number of key splits is out of range";
+    case OSM_ERR_WORKSPACE: return "the workspace is smaller than attn_fwd_splitkv_plan requires";
     default: return "unknown status";
     }
 }

@@ -117,11 +117,18 @@ struct Cfg {
     static_assert(KTILE_B % 1024 == 0 && VTILE_B % 1024 == 0, "tiles are whole wave loads");
 };
 
-template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL>
+// With SPLIT the key tiles of each query block are divided into nsplit
+// contiguous ranges, one workgroup per (query block, range), and each
+// workgroup writes the normalised partial output of its range in fp32 to
+// opart [nsplit][BH][N][D] and the partial logsumexp to lpart [nsplit][BH][N]
+// (-inf for a row that sees no key of the range); attn_combine_kernel merges
+// them.  O and lse are then unused.
+template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, __bf16* __restrict__ O,
-                     float* __restrict__ lse, int N, int BH, int nqt, float scale)
+                     float* __restrict__ lse, int N, int BH, int nqt, float scale,
+                     float* __restrict__ opart, float* __restrict__ lpart, int nsplit)
 {
     using C = Cfg<D, QT, NW, BC>;
     constexpr int NMT = BC / 32;  // 32-key MFMA tiles per key tile
@@ -138,7 +145,17 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int j = lane & 31, h = lane >> 5;
-    const int t = blockIdx.x / BH, bh = blockIdx.x - t * BH;
+    // Workgroup id = (t * nsplit + split) * BH + bh.
+    int t, bh, split = 0;
+    if constexpr (SPLIT) {
+        bh = blockIdx.x % BH;
+        const int rest = blockIdx.x / BH;
+        t = rest / nsplit;
+        split = rest - t * nsplit;
+    } else {
+        t = blockIdx.x / BH;
+        bh = blockIdx.x - t * BH;
+    }
     const int qt = CAUSAL ? nqt - 1 - t : t;
     const int q0 = qt * C::BR;
     const size_t base = (size_t)bh * N * D;
@@ -299,7 +316,9 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     auto probs = [&](f32x16 (&s)[NMT][QT], bf16x8 (&pf)[BC / 16][QT]) {
 #pragma unroll
         for (int nt = 0; nt < QT; ++nt) {
-            const float mc = m[nt] * c;
+            // A key range of a split can lie wholly in a row's future; that
+            // row keeps m = -inf and all its p must come out 0, not NaN.
+            const float mc = (SPLIT && m[nt] == kNegInf) ? 0.f : m[nt] * c;
             float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) {
@@ -342,9 +361,26 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     using B1 = std::integral_constant<int, 1>;
     const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
     const int ntiles = (kv_end + BC - 1) / BC;
-    // Tiles this wave computes: 0 .. wt - 1 (under the causal mask the later
-    // tiles of the workgroup lie wholly in this wave's future).
-    const int wt = CAUSAL ? min(ntiles, (qw0 + QT * 32 - 1) / BC + 1) : ntiles;
+    // Key tiles of this workgroup: t_lo .. t_hi - 1 (all of them, or split
+    // number `split` of nsplit near-equal ranges).
+    int t_lo = 0, t_hi = ntiles;
+    if constexpr (SPLIT) {
+        const int per = (ntiles + nsplit - 1) / nsplit;
+        t_lo = min(ntiles, split * per);
+        t_hi = min(ntiles, t_lo + per);
+        if (t_lo >= t_hi) {
+            // Empty range: only the -inf partial logsumexp of every row.
+            const __amdgpu_buffer_rsrc_t lrs =
+                make_rsrc(lpart + ((size_t)split * BH + bh) * N, (uint32_t)N * 4);
+            for (int r = tid; r < C::BR; r += C::T)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(kNegInf), lrs,
+                                                      (uint32_t)(q0 + r) * 4, 0, 0);
+            return;
+        }
+    }
+    // Tiles this wave computes: t_lo .. wt - 1 (under the causal mask the
+    // later tiles of the workgroup lie wholly in this wave's future).
+    const int wt = CAUSAL ? min(t_hi, (qw0 + QT * 32 - 1) / BC + 1) : t_hi;
 
     auto compute = [&](auto bufc, int kt) {
         if (kt >= wt) return;
@@ -355,18 +391,46 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         probs(s, pf);
         pv(bufc, pf);
     };
-    issue(B0{}, 0);
+    issue(B0{}, t_lo);
     __syncthreads();  // waits for the tile loads (vmcnt) before publishing
-    for (int kt = 0; kt < ntiles; kt += 2) {
+    for (int kt = t_lo; kt < t_hi; kt += 2) {
         // even tile: compute buffer 0 while tile kt + 1 streams into buffer 1
-        if (kt + 1 < ntiles) issue(B1{}, kt + 1);
+        if (kt + 1 < t_hi) issue(B1{}, kt + 1);
         compute(B0{}, kt);
         __syncthreads();
-        if (kt + 1 >= ntiles) break;
+        if (kt + 1 >= t_hi) break;
         // odd tile: compute buffer 1 while tile kt + 2 streams into buffer 0
-        if (kt + 2 < ntiles) issue(B0{}, kt + 2);
+        if (kt + 2 < t_hi) issue(B0{}, kt + 2);
         compute(B1{}, kt + 1);
         __syncthreads();
+    }
+
+    if constexpr (SPLIT) {
+        // ---- partial epilogue: fp32 acc / l and m scale + ln l of this key
+        // range; a row that saw no key of it gets O = 0 and -inf ----
+        const size_t pslice = (size_t)split * BH + bh;
+        const __amdgpu_buffer_rsrc_t ors = make_rsrc(opart + pslice * N * D, (uint32_t)N * D * 4);
+        const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lpart + pslice * N, (uint32_t)N * 4);
+#pragma unroll
+        for (int nt = 0; nt < QT; ++nt) {
+            const int q = qw0 + nt * 32 + j;
+            const float l_tot = combine_xor32(l[nt], SumOp());
+            const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 o4 = {acc[nt][dt][4 * g] * inv, acc[nt][dt][4 * g + 1] * inv,
+                                      acc[nt][dt][4 * g + 2] * inv, acc[nt][dt][4 * g + 3] * inv};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), ors,
+                                                           (uint32_t)(q * D + dt * 32 + 8 * g + 4 * h) * 4, 0, 0);
+                }
+            if (h == 0) {
+                const float ls = l_tot > 0.f ? m[nt] * scale + logf(l_tot) : kNegInf;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ls), lrs, (uint32_t)q * 4, 0, 0);
+            }
+        }
+        return;
     }
 
     // ---- epilogue: O = acc / l in bf16 (rows past N dropped), lse = m scale + ln l ----
@@ -692,9 +756,9 @@ hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* l
     using C = Cfg<D, QT, NW, BC>;
     const int nqt = (N + C::BR - 1) / C::BR;
     const dim3 grid((unsigned)(nqt * BH)), block(C::T);
-    attn_fwd_bf16_kernel<D, QT, NW, WPE, BC, CAUSAL><<<grid, block, 0, stream>>>(
+    attn_fwd_bf16_kernel<D, QT, NW, WPE, BC, CAUSAL, false><<<grid, block, 0, stream>>>(
         static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
-        static_cast<__bf16*>(O), lse, N, BH, nqt, scale);
+        static_cast<__bf16*>(O), lse, N, BH, nqt, scale, nullptr, nullptr, 1);
     return hipGetLastError();
 }
 
@@ -720,7 +784,115 @@ hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float*
     return launch<D, 1, 2, 2, 64, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
 }
 
+// Merge of split partials, one row per D / 4 lanes (four fp32 columns per
+// lane).  The partials are folded in one pass with the merge rule of Lesson
+// 22, section 22: keep the largest partial logsumexp M seen so far, scale
+// what was accumulated by e^(M_old - M_new) when it grows, and add each
+// partial output with weight e^(lse_s - M).  At the end
+// O = sum_s e^(lse_s - M) O_s / sum_s e^(lse_s - M) and
+// lse = M + ln sum_s e^(lse_s - M).  Partials with lse_s = -inf are empty and
+// skipped without reading their O_s; a row with no non-empty partial gets
+// O = 0 and lse = -inf.  Rows are walked grid-stride.
+template <int D>
+__global__ void __launch_bounds__(256)
+attn_combine_kernel(const float* __restrict__ opart, const float* __restrict__ lpart,
+                    __bf16* __restrict__ O, float* __restrict__ lse, int S, long long rows)
+{
+    constexpr int LPR = D / 4;         // lanes per row
+    constexpr int RPB = 256 / LPR;     // rows per workgroup and pass
+    const int c4 = threadIdx.x % LPR;  // column group of this lane
+    for (long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR; row < rows;
+         row += (long long)gridDim.x * RPB) {
+        float M = kNegInf, l = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < S; ++s) {
+            const size_t pr = (size_t)s * rows + row;
+            const float ls = lpart[pr];
+            if (ls == kNegInf) continue;
+            const f32x4 o = *reinterpret_cast<const f32x4*>(opart + pr * D + 4 * c4);
+            if (ls > M) {
+                const float a = exp2_hw((M - ls) * kLog2e);  // M = -inf gives 0
+                acc *= a;
+                l *= a;
+                M = ls;
+            }
+            const float w = exp2_hw((ls - M) * kLog2e);
+            acc += w * o;
+            l += w;
+        }
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        const bf16x4 ob = __builtin_convertvector(acc * inv, bf16x4);
+        *reinterpret_cast<bf16x4*>(O + (size_t)row * D + 4 * c4) = ob;
+        if (c4 == 0) lse[row] = l > 0.f ? M + logf(l) : kNegInf;
+    }
+}
+
+// Split-KV forward: 8-wave workgroups (256 query rows) over nsplit key ranges
+// each, then the merge.
+template <int D, bool CAUSAL>
+hipError_t launch_split(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
+                        int N, float scale, int nsplit, float* opart, float* lpart,
+                        hipStream_t stream)
+{
+    using C = Cfg<D, 1, 8, 64>;
+    const int nqt = (N + C::BR - 1) / C::BR;
+    attn_fwd_bf16_kernel<D, 1, 8, 2, 64, CAUSAL, true>
+        <<<dim3((unsigned)(nqt * nsplit * BH)), dim3(C::T), 0, stream>>>(
+            static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K),
+            static_cast<const __bf16*>(V), nullptr, nullptr, N, BH, nqt, scale, opart, lpart,
+            nsplit);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_attn_combine(opart, lpart, O, lse, nsplit, (long long)BH * N, D, stream);
+}
+
 }  // namespace
+
+hipError_t launch_attn_combine(const float* opart, const float* lpart, void* O, float* lse, int S,
+                               long long rows, int d, hipStream_t stream)
+{
+    // Enough workgroups for several per CU; larger problems loop.
+    const int rpb = 256 / (d / 4);
+    const long long need = (rows + rpb - 1) / rpb;
+    const dim3 grid((unsigned)(need < 65536 ? need : 65536)), block(256);
+    if (d == 64)
+        attn_combine_kernel<64><<<grid, block, 0, stream>>>(opart, lpart, static_cast<__bf16*>(O),
+                                                            lse, S, rows);
+    else
+        attn_combine_kernel<128><<<grid, block, 0, stream>>>(opart, lpart, static_cast<__bf16*>(O),
+                                                             lse, S, rows);
+    return hipGetLastError();
+}
+
+int attn_splitkv_auto(int BH, int N, int d, bool causal)
+{
+    // Every wave of the single pass owns 32 query rows; 2048 waves (two per
+    // SIMD on 256 CUs) keep both the matrix core and the vector unit of every
+    // SIMD busy.  Below that, split the keys so that the partial pass reaches
+    // 2048 waves, twice that under the causal mask (its query blocks differ
+    // in length, and more, shorter ranges even them out), with at least 512
+    // keys per range.  Rows shorter than 2048 keys are not split: there the
+    // fp32 partials cost as much HBM time as the occupancy gains.
+    (void)d;
+    const long long rows = (long long)BH * N;
+    if (N < 2048 || rows >= 65536) return 1;
+    long long s = (65536 * (causal ? 2 : 1) + rows - 1) / rows;
+    const long long cap = N / 512;
+    if (s > cap) s = cap;
+    if (s > 16) s = 16;
+    return s < 1 ? 1 : (int)s;
+}
+
+hipError_t launch_attn_fwd_bf16_split(const void* Q, const void* K, const void* V, void* O,
+                                      float* lse, int BH, int N, int d, float scale, bool causal,
+                                      int nsplit, float* opart, float* lpart, hipStream_t stream)
+{
+    if (d == 64)
+        return causal ? launch_split<64, true>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, stream)
+                      : launch_split<64, false>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, stream);
+    return causal ? launch_split<128, true>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, stream)
+                  : launch_split<128, false>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, stream);
+}
 
 hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, void* O,
                                 float* lse, int BH, int N, int d, float scale, bool causal,

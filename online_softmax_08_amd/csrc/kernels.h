@@ -17,6 +17,18 @@ hipError_t launch_row_softmax(const float* x, float* y, int B, int N, hipStream_
 hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, void* O,
                                 float* lse, int BH, int N, int d, float scale, bool causal,
                                 hipStream_t stream);
+// Split-KV forward.  opart: fp32 [nsplit][B*H][N][d], lpart: fp32
+// [nsplit][B*H][N] (workspace); 1 <= nsplit <= kMaxSplits.
+constexpr int kMaxSplits = 64;
+hipError_t launch_attn_fwd_bf16_split(const void* Q, const void* K, const void* V, void* O,
+                                      float* lse, int BH, int N, int d, float scale, bool causal,
+                                      int nsplit, float* opart, float* lpart, hipStream_t stream);
+// The number of key ranges the split-KV forward picks when asked to choose.
+int attn_splitkv_auto(int BH, int N, int d, bool causal);
+// Merge of S partials (opart [S][rows][d] fp32, lpart [S][rows]) into O (bf16
+// [rows][d]) and lse ([rows]).
+hipError_t launch_attn_combine(const float* opart, const float* lpart, void* O, float* lse, int S,
+                               long long rows, int d, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const float* Q, const float* K, const float* V, float* O,
                                float* lse, int BH, int N, int d, float scale, bool causal,
                                hipStream_t stream);

@@ -49,6 +49,59 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     return out, lse
 
 
+def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                      scale: float | None = None, nsplit: int = 0,
+                      workspace: torch.Tensor | None = None):
+    """attention() for bf16 with the keys split into nsplit parallel ranges and
+    the partial results merged (nsplit 0: the library's choice).
+
+    ``workspace`` (optional) is a device uint8 tensor of at least the planned
+    size; otherwise one is allocated.  Returns (O bf16, lse fp32 [B, H, N]).
+    """
+    _check_attn(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("split-KV attention takes bfloat16 q, k, v")
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    ns, ws_bytes = _abi.attn_fwd_splitkv_plan(B, H, N, d, causal, nsplit)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        _abi.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), B, H, N, d, scale, causal, ns,
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              _stream_handle(q.device))
+    return out, lse
+
+
+def attention_combine(o_part: torch.Tensor, lse_part: torch.Tensor):
+    """Merge partial attention results over disjoint key sets.
+
+    o_part: contiguous fp32 [S, B, H, N, d] (each normalised over its keys);
+    lse_part: contiguous fp32 [S, B, H, N] (-inf: the partial saw no key).
+    Returns (O bf16 [B, H, N, d], lse fp32 [B, H, N]).
+    """
+    if not (o_part.is_cuda and lse_part.is_cuda):
+        raise ValueError("o_part and lse_part must be GPU tensors")
+    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
+        raise ValueError("o_part and lse_part must be float32")
+    if o_part.dim() != 5 or tuple(lse_part.shape) != tuple(o_part.shape[:4]):
+        raise ValueError("o_part must be [S, B, H, N, d] and lse_part [S, B, H, N]")
+    if not (o_part.is_contiguous() and lse_part.is_contiguous()):
+        raise ValueError("o_part and lse_part must be contiguous")
+    S, B, H, N, d = o_part.shape
+    out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=o_part.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=o_part.device)
+    with torch.cuda.device(o_part.device):
+        _abi.attn_combine(o_part.data_ptr(), lse_part.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          S, B, H, N, d, _stream_handle(o_part.device))
+    return out, lse
+
+
 def softmax(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Stable softmax over the last dimension of a contiguous fp32 [B, N] GPU tensor.
     ``out`` may be ``x`` itself (in place)."""

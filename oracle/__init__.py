@@ -66,8 +66,9 @@ class Oracle:
         lib.oracle_online_row_trace.argtypes = [_dp, _L, _L, _dp, _dp]
         lib.oracle_attn_online.argtypes = [_dp, _dp, _dp, _dp, _dp, _L, _L, _L, _L,
                                            ctypes.c_double, ctypes.c_int, _L, _L]
+        lib.oracle_attn_merge.argtypes = [_dp, _dp, _dp, _dp, _L, _L, _L]
         for name in ("oracle_row_softmax", "oracle_attn_fwd", "oracle_attn_rows",
-                     "oracle_online_row_trace", "oracle_attn_online"):
+                     "oracle_online_row_trace", "oracle_attn_online", "oracle_attn_merge"):
             getattr(lib, name).restype = ctypes.c_int
         self._lib = lib
 
@@ -150,6 +151,23 @@ class Oracle:
                "attn_online")
         return O, lse
 
+    def attn_merge(self, O_part, lse_part):
+        """Merge of partial results over disjoint key sets, joined one by one
+        with the rule of Lesson 22, section 22 (each normalised partial taken
+        as the state m = lse_s, l = 1, a = O_s).  O_part [S, ..., d],
+        lse_part [S, ...]; returns (O [..., d], lse [...])."""
+        O_part, lse_part = _f64(O_part), _f64(lse_part)
+        if O_part.ndim < 2 or lse_part.shape != O_part.shape[:-1]:
+            raise ValueError("O_part must be [S, ..., d] and lse_part [S, ...]")
+        S, d = O_part.shape[0], O_part.shape[-1]
+        lead = O_part.shape[1:-1]
+        rows = int(np.prod(lead)) if lead else 1
+        O = np.empty(lead + (d,), dtype=np.float64)
+        lse = np.empty(lead, dtype=np.float64)
+        _check(self._lib.oracle_attn_merge(_ptr(O_part), _ptr(lse_part), _ptr(O), _ptr(lse),
+                                           S, rows, d), "attn_merge")
+        return O, lse
+
 
 _default: Oracle | None = None
 
@@ -187,3 +205,7 @@ def online_row_trace(x, bc):
 
 def attn_online(Q, K, V, scale, causal, br, bc):
     return default().attn_online(Q, K, V, scale, causal, br, bc)
+
+
+def attn_merge(O_part, lse_part):
+    return default().attn_merge(O_part, lse_part)

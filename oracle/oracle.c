@@ -329,3 +329,61 @@ int oracle_attn_online(const double *Q, const double *K, const double *V,
     }
     return failed ? -2 : 0;
 }
+
+/* ------------------------------------------------------------------------ *
+ * Merge of S partial attention results over disjoint key sets ([L22]
+ * section 22: two partial states (m_A, l_A, a_A) and (m_B, l_B, a_B) of one
+ * row join as m = max(m_A, m_B), l = e^(m_A - m) l_A + e^(m_B - m) l_B,
+ * a = e^(m_A - m) a_A + e^(m_B - m) a_B, and o = a / l; [FUS], the risks
+ * list, item 6, for partials kept as accumulated lse and output).
+ * Partial s of a row is given normalised, as o_s and lse_s = m_s + ln l_s.
+ * Taking lse_s itself as the reference, the same partial is the state
+ * (m = lse_s, l = 1, a = o_s); the partials are joined into a running state
+ * one after another, s = 0 .. S-1, and the result is o = a / l,
+ * lse = m + ln l.  A partial with lse_s = -inf saw no key: it is the empty
+ * state and is skipped (its o_s is not read).  A row whose every partial is
+ * empty gets o = 0 and lse = -inf.
+ *   Opart: [S][rows][d], lpart: [S][rows]; O: [rows][d], lse: [rows].
+ * ------------------------------------------------------------------------ */
+int oracle_attn_merge(const double *Opart, const double *lpart, double *O,
+                      double *lse, long S, long rows, long d)
+{
+    if (S < 1 || rows < 0 || d < 1) return -1;
+    if (rows == 0) return 0;
+    if (!Opart || !lpart || !O || !lse) return -1;
+    int failed = 0;
+#pragma omp parallel reduction(|| : failed)
+    {
+        double *a = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!a) {
+            failed = 1;
+        } else {
+            long r;
+#pragma omp for schedule(static)
+            for (r = 0; r < rows; ++r) {
+                double m = -INFINITY, l = 0.0;
+                for (long t = 0; t < d; ++t) a[t] = 0.0;
+                for (long s = 0; s < S; ++s) {
+                    double m_b = lpart[s * rows + r];
+                    if (m_b == -INFINITY) continue;
+                    const double *a_b = Opart + (s * rows + r) * d; /* l_b = 1 */
+                    double m_new = m > m_b ? m : m_b;
+                    double wa = (m == -INFINITY) ? 0.0 : exp(m - m_new);
+                    double wb = exp(m_b - m_new);
+                    l = wa * l + wb * 1.0;
+                    for (long t = 0; t < d; ++t) a[t] = wa * a[t] + wb * a_b[t];
+                    m = m_new;
+                }
+                if (m == -INFINITY) {
+                    for (long t = 0; t < d; ++t) O[r * d + t] = 0.0;
+                    lse[r] = -INFINITY;
+                    continue;
+                }
+                for (long t = 0; t < d; ++t) O[r * d + t] = a[t] / l;
+                lse[r] = m + log(l);
+            }
+        }
+        free(a);
+    }
+    return failed ? -2 : 0;
+}

@@ -382,4 +382,73 @@ def pin_online_trace_final_state(orc):
                    what=f"online trace n={n} bc={bc}")
 
 
+def pin_merge_key_shards(orc):
+    # Attention over the union of disjoint key sets, computed whole, equals the
+    # merge of the attention over each set (Lesson 22, section 22).  Three
+    # shards of N keys each: the whole problem stacks the query block three
+    # times so the definition can be evaluated with equal query and key
+    # counts; its first N rows are the queries of every shard.
+    rng = _rng(31)
+    for N, d in ((1, 1), (5, 3), (16, 8)):
+        Q, _, _ = _rand_attn(rng, 1, 2, N, d)
+        shards = [_rand_attn(rng, 1, 2, N, d, std=1.0 + 2.0 * s)[1:] for s in range(3)]
+        Kall = np.concatenate([k for k, _ in shards], axis=2)
+        Vall = np.concatenate([v for _, v in shards], axis=2)
+        O, lse = orc.attn_fwd(np.concatenate([Q] * 3, axis=2), Kall, Vall, 0.7, False)
+        parts = [orc.attn_fwd(Q, k, v, 0.7, False) for k, v in shards]
+        Om, lsem = orc.attn_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+        _close(Om, O[:, :, :N], 1e-12, 1e-12, what=f"merged O N={N} d={d}")
+        _close(lsem, lse[:, :, :N], 1e-12, 1e-12, what=f"merged lse N={N} d={d}")
+
+
+def pin_merge_causal_halves(orc):
+    # Causal attention with the keys cut at c = N / 2.  Keys 0..c-1: rows
+    # below c see them causally, rows from c on see all of them; keys c..N-1:
+    # rows from c on see them causally (the same problem shifted by c), rows
+    # below c see none (lse -inf, output left as NaN: it must not be read).
+    rng = _rng(32)
+    for N, d in ((2, 1), (8, 4), (32, 8)):
+        c = N // 2
+        Q, K, V = _rand_attn(rng, 1, 2, N, d, std=1.5)
+        O, lse = orc.attn_fwd(Q, K, V, 0.9, True)
+        o0 = np.full_like(O, np.nan)
+        l0 = np.full_like(lse, np.nan)
+        o1 = np.full_like(O, np.nan)
+        l1 = np.full_like(lse, -np.inf)
+        o0[:, :, :c], l0[:, :, :c] = orc.attn_fwd(Q[:, :, :c], K[:, :, :c], V[:, :, :c], 0.9, True)
+        o0[:, :, c:], l0[:, :, c:] = orc.attn_fwd(Q[:, :, c:], K[:, :, :c], V[:, :, :c], 0.9, False)
+        o1[:, :, c:], l1[:, :, c:] = orc.attn_fwd(Q[:, :, c:], K[:, :, c:], V[:, :, c:], 0.9, True)
+        Om, lsem = orc.attn_merge(np.stack([o0, o1]), np.stack([l0, l1]))
+        _close(Om, O, 1e-12, 1e-12, what=f"causal merged O N={N}")
+        _close(lsem, lse, 1e-12, 1e-12, what=f"causal merged lse N={N}")
+
+
+def pin_merge_special_cases(orc):
+    # One partial merges to itself; empty partials (-inf) change nothing and
+    # their outputs are never read; a row with only empty partials is O = 0,
+    # lse = -inf; the order of the partials does not matter.
+    rng = _rng(33)
+    o = rng.standard_normal((2, 3, 4))
+    l = rng.standard_normal((2, 3)) * 5.0
+    Om, lsem = orc.attn_merge(o[None], l[None])
+    assert np.array_equal(Om, o) and np.array_equal(lsem, l), "single partial must merge to itself"
+    empty_o = np.full_like(o, np.nan)
+    empty_l = np.full_like(l, -np.inf)
+    Om, lsem = orc.attn_merge(np.stack([empty_o, o, empty_o]), np.stack([empty_l, l, empty_l]))
+    assert np.array_equal(Om, o) and np.array_equal(lsem, l), "empty partials must change nothing"
+    Om, lsem = orc.attn_merge(np.stack([empty_o, empty_o]), np.stack([empty_l, empty_l]))
+    assert np.all(Om == 0.0) and np.all(lsem == -np.inf), "all-empty row must be O = 0, -inf"
+    parts_o = rng.standard_normal((5, 2, 3, 4))
+    parts_l = rng.standard_normal((5, 2, 3)) * 4.0
+    O1, l1 = orc.attn_merge(parts_o, parts_l)
+    perm = [3, 0, 4, 2, 1]
+    O2, l2 = orc.attn_merge(parts_o[perm], parts_l[perm])
+    _close(O2, O1, 1e-13, 1e-13, what="merge order O")
+    _close(l2, l1, 1e-13, 1e-13, what="merge order lse")
+    # Two equal partials: same output, lse grows by ln 2.
+    O3, l3 = orc.attn_merge(np.stack([o, o]), np.stack([l, l]))
+    _close(O3, o, 1e-14, 1e-14, what="equal partials O")
+    _close(l3, l + math.log(2.0), 1e-14, 1e-14, what="equal partials lse")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

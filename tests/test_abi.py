@@ -23,7 +23,8 @@ def abi():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "row_softmax",
+    assert _declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_splitkv_plan",
+                                            "attn_fwd_splitkv", "attn_combine", "row_softmax",
                                             "osm_status_str"])
 
 
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_symbol(abi):
 
 
 def test_status_strings(abi):
-    for st in range(0, 9):
+    for st in range(0, 11):
         assert abi.osm_status_str(st) and abi.osm_status_str(st) != "unknown status"
     assert abi.osm_status_str(99) == "unknown status"
 
@@ -97,3 +98,86 @@ def test_valid_call_without_a_gpu_fails_loudly(abi):
     with pytest.raises(abi.OsmError) as e:
         abi.attn_fwd(FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 5 * FAKE, 1, 1, 16, 64, 0.125, 0)
     assert e.value.status in (abi.OSM_ERR_HIP, abi.OSM_ERR_DEVICE)
+
+
+def test_splitkv_plan(abi):
+    # Explicit counts are kept; the workspace holds nsplit fp32 partial
+    # outputs and logsumexps per row, none when the count is 1.
+    assert abi.attn_fwd_splitkv_plan(2, 8, 1024, 64, False, 1) == (1, 0)
+    assert abi.attn_fwd_splitkv_plan(2, 8, 1024, 64, False, 3) == (3, 3 * 16 * 1024 * 65 * 4)
+    assert abi.attn_fwd_splitkv_plan(1, 2, 777, 128, True, 64) == (64, 64 * 2 * 777 * 129 * 4)
+    # Automatic choice: no split once 256-row blocks fill the 256 CUs ...
+    assert abi.attn_fwd_splitkv_plan(2, 16, 4096, 128, True, 0) == (1, 0)
+    assert abi.attn_fwd_splitkv_plan(1, 32, 8192, 128, True, 0) == (1, 0)
+    # ... below that, a split that brings the partial pass to 2048 waves of
+    # 32 rows (twice that under the causal mask), at least 512 keys per range ...
+    ns, ws = abi.attn_fwd_splitkv_plan(1, 2, 8192, 128, False, 0)
+    assert ns == 4 and ws == 4 * 2 * 8192 * 129 * 4
+    assert abi.attn_fwd_splitkv_plan(1, 2, 8192, 128, True, 0)[0] == 8
+    assert abi.attn_fwd_splitkv_plan(1, 1, 32768, 64, False, 0)[0] == 2
+    assert abi.attn_fwd_splitkv_plan(1, 1, 32768, 64, True, 0)[0] == 4
+    assert abi.attn_fwd_splitkv_plan(1, 8, 2048, 128, True, 0)[0] == 4
+    assert abi.attn_fwd_splitkv_plan(1, 1, 65536, 64, True, 0) == (1, 0)
+    # ... and none for rows under 2048 keys or empty problems.
+    assert abi.attn_fwd_splitkv_plan(1, 1, 256, 64, False, 0) == (1, 0)
+    assert abi.attn_fwd_splitkv_plan(2, 8, 1024, 64, False, 0) == (1, 0)
+    assert abi.attn_fwd_splitkv_plan(0, 4, 4096, 64, False, 0) == (1, 0)
+    for bad, st in (((1, 1, 64, 96, False, 2), abi.OSM_ERR_HEAD_DIM),
+                    ((1, 1, 64, 64, False, 65), abi.OSM_ERR_SPLITS),
+                    ((1, 1, 64, 64, False, -1), abi.OSM_ERR_SPLITS),
+                    ((-1, 1, 64, 64, False, 2), abi.OSM_ERR_SIZE)):
+        with pytest.raises(abi.OsmError) as e:
+            abi.attn_fwd_splitkv_plan(*bad)
+        assert e.value.status == st
+
+
+def _splitkv_status(abi, nsplit=2, ws=6 * FAKE, ws_bytes=None, **kw):
+    args = dict(Q=FAKE, K=2 * FAKE, V=3 * FAKE, O=4 * FAKE, lse=5 * FAKE, B=1, H=1, N=16, d=64,
+                scale=0.125, causal=0)
+    args.update(kw)
+    if ws_bytes is None:
+        ws_bytes = 1 << 40  # ample; the overlap checks use the bytes actually needed
+    with pytest.raises(abi.OsmError) as e:
+        abi.attn_fwd_splitkv(args["Q"], args["K"], args["V"], args["O"], args["lse"], args["B"],
+                             args["H"], args["N"], args["d"], args["scale"], args["causal"],
+                             nsplit, ws, ws_bytes)
+    return e.value.status
+
+
+def test_splitkv_validation(abi):
+    # The shared attention checks come first ...
+    assert _splitkv_status(abi, d=80) == abi.OSM_ERR_HEAD_DIM
+    assert _splitkv_status(abi, scale=0.0) == abi.OSM_ERR_SCALE
+    assert _splitkv_status(abi, O=FAKE) == abi.OSM_ERR_ALIAS
+    # ... then the split count and the workspace.
+    assert _splitkv_status(abi, nsplit=65, ws_bytes=0) == abi.OSM_ERR_SPLITS
+    assert _splitkv_status(abi, nsplit=-2, ws_bytes=0) == abi.OSM_ERR_SPLITS
+    assert _splitkv_status(abi, ws=0) == abi.OSM_ERR_NULL
+    need = abi.attn_fwd_splitkv_plan(1, 1, 16, 64, False, 2)[1]
+    assert _splitkv_status(abi, ws_bytes=need - 1) == abi.OSM_ERR_WORKSPACE
+    assert _splitkv_status(abi, ws=6 * FAKE + 4) == abi.OSM_ERR_ALIGN
+    assert _splitkv_status(abi, ws=4 * FAKE) == abi.OSM_ERR_ALIAS          # workspace is O
+    assert _splitkv_status(abi, ws=FAKE - 64) == abi.OSM_ERR_ALIAS         # runs into Q
+    # N * d * 4 bytes of one fp32 partial slice must fit in 32 bits.
+    far = {n: (i + 1) << 40 for i, n in enumerate(("Q", "K", "V", "O", "lse"))}
+    assert _splitkv_status(abi, N=1 << 23, d=128, ws=6 << 40, ws_bytes=1 << 45,
+                           **far) == abi.OSM_ERR_SIZE
+    # Empty problems are a no-op with any pointers.
+    abi.attn_fwd_splitkv(0, 0, 0, 0, 0, 0, 4, 128, 64, 0.125, 1, 4, 0, 0)
+
+
+def test_combine_validation(abi):
+    def status(Op=FAKE, Lp=2 * FAKE, O=3 * FAKE, lse=4 * FAKE, S=2, B=1, H=1, N=16, d=64):
+        with pytest.raises(abi.OsmError) as e:
+            abi.attn_combine(Op, Lp, O, lse, S, B, H, N, d)
+        return e.value.status
+    assert status(d=32) == abi.OSM_ERR_HEAD_DIM
+    assert status(S=0) == abi.OSM_ERR_SPLITS
+    assert status(S=65) == abi.OSM_ERR_SPLITS
+    assert status(N=-1) == abi.OSM_ERR_SIZE
+    assert status(Op=0) == abi.OSM_ERR_NULL
+    assert status(Op=FAKE + 8) == abi.OSM_ERR_ALIGN
+    assert status(O=3 * FAKE + 4) == abi.OSM_ERR_ALIGN
+    assert status(O=FAKE + 1024) == abi.OSM_ERR_ALIAS      # O inside the partial outputs
+    assert status(lse=3 * FAKE + 64) == abi.OSM_ERR_ALIAS  # lse inside O
+    abi.attn_combine(0, 0, 0, 0, 3, 1, 0, 16, 64)          # empty: a valid no-op

@@ -1,0 +1,165 @@
+"""GPU parity of the split-KV forward and of the partial merge, through the C
+ABI, against the fp64 oracle on seeded inputs.
+
+Split-KV output: the same tolerance as attn_fwd (bf16: 2e-2 on O, 1e-3 on
+lse), since it computes the same exact attention.  The merge alone is fp32
+arithmetic on fp32 partials, compared with the oracle's merge of the very same
+partials: lse within 1e-5, O within one bf16 rounding (2^-8 relative to the
+largest |O| of the case) plus 1e-6.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from online_softmax_08_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_O, TOL_LSE = 2e-2, 1e-3
+
+
+@pytest.fixture(scope="module")
+def osm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import online_softmax_08_amd
+    return online_softmax_08_amd
+
+
+def _maxabs(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def _inputs(B, H, N, d, seed):
+    base = inputs.ATTN["attn_bf16_B2H8N1024d64" if d == 64 else "attn_bf16_B4H16N2048d128"]
+    return inputs.attn_inputs(base, B=B, H=H, N=N, d=d, seed=seed)
+
+
+def _gpu_split(osm, q, k, v, causal, nsplit):
+    dev = torch.device("cuda:0")
+    O, lse = osm.attention_splitkv(q.to(dev), k.to(dev), v.to(dev), causal=causal, nsplit=nsplit)
+    torch.cuda.synchronize()
+    return O.to(torch.float64).cpu().numpy(), lse.to(torch.float64).cpu().numpy()
+
+
+# Full comparison: ragged N, both head sizes and masks, split counts that give
+# ranges of one or several tiles, uneven ranges, and (16, 64) empty ranges.
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape,nsplit", [((1, 2, 1000, 64), 2), ((1, 2, 1000, 64), 3),
+                                          ((1, 2, 1000, 64), 7), ((1, 2, 1000, 64), 16),
+                                          ((2, 1, 777, 128), 5), ((2, 1, 777, 128), 64),
+                                          ((1, 1, 65, 128), 2), ((1, 3, 1, 64), 4)])
+def test_splitkv_full(osm, shape, nsplit, causal):
+    B, H, N, d = shape
+    q, k, v = _inputs(B, H, N, d, seed=1000 + N + d + nsplit)
+    print(f"splitkv B{B}H{H}N{N}d{d} causal={causal} nsplit={nsplit}", flush=True)
+    O, lse = _gpu_split(osm, q, k, v, causal, nsplit)
+    Oref, lref = oracle.attn_fwd(q, k, v, 1.0 / math.sqrt(d), causal)
+    eo, el = _maxabs(O, Oref), _maxabs(lse, lref)
+    print(f"  max|dO|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse))
+    assert eo <= TOL_O and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_splitkv_small_workload(osm, causal):
+    # The 2 x 8 x 1024 x 64 workload: the library does not split rows this
+    # short, and an explicit split of 2 still matches the oracle in full.
+    w = inputs.ATTN["attn_bf16_B2H8N1024d64"]
+    assert osm.attn_fwd_splitkv_plan(w.B, w.H, w.N, w.d, causal, 0)[0] == 1
+    q, k, v = inputs.attn_inputs(w)
+    print(f"{w.describe()} causal={causal} nsplit=2", flush=True)
+    O, lse = _gpu_split(osm, q, k, v, causal, 2)
+    Oref, lref = oracle.attn_fwd(q, k, v, w.scale, causal)
+    eo, el = _maxabs(O, Oref), _maxabs(lse, lref)
+    print(f"  max|dO|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    assert eo <= TOL_O and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 2, 8192, 128), (1, 1, 16384, 64)])
+def test_splitkv_long_rows_sampled(osm, shape, causal):
+    # Long rows and few heads, the case split-KV exists for, with the split
+    # count the library picks.  Every row finite and within the value range;
+    # sampled rows (first, last, range boundaries, random) against the oracle.
+    B, H, N, d = shape
+    ns, _ = osm.attn_fwd_splitkv_plan(B, H, N, d, causal, 0)
+    assert ns > 1
+    q, k, v = _inputs(B, H, N, d, seed=2000 + N + d)
+    print(f"splitkv B{B}H{H}N{N}d{d} causal={causal} auto nsplit={ns}", flush=True)
+    O, lse = _gpu_split(osm, q, k, v, causal, 0)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse))
+    vf = v.to(torch.float32)
+    assert np.all(O >= vf.amin(dim=2, keepdim=True).numpy() - 2e-2)
+    assert np.all(O <= vf.amax(dim=2, keepdim=True).numpy() + 2e-2)
+    rng = np.random.default_rng(N + causal)
+    rows = sorted({0, 1, 63, 64, 255, 256, 511, 512, 1023, 1024, N // 2, N - 257, N - 256, N - 1,
+                   *rng.choice(N, size=24, replace=False).tolist()})
+    bh = np.array([s for s in range(B * H) for _ in rows])
+    qi = np.array(rows * (B * H))
+    Oref, lref = oracle.attn_rows(q, k, v, 1.0 / math.sqrt(d), causal, bh, qi)
+    eo = _maxabs(O.reshape(B * H, N, d)[bh, qi], Oref)
+    el = _maxabs(lse.reshape(B * H, N)[bh, qi], lref)
+    print(f"  {len(qi)} rows max|dO|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    assert eo <= TOL_O and el <= TOL_LSE
+
+
+def test_splitkv_deterministic_and_one_split_is_attn_fwd(osm):
+    q, k, v = _inputs(1, 2, 3000, 128, seed=77)
+    dev = torch.device("cuda:0")
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    O1, l1 = osm.attention_splitkv(q, k, v, causal=True, nsplit=6)
+    O2, l2 = osm.attention_splitkv(q, k, v, causal=True, nsplit=6)
+    # One split is the single-pass forward itself.
+    O3, l3 = osm.attention_splitkv(q, k, v, causal=True, nsplit=1)
+    O4, l4 = osm.attention(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(l1, l2)
+    assert torch.equal(O3, O4) and torch.equal(l3, l4)
+
+
+def _oracle_partials(q, k, v, shards, scale):
+    # Partials over disjoint key sets of a non-causal problem, from the oracle
+    # (each shard holds as many keys as there are queries), rounded to fp32.
+    parts = [oracle.attn_fwd(q, k[:, :, s], v[:, :, s], scale, False) for s in shards]
+    Op = np.stack([p[0] for p in parts]).astype(np.float32)
+    Lp = np.stack([p[1] for p in parts]).astype(np.float32)
+    return Op, Lp
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_combine_against_oracle_merge(osm, d):
+    B, H, N, S = 2, 3, 300, 3
+    rng = np.random.default_rng(d)
+    q, _, _ = _inputs(B, H, N, d, seed=300 + d)
+    _, k, v = _inputs(B, H, S * N, d, seed=301 + d)
+    # Shards of keys scattered over the whole key range.
+    perm = rng.permutation(S * N)
+    shards = [np.sort(perm[i * N:(i + 1) * N]) for i in range(S)]
+    Op, Lp = _oracle_partials(q, k, v, shards, 1.0 / math.sqrt(d))
+    # Empty partials: shard 1 has no key for some rows (-inf, output NaN: it
+    # must not be read), and row 5 of every slice has no key at all.
+    Lp[1, :, :, 7::11] = -np.inf
+    Op[1, :, :, 7::11] = np.nan
+    Lp[:, :, :, 5] = -np.inf
+    Op[:, :, :, 5] = np.nan
+    dev = torch.device("cuda:0")
+    O, lse = osm.attention_combine(torch.from_numpy(Op).to(dev), torch.from_numpy(Lp).to(dev))
+    torch.cuda.synchronize()
+    O = O.to(torch.float64).cpu().numpy()
+    lse = lse.to(torch.float64).cpu().numpy()
+    Oref, lref = oracle.attn_merge(Op, Lp)
+    assert np.all(lse[:, :, 5] == -np.inf) and np.all(O[:, :, 5] == 0.0)
+    fin = np.isfinite(lref)
+    assert np.array_equal(fin, np.isfinite(lse))
+    eo, el = _maxabs(O, Oref), _maxabs(lse[fin], lref[fin])
+    tol_o = 2.0 ** -8 * float(np.max(np.abs(Oref))) + 1e-6
+    print(f"combine d={d}: max|dO|={eo:.3e} (tol {tol_o:.2e}) max|dlse|={el:.3e}", flush=True)
+    assert eo <= tol_o and el <= 1e-5

@@ -39,6 +39,14 @@ MUTANTS = [
      "if (causal && j >= i) { S[r * bc + c] = -INFINITY; continue; }"),
     ("online_denominator_not_rescaled", "l[r] = corr * l[r] + psum;",
      "l[r] = l[r] + psum;"),
+    ("merge_weight_sign", "double wb = exp(m_b - m_new);", "double wb = exp(m_new - m_b);"),
+    ("merge_denominator_unweighted", "l = wa * l + wb * 1.0;", "l = l + 1.0;"),
+    ("merge_accumulator_not_rescaled",
+     "for (long t = 0; t < d; ++t) a[t] = wa * a[t] + wb * a_b[t];",
+     "for (long t = 0; t < d; ++t) a[t] = a[t] + wb * a_b[t];"),
+    ("merge_lse_without_max", "lse[r] = m + log(l);", "lse[r] = log(l);"),
+    ("merge_keeps_first_partial_only", "if (m_b == -INFINITY) continue;",
+     "if (m_b == -INFINITY || s > 0) continue;"),
 ]
 
 

@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for exact attention forward and the stable row softmax.
+"""fp64 CPU oracle for exact attention forward and backward, the merge of
+partial attention results, and the stable row softmax.
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package; the product path never does.  It
@@ -67,8 +68,11 @@ class Oracle:
         lib.oracle_attn_online.argtypes = [_dp, _dp, _dp, _dp, _dp, _L, _L, _L, _L,
                                            ctypes.c_double, ctypes.c_int, _L, _L]
         lib.oracle_attn_merge.argtypes = [_dp, _dp, _dp, _dp, _L, _L, _L]
+        lib.oracle_attn_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _L, _L, _L, _L,
+                                        ctypes.c_double, ctypes.c_int]
         for name in ("oracle_row_softmax", "oracle_attn_fwd", "oracle_attn_rows",
-                     "oracle_online_row_trace", "oracle_attn_online", "oracle_attn_merge"):
+                     "oracle_online_row_trace", "oracle_attn_online", "oracle_attn_merge",
+                     "oracle_attn_bwd"):
             getattr(lib, name).restype = ctypes.c_int
         self._lib = lib
 
@@ -168,6 +172,22 @@ class Oracle:
                                            S, rows, d), "attn_merge")
         return O, lse
 
+    def attn_bwd(self, Q, K, V, dO, scale: float, causal: bool):
+        """Gradients of sum(dO * O) with respect to Q, K, V for the attention
+        forward, by the chain rule with the probabilities recomputed from Q
+        and K (Lesson 22, sections 30-31; four generations, 2.4).  Returns
+        (dQ, dK, dV), each [B, H, N, d]."""
+        Q, K, V = self._attn_shapes(Q, K, V)
+        dO = _f64(dO)
+        if dO.shape != Q.shape:
+            raise ValueError("dO must have the shape of Q")
+        B, H, N, d = Q.shape
+        dQ, dK, dV = np.empty_like(Q), np.empty_like(Q), np.empty_like(Q)
+        _check(self._lib.oracle_attn_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(dQ),
+                                         _ptr(dK), _ptr(dV), B, H, N, d, float(scale),
+                                         int(bool(causal))), "attn_bwd")
+        return dQ, dK, dV
+
 
 _default: Oracle | None = None
 
@@ -209,3 +229,7 @@ def attn_online(Q, K, V, scale, causal, br, bc):
 
 def attn_merge(O_part, lse_part):
     return default().attn_merge(O_part, lse_part)
+
+
+def attn_bwd(Q, K, V, dO, scale, causal):
+    return default().attn_bwd(Q, K, V, dO, scale, causal)

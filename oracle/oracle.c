@@ -387,3 +387,88 @@ int oracle_attn_merge(const double *Opart, const double *lpart, double *O,
     }
     return failed ? -2 : 0;
 }
+
+/* ------------------------------------------------------------------------ *
+ * Attention backward: the gradients of the scalar L = sum_{i,t} dO_it O_it
+ * with respect to Q, K and V, for the forward above ([L22] sections 30-31
+ * and [GEN] 2.4: the probabilities are recomputed from Q and K rather than
+ * stored, then dQ, dK, dV follow; the pages do not print the gradient
+ * formulas, so they are written out here from the chain rule through
+ * O = P V and the row softmax P = softmax(S), S = scale Q K^T with masked
+ * entries held at -inf):
+ *   dV = P^T dO
+ *   dP = dO V^T
+ *   D_i = sum_k P_ik dP_ik
+ *   dS_ij = P_ij (dP_ij - D_i)            (the softmax Jacobian)
+ *   dQ = scale dS K
+ *   dK = scale dS^T Q
+ * Per (b, h) slice the N x N matrices P and dS are materialised in full; P
+ * comes from the three-pass row definition of attn_row.  Rows and columns
+ * are distributed over threads; every output element is one serial sum.
+ * All tensors are [B][H][N][d].
+ * ------------------------------------------------------------------------ */
+int oracle_attn_bwd(const double *Q, const double *K, const double *V,
+                    const double *dO, double *dQ, double *dK, double *dV,
+                    long B, long H, long N, long d, double scale, int causal)
+{
+    if (!attn_args_ok(Q, K, V, dO, dQ, B, H, N, d) || (B * H * N != 0 && (!dK || !dV)))
+        return -1;
+    if (B * H * N == 0) return 0;
+    double *P = (double *)malloc(sizeof(double) * (size_t)(N * N));
+    double *dS = (double *)malloc(sizeof(double) * (size_t)(N * N));
+    int failed = (!P || !dS);
+    for (long sl = 0; sl < B * H && !failed; ++sl) {
+        const double *Qs = Q + sl * N * d, *Ks = K + sl * N * d, *Vs = V + sl * N * d;
+        const double *dOs = dO + sl * N * d;
+        double *dQs = dQ + sl * N * d, *dKs = dK + sl * N * d, *dVs = dV + sl * N * d;
+        int bad = 0;
+#pragma omp parallel reduction(|| : bad)
+        {
+            double *s = (double *)malloc(sizeof(double) * (size_t)N);
+            double *o = (double *)malloc(sizeof(double) * (size_t)d);
+            if (!s || !o) {
+                bad = 1;
+            } else {
+                long i;
+#pragma omp for schedule(dynamic, 8)
+                for (i = 0; i < N; ++i) {
+                    double lse_i;
+                    long visible = causal ? i + 1 : N;
+                    attn_row(Qs + i * d, Ks, Vs, N, d, scale, visible, s, P + i * N, o, &lse_i);
+                    for (long j = visible; j < N; ++j) P[i * N + j] = 0.0;
+                    /* dP_ij = dO_i . V_j, then D_i and dS_ij */
+                    double D = 0.0;
+                    for (long j = 0; j < N; ++j) {
+                        double dp = 0.0;
+                        for (long t = 0; t < d; ++t) dp += dOs[i * d + t] * Vs[j * d + t];
+                        dS[i * N + j] = dp;
+                        D += P[i * N + j] * dp;
+                    }
+                    for (long j = 0; j < N; ++j) dS[i * N + j] = P[i * N + j] * (dS[i * N + j] - D);
+                }
+            }
+            free(s);
+            free(o);
+        }
+        if (bad) { failed = 1; break; }
+        long r;
+#pragma omp parallel for schedule(static)
+        for (r = 0; r < N; ++r) {
+            /* row r of dQ: sum over keys j; row r of dK and dV: sum over queries i */
+            for (long t = 0; t < d; ++t) {
+                double aq = 0.0, ak = 0.0, av = 0.0;
+                for (long j = 0; j < N; ++j) aq += dS[r * N + j] * Ks[j * d + t];
+                for (long i = 0; i < N; ++i) {
+                    ak += dS[i * N + r] * Qs[i * d + t];
+                    av += P[i * N + r] * dOs[i * d + t];
+                }
+                dQs[r * d + t] = scale * aq;
+                dKs[r * d + t] = scale * ak;
+                dVs[r * d + t] = av;
+            }
+        }
+    }
+    free(P);
+    free(dS);
+    return failed ? -2 : 0;
+}

@@ -451,4 +451,69 @@ def pin_merge_special_cases(orc):
     _close(l3, l + math.log(2.0), 1e-14, 1e-14, what="equal partials lse")
 
 
+def pin_bwd_finite_differences(orc):
+    # The gradients of L = sum(dO * O) against central differences of L
+    # computed with the forward oracle alone: no gradient formula involved.
+    rng = _rng(41)
+    h = 1e-6
+    for N, d, causal in ((1, 2, False), (3, 2, True), (4, 3, False), (5, 2, True)):
+        Q, K, V = _rand_attn(rng, 1, 2, N, d, std=1.2)
+        dO = rng.standard_normal(Q.shape)
+        grads = orc.attn_bwd(Q, K, V, dO, 0.7, causal)
+
+        def loss(X, which):
+            args = [Q, K, V]
+            args[which] = X
+            O, _ = orc.attn_fwd(*args, 0.7, causal)
+            return float((O * dO).sum())
+
+        for which, (X, G) in enumerate(zip((Q, K, V), grads)):
+            fd = np.zeros_like(X)
+            for idx in np.ndindex(X.shape):
+                Xp, Xm = X.copy(), X.copy()
+                Xp[idx] += h
+                Xm[idx] -= h
+                fd[idx] = (loss(Xp, which) - loss(Xm, which)) / (2 * h)
+            _close(G, fd, 1e-7, 1e-7, what=f"grad {'QKV'[which]} N={N} d={d} causal={causal}")
+
+
+def pin_bwd_library(orc):
+    # torch autograd in float64 through a plain softmax attention.
+    import torch
+    rng = _rng(42)
+    for causal in (False, True):
+        Q, K, V = _rand_attn(rng, 2, 3, 17, 8)
+        dO = rng.standard_normal(Q.shape)
+        q, k, v = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (Q, K, V))
+        s = 0.35 * (q @ k.transpose(-1, -2))
+        if causal:
+            s = s.masked_fill(torch.triu(torch.ones(17, 17, dtype=torch.bool), 1), float("-inf"))
+        o = torch.softmax(s, dim=-1) @ v
+        o.backward(torch.tensor(dO))
+        got = orc.attn_bwd(Q, K, V, dO, 0.35, causal)
+        for name, g, t in zip("QKV", got, (q, k, v)):
+            _close(g, t.grad.numpy(), 1e-12, 1e-10, what=f"torch grad {name} causal={causal}")
+
+
+def pin_bwd_invariants(orc):
+    # Adding one vector to every key leaves each softmax row unchanged, so the
+    # key gradients sum to zero; the probabilities of a row sum to one, so the
+    # value gradients sum to the sum of dO.  One key: P = 1 whatever Q and K,
+    # so dQ = dK = 0 and dV = dO.  dO = 0 gives zero gradients.
+    rng = _rng(43)
+    for causal in (False, True):
+        Q, K, V = _rand_attn(rng, 1, 2, 9, 4, std=1.5)
+        dO = rng.standard_normal(Q.shape)
+        dQ, dK, dV = orc.attn_bwd(Q, K, V, dO, 0.6, causal)
+        _close(dK.sum(axis=2), np.zeros((1, 2, 4)), 1e-12, what=f"sum dK causal={causal}")
+        _close(dV.sum(axis=2), dO.sum(axis=2), 1e-12, 1e-12, what=f"sum dV causal={causal}")
+        z = orc.attn_bwd(Q, K, V, np.zeros_like(dO), 0.6, causal)
+        assert all(np.all(g == 0.0) for g in z), "dO = 0 must give zero gradients"
+    Q, K, V = _rand_attn(rng, 2, 1, 1, 5)
+    dO = rng.standard_normal(Q.shape)
+    dQ, dK, dV = orc.attn_bwd(Q, K, V, dO, 0.9, False)
+    assert np.all(dQ == 0.0) and np.all(dK == 0.0), "one key: dQ = dK = 0"
+    assert np.array_equal(dV, dO), "one key: dV = dO"
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

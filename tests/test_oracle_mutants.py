@@ -47,6 +47,17 @@ MUTANTS = [
     ("merge_lse_without_max", "lse[r] = m + log(l);", "lse[r] = log(l);"),
     ("merge_keeps_first_partial_only", "if (m_b == -INFINITY) continue;",
      "if (m_b == -INFINITY || s > 0) continue;"),
+    ("bwd_softmax_jacobian_sign",
+     "for (long j = 0; j < N; ++j) dS[i * N + j] = P[i * N + j] * (dS[i * N + j] - D);",
+     "for (long j = 0; j < N; ++j) dS[i * N + j] = P[i * N + j] * (D - dS[i * N + j]);"),
+    ("bwd_missing_row_term",
+     "for (long j = 0; j < N; ++j) dS[i * N + j] = P[i * N + j] * (dS[i * N + j] - D);",
+     "for (long j = 0; j < N; ++j) dS[i * N + j] = P[i * N + j] * dS[i * N + j];"),
+    ("bwd_dq_without_scale", "dQs[r * d + t] = scale * aq;", "dQs[r * d + t] = aq;"),
+    ("bwd_dk_from_keys", "ak += dS[i * N + r] * Qs[i * d + t];", "ak += dS[i * N + r] * Ks[i * d + t];"),
+    ("bwd_dv_transposed_p", "av += P[i * N + r] * dOs[i * d + t];", "av += P[r * N + i] * dOs[i * d + t];"),
+    ("bwd_dp_from_keys", "for (long t = 0; t < d; ++t) dp += dOs[i * d + t] * Vs[j * d + t];",
+     "for (long t = 0; t < d; ++t) dp += dOs[i * d + t] * Ks[j * d + t];"),
 ]
 
 

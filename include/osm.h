@@ -24,6 +24,13 @@
  *    lse and output partials, then a combine); the merge is the rule for
  *    joining two partial softmax states of Lesson 22, section 22.
  *
+ *  attn_bwd
+ *    The gradients dQ, dK, dV of the scalar sum(dO * O) for attn_fwd's
+ *    output O.  The probabilities are recomputed from Q, K and the forward's
+ *    lse instead of being stored (Lesson 22, sections 30-31; "Moving less",
+ *    section 2.4, P_ij = exp(S_ij - L_i)); the gradient formulas themselves
+ *    are the chain rule through O = P V and the row softmax.
+ *
  *  row_softmax
  *    Numerically stable softmax of each row of x [B][N]:
  *    y[b][j] = exp(x[b][j] - m_b) / sum_t exp(x[b][t] - m_b),
@@ -148,6 +155,36 @@ int attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float
  */
 int attn_combine(const float* O_part, const float* lse_part, void* O, float* lse, int S,
                  int B, int H, int N, int d, void* stream);
+
+/*
+ * attn_bwd_workspace_bytes -- device bytes attn_bwd needs as workspace:
+ *   2 * B * H * N * 4 (two fp32 values per query row), 0 for an empty problem.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int N);
+
+/*
+ * attn_bwd -- backward pass of attn_fwd (bf16 inputs, fp32 accumulation).
+ *   Q, K, V : const bf16 [B][H][N][d], the forward's inputs
+ *   O       : const bf16 [B][H][N][d], the forward's output
+ *   dO      : const bf16 [B][H][N][d], the gradient of the loss w.r.t. O
+ *   lse     : const fp32 [B][H][N], the forward's logsumexp
+ *   dQ, dK, dV : bf16 [B][H][N][d], written (round-to-nearest-even):
+ *             dV = P^T dO, dQ = scale dS K, dK = scale dS^T Q with
+ *             P_ij = exp(scale q_i.k_j - lse_i) over the visible keys and
+ *             dS_ij = P_ij (dO_i.v_j - sum_t dO_it O_it)
+ *   B, H, N, d, scale, causal : as for the forward call that produced O, lse
+ *   workspace : device memory of at least attn_bwd_workspace_bytes(B, H, N),
+ *             16-byte aligned, caller-owned, contents irrelevant on entry
+ *   stream  : hipStream_t or NULL
+ * The probabilities and dS are rounded to bf16 before they enter the dV, dK
+ * and dQ products.  Q, K, V, O, dO, dQ, dK, dV need 16-byte alignment, lse 4.
+ * dQ, dK, dV may overlap neither each other, nor any input, nor the
+ * workspace.  The result is deterministic (no atomic accumulation).  Returns
+ * an osm_status (OSM_ERR_WORKSPACE if workspace_bytes is too small).
+ */
+int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* lse, void* dQ, void* dK, void* dV, int B, int H, int N, int d,
+             float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * row_softmax -- stable softmax of each fp32 row.

@@ -40,11 +40,17 @@ _lib.attn_fwd_splitkv.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _
 _lib.attn_fwd_splitkv.restype = _i
 _lib.attn_combine.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
 _lib.attn_combine.restype = _i
+_lib.attn_bwd_workspace_bytes.argtypes = [_i, _i, _i]
+_lib.attn_bwd_workspace_bytes.restype = _sz
+_lib.attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i,
+                          _vp, _sz, _vp]
+_lib.attn_bwd.restype = _i
 _lib.osm_status_str.argtypes = [_i]
 _lib.osm_status_str.restype = ctypes.c_char_p
 
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_splitkv_plan", "attn_fwd_splitkv",
-           "attn_combine", "row_softmax", "osm_status_str")
+           "attn_combine", "attn_bwd_workspace_bytes", "attn_bwd", "row_softmax",
+           "osm_status_str")
 
 OSM_OK = 0
 OSM_ERR_NULL = 1
@@ -118,3 +124,16 @@ def attn_combine(O_part: int, lse_part: int, O: int, lse: int, S: int, B: int, H
                  d: int, stream: int = 0) -> None:
     """Merge of S partial attention results; see include/osm.h."""
     _call("attn_combine", O_part, lse_part, O, lse, S, B, H, N, d, stream)
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    """Device bytes attn_bwd needs as workspace; see include/osm.h."""
+    return int(_lib.attn_bwd_workspace_bytes(B, H, N))
+
+
+def attn_bwd(Q: int, K: int, V: int, O: int, dO: int, lse: int, dQ: int, dK: int, dV: int,
+             B: int, H: int, N: int, d: int, scale: float, causal: bool, workspace: int,
+             workspace_bytes: int, stream: int = 0) -> None:
+    """Backward pass of attn_fwd (dQ, dK, dV); see include/osm.h."""
+    _call("attn_bwd", Q, K, V, O, dO, lse, dQ, dK, dV, B, H, N, d, scale, int(bool(causal)),
+          workspace, workspace_bytes, stream)

@@ -42,20 +42,33 @@ int check_device()
 
 int finish(hipError_t e) { return e == hipSuccess ? OSM_OK : OSM_ERR_HIP; }
 
-// Shared validation of attn_fwd / attn_fwd_f32.  *work is set to false for an
-// empty problem (valid, nothing to launch).
-int validate_attn(const void* Q, const void* K, const void* V, const void* O, const float* lse,
-                  int B, int H, int N, int d, float scale, size_t elem, bool* work)
+// Shape and scale checks shared by the attention entry points.
+int check_attn_shape(int B, int H, int N, int d, float scale, size_t elem)
 {
-    *work = false;
     if (B < 0 || H < 0 || N < 0) return OSM_ERR_SIZE;
     if (d != 64 && d != 128) return OSM_ERR_HEAD_DIM;
     if (!(std::isfinite(scale) && scale > 0.f)) return OSM_ERR_SCALE;
     if (B == 0 || H == 0 || N == 0) return OSM_OK;
     const long long bh = (long long)B * H;
     // Work-group ids (bh * query blocks of at least 128 rows) and row indices
-    // must fit in 32 bits.
+    // must fit in 32 bits, a dispatch counts at most 2^32 - 1 work-items (every
+    // launch here has at most two per row, rounded up to 256-row blocks), and
+    // the bytes of one (b, h) slice are a 32-bit buffer offset.
     if (bh > INT_MAX || bh * ((N + 127) / 128) > INT_MAX) return OSM_ERR_SIZE;
+    if (bh * ((N + 255) / 256) * 512 > UINT32_MAX || (long long)N * d * (long long)elem > UINT32_MAX)
+        return OSM_ERR_SIZE;
+    return OSM_OK;
+}
+
+// Shared validation of attn_fwd / attn_fwd_f32.  *work is set to false for an
+// empty problem (valid, nothing to launch).
+int validate_attn(const void* Q, const void* K, const void* V, const void* O, const float* lse,
+                  int B, int H, int N, int d, float scale, size_t elem, bool* work)
+{
+    *work = false;
+    int st = check_attn_shape(B, H, N, d, scale, elem);
+    if (st != OSM_OK || B == 0 || H == 0 || N == 0) return st;
+    const long long bh = (long long)B * H;
     if (!Q || !K || !V || !O || !lse) return OSM_ERR_NULL;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(lse, 4))
         return OSM_ERR_ALIGN;
@@ -192,6 +205,47 @@ int attn_combine(const float* O_part, const float* lse_part, void* O, float* lse
                                            static_cast<hipStream_t>(stream)));
 }
 
+size_t attn_bwd_workspace_bytes(int B, int H, int N)
+{
+    if (B <= 0 || H <= 0 || N <= 0) return 0;
+    return (size_t)2 * B * H * N * sizeof(float);
+}
+
+int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* lse, void* dQ, void* dK, void* dV, int B, int H, int N, int d,
+             float scale, int causal, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int st = check_attn_shape(B, H, N, d, scale, 2);
+    if (st != OSM_OK || B == 0 || H == 0 || N == 0) return st;
+    if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || !workspace)
+        return OSM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+        !aligned(dO, 16) || !aligned(lse, 4) || !aligned(dQ, 16) || !aligned(dK, 16) ||
+        !aligned(dV, 16) || !aligned(workspace, 16))
+        return OSM_ERR_ALIGN;
+    const long long bh = (long long)B * H;
+    const size_t need = attn_bwd_workspace_bytes(B, H, N);
+    if (workspace_bytes < need) return OSM_ERR_WORKSPACE;
+    const size_t tb = (size_t)bh * N * d * 2, lb = (size_t)bh * N * sizeof(float);
+    const void* outs[3] = {dQ, dK, dV};
+    const void* ins[6] = {Q, K, V, O, dO, lse};
+    const size_t in_bytes[6] = {tb, tb, tb, tb, tb, lb};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = 0; b < 6; ++b)
+            if (overlaps(outs[a], tb, ins[b], in_bytes[b])) return OSM_ERR_ALIAS;
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a], tb, outs[b], tb)) return OSM_ERR_ALIAS;
+        if (overlaps(outs[a], tb, workspace, need)) return OSM_ERR_ALIAS;
+    }
+    for (int b = 0; b < 6; ++b)
+        if (overlaps(workspace, need, ins[b], in_bytes[b])) return OSM_ERR_ALIAS;
+    if ((st = check_device()) != OSM_OK) return st;
+    float* Dl = static_cast<float*>(workspace);
+    float* Lc = Dl + (size_t)bh * N;
+    return finish(osm::launch_attn_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, (int)bh, N, d, scale,
+                                            causal != 0, Dl, Lc, static_cast<hipStream_t>(stream)));
+}
+
 const char* osm_status_str(int status)
 {
     switch (status) {
@@ -205,7 +259,7 @@ const char* osm_status_str(int status)
     case OSM_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
     case OSM_ERR_HIP: return "the HIP runtime reported an error";
     case OSM_ERR_SPLITS: return "the number of key splits is out of range";
-    case OSM_ERR_WORKSPACE: return "the workspace is smaller than attn_fwd_splitkv_plan requires";
+    case OSM_ERR_WORKSPACE: return "the workspace is smaller than the call requires";
     default: return "unknown status";
     }
 }

@@ -1,0 +1,503 @@
+// attn_bwd_bf16.hip -- backward pass of the bf16 attention forward on the
+// gfx950 bf16 matrix cores: dQ, dK, dV of L = sum(dO * O), written as bf16.
+//
+// Method: recompute instead of store ("Lesson 22: why softmax is hard to make
+// efficient, and how FlashAttention reduces memory traffic", sections 30-31;
+// "Moving less: four generations of FlashAttention", 2.4): every probability
+// tile is rebuilt from Q, K and the forward's row statistic,
+// P_ij = exp(S_ij - L_i) with L = lse, so no N x N matrix is read or written.
+// The gradients are the chain rule through O = P V and the row softmax:
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  D_i = sum_t dO_it O_it,
+//   dQ = scale dS K,  dK = scale dS^T Q
+// (D_i equals sum_j P_ij dP_ij because O_i = sum_j P_ij V_j).
+//
+// gfx950 design -- three kernels, no atomics, bitwise deterministic:
+//  * attn_bwd_delta_kernel: D and L log2(e) per row (HBM bound, reads O, dO).
+//  * attn_bwd_dkdv_kernel: one workgroup per (batch*head, 128 keys), a wave
+//    per 32 keys, the keys' K and V rows held in VGPRs for the whole kernel
+//    as the B operands of S = Q K^T and dP = dO V^T (one key per lane, the
+//    queries of a 32-query step in the accumulator registers).  Query tiles
+//    of 64 rows of Q and dO stream through LDS, double-buffered.  P and dS,
+//    rounded to bf16, are register for register the B operands of
+//    dV^T += dO^T P and dK^T += Q^T dS, whose A operands come from the same
+//    tiles through the transposing LDS read.  The column-block split is the
+//    one of the four-generations page, 3.3; unlike there, dQ is not summed
+//    across these workgroups with atomic adds.
+//  * attn_bwd_dq_kernel: one workgroup per (batch*head, 256 queries), a wave
+//    per 32 queries with Q and dO in VGPRs, K and V tiles of 64 keys through
+//    LDS: S^T = K Q^T and dP^T = V dO^T (one query per lane, as in the
+//    forward), then dQ^T += K^T dS^T.  Recomputing S and dP here costs two
+//    more products than accumulating dQ with atomics, and keeps dQ exact to
+//    the summation order and reproducible.
+//  * Q/dO (dK/dV kernel) and K (dQ kernel) tiles are read both row-wise
+//    (ds_read_b128, rows permuted at read time so that each 8-register group
+//    of an accumulator holds 8 consecutive tile rows) and transposed
+//    (ds_read_b64_tr_b16), so they stay in natural row order in LDS.
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace osm {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+__device__ __forceinline__ int swap_bits23(int i)
+{
+    return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, lds_void_t* dst, uint32_t voff)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Tile of R rows x D bf16 in LDS with row pitch D + 8 elements, filled by
+// 1 KiB wave loads: load i writes chunk positions 64 i .. 64 i + 63; chunk
+// position p holds row p / (D/8 + 1), column chunk p % (D/8 + 1) (the last
+// chunk of a row is padding and re-fetches the row's last real chunk).
+template <int D, int R>
+struct Tile {
+    static constexpr int P = D + 8;          // row pitch (elements)
+    static constexpr int CPR = P / 8;        // 16-byte chunks per row
+    static constexpr int BYTES = R * P * 2;
+    static constexpr int INST = BYTES / 1024;
+    static_assert(BYTES % 1024 == 0, "tile is whole wave loads");
+    __device__ static uint32_t src_offset(int p)
+    {
+        const int row = p / CPR, ch = min(p % CPR, D / 8 - 1);
+        return (uint32_t)(row * D + ch * 8) * 2;
+    }
+};
+
+// A operand of a 32x32x16 product from a row-major LDS tile, row-wise: lane
+// (i, h) supplies tile row row0 + swap_bits23(i), columns col0 + 8 h .. + 7.
+template <int PITCH>
+__device__ __forceinline__ bf16x8 rows_a(const char* tile, int row0, int col0, int i, int h)
+{
+    return *reinterpret_cast<const bf16x8*>(tile + ((row0 + swap_bits23(i)) * PITCH + col0 + 8 * h) * 2);
+}
+
+// A operand from a row-major LDS tile, transposed: operand row i is tile
+// column col0 + i, operand column k (= 8 h + e) is tile row row0 + k, via
+// two ds_read_b64_tr_b16 (lane 16 g + 4 e + a reads 4 columns
+// 16 (g % 2) + 4 a of tile row 8 (g / 2) + e, and 4 rows further).
+template <int PITCH>
+__device__ __forceinline__ bf16x8 cols_a(const char* tile, int row0, int col0, int lane)
+{
+    const int g16 = lane >> 4, e4 = (lane >> 2) & 3, a4 = lane & 3;
+    const char* p = tile + ((row0 + 8 * (g16 >> 1) + e4) * PITCH + col0 + 16 * (g16 & 1) + 4 * a4) * 2;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * PITCH * 2));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// bf16 of registers 8 G .. 8 G + 7 of an accumulator.
+__device__ __forceinline__ bf16x8 half_bf16(const f32x16& v, int G)
+{
+    const f32x8 p8 = G ? __builtin_shufflevector(v, v, 8, 9, 10, 11, 12, 13, 14, 15)
+                       : __builtin_shufflevector(v, v, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_convertvector(p8, bf16x8);
+}
+
+// Store of a transposed accumulator set acc[D/32] (operand row = column t of
+// the output, operand column = output row) as bf16 rows of [N][D], times mul.
+template <int D>
+__device__ __forceinline__ void store_rows_t(__bf16* out, uint32_t slice_bytes, int row, int h,
+                                             const f32x16 (&acc)[D / 32], float mul)
+{
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(out, slice_bytes);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 o4 = {acc[dt][4 * g] * mul, acc[dt][4 * g + 1] * mul,
+                              acc[dt][4 * g + 2] * mul, acc[dt][4 * g + 3] * mul};
+            const bf16x4 ob = __builtin_convertvector(o4, bf16x4);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), rs,
+                                                  (uint32_t)(row * D + dt * 32 + 8 * g + 4 * h) * 2, 0, 0);
+        }
+}
+
+// ---------------------------------------------------------------- delta ----
+// D[r] = sum_t dO[r][t] O[r][t] (bf16 products, fp32 sums) and
+// Lc[r] = lse[r] log2(e), for rows r of [rows][D]; D / 8 lanes per row.
+template <int D>
+__global__ void __launch_bounds__(256)
+attn_bwd_delta_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO,
+                      const float* __restrict__ lse, float* __restrict__ Dl,
+                      float* __restrict__ Lc, long long rows)
+{
+    constexpr int LPR = D / 8, RPB = 256 / LPR;
+    const int c8 = threadIdx.x % LPR;
+    for (long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR; row < rows;
+         row += (long long)gridDim.x * RPB) {
+        const bf16x8 o = *reinterpret_cast<const bf16x8*>(O + row * D + 8 * c8);
+        const bf16x8 g = *reinterpret_cast<const bf16x8*>(dO + row * D + 8 * c8);
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fmaf((float)o[e], (float)g[e], s);
+#pragma unroll
+        for (int w = LPR / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, LPR);
+        if (c8 == 0) {
+            Dl[row] = s;
+            Lc[row] = lse[row] * kLog2e;
+        }
+    }
+}
+
+// ------------------------------------------------------------ dK and dV ----
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                     const float* __restrict__ Lc, const float* __restrict__ Dl,
+                     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int BH, float scale)
+{
+    constexpr int NW = 4, BK = NW * 32, BQ = 64;
+    using TQ = Tile<D, BQ>;
+    constexpr int LPW = (TQ::INST + NW - 1) / NW;  // loads per wave per tile
+    __shared__ __attribute__((aligned(1024))) char qb0[TQ::BYTES];
+    __shared__ __attribute__((aligned(1024))) char qb1[TQ::BYTES];
+    __shared__ __attribute__((aligned(1024))) char ob0[TQ::BYTES];
+    __shared__ __attribute__((aligned(1024))) char ob1[TQ::BYTES];
+    __shared__ __attribute__((aligned(16))) float lb[2][BQ];
+    __shared__ __attribute__((aligned(16))) float db[2][BQ];
+    auto qbuf = [&](auto bc) -> char* { if constexpr (decltype(bc)::value == 0) return qb0; else return qb1; };
+    auto obuf = [&](auto bc) -> char* { if constexpr (decltype(bc)::value == 0) return ob0; else return ob1; };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, h = lane >> 5;
+    // Key blocks in natural order: under the mask the first ones see the
+    // most queries, so the longest workgroups start first.
+    const int t = blockIdx.x / BH, bh = blockIdx.x - t * BH;
+    const int k0 = t * BK, kw0 = k0 + wave * 32;
+    const size_t base = (size_t)bh * N * D;
+    const uint32_t slice_b = (uint32_t)N * D * 2;
+    const float c = scale * kLog2e;
+
+    // K and V rows of this wave's keys as B operands: lane (j, h), step kk
+    // holds row kw0 + j, columns 16 kk + 8 h .. + 7 (zero past N).
+    bf16x8 kf[D / 16], vf[D / 16];
+    {
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, slice_b);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, slice_b);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const uint32_t off = (uint32_t)((kw0 + j) * D + kk * 16 + 8 * h) * 2;
+            kf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+            vf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+        }
+    }
+    f32x16 dvt[D / 32], dkt[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+        dvt[dt] = f32x16{};
+        dkt[dt] = f32x16{};
+    }
+
+    uint32_t src[LPW];
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) src[u] = TQ::src_offset((wave + u * NW) * 64 + lane);
+    auto issue = [&](auto bc, int qt) {
+        const int r0 = qt * BQ;
+        const uint32_t left = (uint32_t)(N - r0) * D * 2;
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base + (size_t)r0 * D, left);
+        const __amdgpu_buffer_rsrc_t ors = make_rsrc(dO + base + (size_t)r0 * D, left);
+#pragma unroll
+        for (int u = 0; u < LPW; ++u) {
+            const int i = wave + u * NW;
+            if (TQ::INST % NW == 0 || i < TQ::INST) {
+                lds_dma16(qrs, (lds_void_t*)(qbuf(bc) + i * 1024), src[u]);
+                lds_dma16(ors, (lds_void_t*)(obuf(bc) + i * 1024), src[u]);
+            }
+        }
+    };
+    // Row statistics of a query tile: threads 0-63 fetch L log2(e), 64-127
+    // fetch D (zero past N); written to LDS before the tile's barrier.
+    auto stat_load = [&](int qt) -> float {
+        const int q = qt * BQ + (tid & 63);
+        if (tid < 2 * BQ && q < N) return (tid < BQ ? Lc : Dl)[(size_t)bh * N + q];
+        return 0.f;
+    };
+    auto stat_store = [&](auto bc, float v) {
+        if (tid < BQ) lb[decltype(bc)::value][tid] = v;
+        else if (tid < 2 * BQ) db[decltype(bc)::value][tid - BQ] = v;
+    };
+
+    const int nqt = (N + BQ - 1) / BQ;
+    const int qt0 = CAUSAL ? k0 / BQ : 0;     // first query tile with a visible pair
+    const int key = kw0 + j;                  // this lane's key
+
+    auto compute = [&](auto bc, int qt) {
+        const char* qt_l = qbuf(bc);
+        const char* ot_l = obuf(bc);
+        const float* lbv = lb[decltype(bc)::value];
+        const float* dbv = db[decltype(bc)::value];
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+            const int qr0 = qt * BQ + 32 * qs;       // first query of the step
+            if (CAUSAL && qr0 + 31 < kw0) continue;  // every query precedes every key
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                s = mfma(rows_a<TQ::P>(qt_l, 32 * qs, 16 * kk, j, h), kf[kk], s);
+                dp = mfma(rows_a<TQ::P>(ot_l, 32 * qs, 16 * kk, j, h), vf[kk], dp);
+            }
+            // Register r of half h holds query qr0 + 16 (r / 8) + 8 h + r % 8.
+            const bool need_mask = (qr0 + 32 > N) || (CAUSAL && qr0 < kw0 + 31);
+            f32x16 p, ds;
+#pragma unroll
+            for (int G = 0; G < 2; ++G) {
+                const int qi0 = 32 * qs + 16 * G + 8 * h;  // tile row of register 8 G
+                const f32x4 l0 = *reinterpret_cast<const f32x4*>(lbv + qi0);
+                const f32x4 l1 = *reinterpret_cast<const f32x4*>(lbv + qi0 + 4);
+                const f32x4 d0 = *reinterpret_cast<const f32x4*>(dbv + qi0);
+                const f32x4 d1 = *reinterpret_cast<const f32x4*>(dbv + qi0 + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int r = 8 * G + e;
+                    const float lq = e < 4 ? l0[e] : l1[e - 4];
+                    const float dq = e < 4 ? d0[e] : d1[e - 4];
+                    float pv = exp2_hw(fmaf(s[r], c, -lq));
+                    if (need_mask) {
+                        const int q = qt * BQ + qi0 + e;
+                        if (q >= N || (CAUSAL && key > q)) pv = 0.f;
+                    }
+                    p[r] = pv;
+                    ds[r] = pv * (dp[r] - dq);
+                }
+            }
+#pragma unroll
+            for (int G = 0; G < 2; ++G) {
+                const bf16x8 pb = half_bf16(p, G), sb = half_bf16(ds, G);
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    dvt[dt] = mfma(cols_a<TQ::P>(ot_l, 32 * qs + 16 * G, 32 * dt, lane), pb, dvt[dt]);
+                    dkt[dt] = mfma(cols_a<TQ::P>(qt_l, 32 * qs + 16 * G, 32 * dt, lane), sb, dkt[dt]);
+                }
+            }
+        }
+    };
+
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    if (qt0 < nqt) {
+        issue(B0{}, qt0);
+        stat_store(B0{}, stat_load(qt0));
+        __syncthreads();
+        for (int qt = qt0; qt < nqt; qt += 2) {
+            float st = 0.f;
+            if (qt + 1 < nqt) {
+                issue(B1{}, qt + 1);
+                st = stat_load(qt + 1);
+            }
+            compute(B0{}, qt);
+            stat_store(B1{}, st);
+            __syncthreads();
+            if (qt + 1 >= nqt) break;
+            if (qt + 2 < nqt) {
+                issue(B0{}, qt + 2);
+                st = stat_load(qt + 2);
+            }
+            compute(B1{}, qt + 1);
+            stat_store(B0{}, st);
+            __syncthreads();
+        }
+    }
+    store_rows_t<D>(dK + base, slice_b, key, h, dkt, scale);
+    store_rows_t<D>(dV + base, slice_b, key, h, dvt, 1.0f);
+}
+
+// ------------------------------------------------------------------- dQ ----
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                   const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                   const float* __restrict__ Lc, const float* __restrict__ Dl,
+                   __bf16* __restrict__ dQ, int N, int BH, int nqb, float scale)
+{
+    constexpr int NW = 8, BR = NW * 32, BC = 64;
+    using TK = Tile<D, BC>;
+    constexpr int LPW = (TK::INST + NW - 1) / NW;
+    __shared__ __attribute__((aligned(1024))) char kb0[TK::BYTES];
+    __shared__ __attribute__((aligned(1024))) char kb1[TK::BYTES];
+    __shared__ __attribute__((aligned(1024))) char vb0[TK::BYTES];
+    __shared__ __attribute__((aligned(1024))) char vb1[TK::BYTES];
+    auto kbuf = [&](auto bc) -> char* { if constexpr (decltype(bc)::value == 0) return kb0; else return kb1; };
+    auto vbuf = [&](auto bc) -> char* { if constexpr (decltype(bc)::value == 0) return vb0; else return vb1; };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, h = lane >> 5;
+    const int t = blockIdx.x / BH, bh = blockIdx.x - t * BH;
+    const int qb = CAUSAL ? nqb - 1 - t : t;  // longest first under the mask
+    const int q0 = qb * BR, qw0 = q0 + wave * 32, q = qw0 + j;
+    const size_t base = (size_t)bh * N * D;
+    const uint32_t slice_b = (uint32_t)N * D * 2;
+    const float c = scale * kLog2e;
+
+    // Q and dO rows of this lane's query as B operands (zero past N).
+    bf16x8 qf[D / 16], gf[D / 16];
+    {
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, slice_b);
+        const __amdgpu_buffer_rsrc_t grs = make_rsrc(dO + base, slice_b);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const uint32_t off = (uint32_t)(q * D + kk * 16 + 8 * h) * 2;
+            qf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
+            gf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0));
+        }
+    }
+    const float lq = q < N ? Lc[(size_t)bh * N + q] : 0.f;
+    const float dq = q < N ? Dl[(size_t)bh * N + q] : 0.f;
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+
+    uint32_t src[LPW];
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) src[u] = TK::src_offset((wave + u * NW) * 64 + lane);
+    auto issue = [&](auto bc, int kt) {
+        const int kv0 = kt * BC;
+        const uint32_t left = (uint32_t)(N - kv0) * D * 2;
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base + (size_t)kv0 * D, left);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base + (size_t)kv0 * D, left);
+#pragma unroll
+        for (int u = 0; u < LPW; ++u) {
+            const int i = wave + u * NW;
+            if (TK::INST % NW == 0 || i < TK::INST) {
+                lds_dma16(krs, (lds_void_t*)(kbuf(bc) + i * 1024), src[u]);
+                lds_dma16(vrs, (lds_void_t*)(vbuf(bc) + i * 1024), src[u]);
+            }
+        }
+    };
+
+    const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+    const int ntiles = (kv_end + BC - 1) / BC;
+    const int wt = CAUSAL ? min(ntiles, (qw0 + 31) / BC + 1) : ntiles;
+
+    auto compute = [&](auto bc, int kt) {
+        if (kt >= wt) return;
+        const char* kt_l = kbuf(bc);
+        const char* vt_l = vbuf(bc);
+        const int kv0 = kt * BC;
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            s[mt] = f32x16{};
+            dp[mt] = f32x16{};
+        }
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                s[mt] = mfma(rows_a<TK::P>(kt_l, 32 * mt, 16 * kk, j, h), qf[kk], s[mt]);
+                dp[mt] = mfma(rows_a<TK::P>(vt_l, 32 * mt, 16 * kk, j, h), gf[kk], dp[mt]);
+            }
+        // Register r of half h of tile mt holds key kv0 + 32 mt + 16 (r / 8) + 8 h + r % 8.
+        const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
+        bf16x8 sb[BC / 16];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            f32x16 ds;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float pv = exp2_hw(fmaf(s[mt][r], c, -lq));
+                if (need_mask) {
+                    const int kidx = kv0 + 32 * mt + 16 * (r >> 3) + 8 * h + (r & 7);
+                    if (kidx >= N || (CAUSAL && kidx > q)) pv = 0.f;
+                }
+                ds[r] = pv * (dp[mt][r] - dq);
+            }
+            sb[2 * mt] = half_bf16(ds, 0);
+            sb[2 * mt + 1] = half_bf16(ds, 1);
+        }
+#pragma unroll
+        for (int ks = 0; ks < BC / 16; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+                acc[dt] = mfma(cols_a<TK::P>(kt_l, 16 * ks, 32 * dt, lane), sb[ks], acc[dt]);
+    };
+
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    issue(B0{}, 0);
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; kt += 2) {
+        if (kt + 1 < ntiles) issue(B1{}, kt + 1);
+        compute(B0{}, kt);
+        __syncthreads();
+        if (kt + 1 >= ntiles) break;
+        if (kt + 2 < ntiles) issue(B0{}, kt + 2);
+        compute(B1{}, kt + 1);
+        __syncthreads();
+    }
+    store_rows_t<D>(dQ + base, slice_b, q, h, acc, scale);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                      const float* lse, void* dQ, void* dK, void* dV, int BH, int N, float scale,
+                      float* Dl, float* Lc, hipStream_t stream)
+{
+    const __bf16* q = static_cast<const __bf16*>(Q);
+    const __bf16* k = static_cast<const __bf16*>(K);
+    const __bf16* v = static_cast<const __bf16*>(V);
+    const __bf16* g = static_cast<const __bf16*>(dO);
+    const long long rows = (long long)BH * N;
+    {
+        constexpr int RPB = 256 / (D / 8);
+        const long long need = (rows + RPB - 1) / RPB;
+        attn_bwd_delta_kernel<D><<<dim3((unsigned)(need < 65536 ? need : 65536)), dim3(256), 0, stream>>>(
+            static_cast<const __bf16*>(O), g, lse, Dl, Lc, rows);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        const int nkb = (N + 127) / 128;
+        attn_bwd_dkdv_kernel<D, CAUSAL><<<dim3((unsigned)(nkb * BH)), dim3(256), 0, stream>>>(
+            q, k, v, g, Lc, Dl, static_cast<__bf16*>(dK), static_cast<__bf16*>(dV), N, BH, scale);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int nqb = (N + 255) / 256;
+    attn_bwd_dq_kernel<D, CAUSAL><<<dim3((unsigned)(nqb * BH)), dim3(512), 0, stream>>>(
+        q, k, v, g, Lc, Dl, static_cast<__bf16*>(dQ), N, BH, nqb, scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, const void* O,
+                                const void* dO, const float* lse, void* dQ, void* dK, void* dV,
+                                int BH, int N, int d, float scale, bool causal, float* Dl,
+                                float* Lc, hipStream_t stream)
+{
+    if (d == 64)
+        return causal ? launch_bwd<64, true>(Q, K, V, O, dO, lse, dQ, dK, dV, BH, N, scale, Dl, Lc, stream)
+                      : launch_bwd<64, false>(Q, K, V, O, dO, lse, dQ, dK, dV, BH, N, scale, Dl, Lc, stream);
+    return causal ? launch_bwd<128, true>(Q, K, V, O, dO, lse, dQ, dK, dV, BH, N, scale, Dl, Lc, stream)
+                  : launch_bwd<128, false>(Q, K, V, O, dO, lse, dQ, dK, dV, BH, N, scale, Dl, Lc, stream);
+}
+
+}  // namespace osm

@@ -29,6 +29,12 @@ int attn_splitkv_auto(int BH, int N, int d, bool causal);
 // [rows][d]) and lse ([rows]).
 hipError_t launch_attn_combine(const float* opart, const float* lpart, void* O, float* lse, int S,
                                long long rows, int d, hipStream_t stream);
+// Backward: dQ, dK, dV (bf16 [B*H][N][d]) from Q, K, V, O, dO (bf16) and the
+// forward's lse; Dl and Lc are fp32 [B*H][N] workspace rows.
+hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, const void* O,
+                                const void* dO, const float* lse, void* dQ, void* dK, void* dV,
+                                int BH, int N, int d, float scale, bool causal, float* Dl,
+                                float* Lc, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const float* Q, const float* K, const float* V, float* O,
                                float* lse, int BH, int N, int d, float scale, bool causal,
                                hipStream_t stream);

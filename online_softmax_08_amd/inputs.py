@@ -12,6 +12,8 @@ reach the GPU and the oracle on any machine:
   workloads; the causal N=4096 workload multiplies every 64th query row
   (i % 64 == 0, every batch and head) by 8 after the cast, which is exact
   in bf16, to force large jumps of the running row maximum;
+* backward: the upstream gradient dO is N(0, 1) of Q's shape, drawn from a
+  generator of its own, then cast to bf16;
 * row softmax: fp32 ``randn`` of shape [B, N] times ``std``; the small
   workload overwrites row 0 with 1000 - j (a strictly falling row of huge
   values that overflows a softmax without the max subtraction).
@@ -120,6 +122,15 @@ def attn_inputs(w: AttnWorkload, *, B: int | None = None, H: int | None = None,
     if w.boost_every > 0 and N > 0:
         q[:, :, ::w.boost_every, :] *= w.boost
     return q, k, v
+
+
+def grad_output(shape, seed: int, dtype: str = "bf16") -> torch.Tensor:
+    """The upstream gradient dO for a backward test: N(0, 1) of ``shape`` from
+    its own generator (seed), so Q, K, V stay those of the forward recipe."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    t = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
 
 
 def softmax_inputs(w: SoftmaxWorkload, *, B: int | None = None, N: int | None = None,

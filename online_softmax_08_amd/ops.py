@@ -102,6 +102,37 @@ def attention_combine(o_part: torch.Tensor, lse_part: torch.Tensor):
     return out, lse
 
 
+def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                       lse: torch.Tensor, grad_out: torch.Tensor, causal: bool = False,
+                       scale: float | None = None, workspace: torch.Tensor | None = None):
+    """Gradients (dq, dk, dv) of sum(grad_out * out) for out, lse = attention(q, k, v).
+
+    All of q, k, v, out, grad_out: contiguous bf16 [B, H, N, d]; lse: fp32
+    [B, H, N] from the same forward call.  ``workspace`` (optional) is a device
+    uint8 tensor of at least attn_bwd_workspace_bytes(B, H, N) bytes.
+    """
+    _check_attn(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("the backward pass takes bfloat16 q, k, v")
+    for name, tsr in (("out", out), ("grad_out", grad_out)):
+        if tsr.shape != q.shape or tsr.dtype != q.dtype or not tsr.is_contiguous() or tsr.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    ws_bytes = _abi.attn_bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    with torch.cuda.device(q.device):
+        _abi.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                      grad_out.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                      dv.data_ptr(), B, H, N, d, scale, causal, workspace.data_ptr(),
+                      workspace.numel() * workspace.element_size(), _stream_handle(q.device))
+    return dq, dk, dv
+
+
 def softmax(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Stable softmax over the last dimension of a contiguous fp32 [B, N] GPU tensor.
     ``out`` may be ``x`` itself (in place)."""

@@ -24,7 +24,8 @@ def abi():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_splitkv_plan",
-                                            "attn_fwd_splitkv", "attn_combine", "row_softmax",
+                                            "attn_fwd_splitkv", "attn_combine",
+                                            "attn_bwd_workspace_bytes", "attn_bwd", "row_softmax",
                                             "osm_status_str"])
 
 
@@ -181,3 +182,33 @@ def test_combine_validation(abi):
     assert status(O=FAKE + 1024) == abi.OSM_ERR_ALIAS      # O inside the partial outputs
     assert status(lse=3 * FAKE + 64) == abi.OSM_ERR_ALIAS  # lse inside O
     abi.attn_combine(0, 0, 0, 0, 3, 1, 0, 16, 64)          # empty: a valid no-op
+
+
+def test_bwd_workspace_and_validation(abi):
+    assert abi.attn_bwd_workspace_bytes(2, 3, 100) == 2 * 2 * 3 * 100 * 4
+    assert abi.attn_bwd_workspace_bytes(0, 3, 100) == 0
+    ws_need = abi.attn_bwd_workspace_bytes(1, 1, 16)
+    ptr = {n: (i + 1) * FAKE for i, n in enumerate(("Q", "K", "V", "O", "dO", "lse", "dQ", "dK",
+                                                      "dV", "ws"))}
+
+    def status(ws_bytes=ws_need, **kw):
+        a = dict(ptr, B=1, H=1, N=16, d=64, scale=0.125, causal=0)
+        a.update(kw)
+        with pytest.raises(abi.OsmError) as e:
+            abi.attn_bwd(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["lse"], a["dQ"], a["dK"],
+                         a["dV"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                         a["ws"], ws_bytes)
+        return e.value.status
+    assert status(d=96) == abi.OSM_ERR_HEAD_DIM
+    assert status(scale=0.0) == abi.OSM_ERR_SCALE
+    assert status(N=-3) == abi.OSM_ERR_SIZE
+    assert status(dO=0) == abi.OSM_ERR_NULL
+    assert status(ws=0) == abi.OSM_ERR_NULL
+    assert status(dK=ptr["dK"] + 8) == abi.OSM_ERR_ALIGN
+    assert status(lse=ptr["lse"] + 2) == abi.OSM_ERR_ALIGN
+    assert status(ws_bytes=ws_need - 4) == abi.OSM_ERR_WORKSPACE
+    assert status(dQ=ptr["Q"]) == abi.OSM_ERR_ALIAS          # dQ is Q
+    assert status(dV=ptr["dK"] + 64) == abi.OSM_ERR_ALIAS    # dV runs into dK
+    assert status(dK=ptr["lse"]) == abi.OSM_ERR_ALIAS        # dK is lse
+    assert status(ws=ptr["dO"] + 32) == abi.OSM_ERR_ALIAS    # workspace inside dO
+    abi.attn_bwd(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 2, 16, 64, 0.125, 1, 0, 0)  # empty: no-op

@@ -13,10 +13,11 @@
 //
 // gfx950 design -- three kernels, no atomics, bitwise deterministic:
 //  * attn_bwd_delta_kernel: D and L log2(e) per row (HBM bound, reads O, dO).
-//  * attn_bwd_dkdv_kernel: one workgroup per (batch*head, 128 keys), a wave
-//    per 32 keys, the keys' K and V rows held in VGPRs for the whole kernel
-//    as the B operands of S = Q K^T and dP = dO V^T (one key per lane, the
-//    queries of a 32-query step in the accumulator registers).  Query tiles
+//  * attn_bwd_dkdv_kernel: one workgroup per (batch*head, 256 keys), a wave
+//    per 32 keys (two per SIMD), the keys' K rows held in VGPRs and their V
+//    rows in LDS for the whole kernel as the B operands of S = Q K^T and
+//    dP = dO V^T (one key per lane, the queries of a 32-query step in the
+//    accumulator registers).  Query tiles
 //    of 64 rows of Q and dO stream through LDS, double-buffered.  P and dS,
 //    rounded to bf16, are register for register the B operands of
 //    dV^T += dO^T P and dK^T += Q^T dS, whose A operands come from the same
@@ -165,16 +166,19 @@ attn_bwd_delta_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ d
 }
 
 // ------------------------------------------------------------ dK and dV ----
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, int NW, bool CAUSAL>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                      const float* __restrict__ Lc, const float* __restrict__ Dl,
                      __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int BH, float scale)
 {
-    constexpr int NW = 4, BK = NW * 32, BQ = 64;
+    constexpr int BK = NW * 32, BQ = 64;
     using TQ = Tile<D, BQ>;
+    using TV = Tile<D, BK>;
     constexpr int LPW = (TQ::INST + NW - 1) / NW;  // loads per wave per tile
+    constexpr int VPW = (TV::INST + NW - 1) / NW;  // loads per wave of the V block
+    __shared__ __attribute__((aligned(1024))) char vblk[TV::BYTES];
     __shared__ __attribute__((aligned(1024))) char qb0[TQ::BYTES];
     __shared__ __attribute__((aligned(1024))) char qb1[TQ::BYTES];
     __shared__ __attribute__((aligned(1024))) char ob0[TQ::BYTES];
@@ -195,19 +199,28 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const uint32_t slice_b = (uint32_t)N * D * 2;
     const float c = scale * kLog2e;
 
-    // K and V rows of this wave's keys as B operands: lane (j, h), step kk
-    // holds row kw0 + j, columns 16 kk + 8 h .. + 7 (zero past N).
-    bf16x8 kf[D / 16], vf[D / 16];
+    // K rows of this wave's keys as B operands in VGPRs: lane (j, h), step
+    // kk holds row kw0 + j, columns 16 kk + 8 h .. + 7 (zero past N).  The
+    // workgroup's V rows wait in LDS (registers would not leave room for two
+    // waves per SIMD); lane (j, h) reads the same part of V row kw0 + j.
+    bf16x8 kf[D / 16];
     {
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, slice_b);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, slice_b);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
             const uint32_t off = (uint32_t)((kw0 + j) * D + kk * 16 + 8 * h) * 2;
             kf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
-            vf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+        }
+        const uint32_t vleft = (uint32_t)(N - k0) * D * 2;
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base + (size_t)k0 * D, vleft);
+#pragma unroll
+        for (int u = 0; u < VPW; ++u) {
+            const int i = wave + u * NW;
+            if (TV::INST % NW == 0 || i < TV::INST)
+                lds_dma16(vrs, (lds_void_t*)(vblk + i * 1024), TV::src_offset(i * 64 + lane));
         }
     }
+    const char* vrow = vblk + ((wave * 32 + j) * TV::P + 8 * h) * 2;
     f32x16 dvt[D / 32], dkt[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
@@ -249,6 +262,7 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int key = kw0 + j;                  // this lane's key
 
     auto compute = [&](auto bc, int qt) {
+        if (CAUSAL && qt * BQ + BQ - 1 < kw0) return;  // every query precedes every key
         const char* qt_l = qbuf(bc);
         const char* ot_l = obuf(bc);
         const float* lbv = lb[decltype(bc)::value];
@@ -256,45 +270,65 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs) {
             const int qr0 = qt * BQ + 32 * qs;       // first query of the step
-            if (CAUSAL && qr0 + 31 < kw0) continue;  // every query precedes every key
-            f32x16 s = f32x16{}, dp = f32x16{};
+            if (qr0 >= N) continue;                  // past the last query
+            // S = Q K^T for the 32 queries and this wave's 32 keys; register
+            // r of half h holds query qr0 + 16 (r / 8) + 8 h + r % 8.
+            f32x16 s = f32x16{};
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
+            for (int kk = 0; kk < D / 16; ++kk)
                 s = mfma(rows_a<TQ::P>(qt_l, 32 * qs, 16 * kk, j, h), kf[kk], s);
-                dp = mfma(rows_a<TQ::P>(ot_l, 32 * qs, 16 * kk, j, h), vf[kk], dp);
-            }
-            // Register r of half h holds query qr0 + 16 (r / 8) + 8 h + r % 8.
-            const bool need_mask = (qr0 + 32 > N) || (CAUSAL && qr0 < kw0 + 31);
-            f32x16 p, ds;
+            // P = exp(S scale - L), in place; masked pairs (query past N, or
+            // key after query) are exactly 0.
 #pragma unroll
             for (int G = 0; G < 2; ++G) {
                 const int qi0 = 32 * qs + 16 * G + 8 * h;  // tile row of register 8 G
                 const f32x4 l0 = *reinterpret_cast<const f32x4*>(lbv + qi0);
                 const f32x4 l1 = *reinterpret_cast<const f32x4*>(lbv + qi0 + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    s[8 * G + e] = exp2_hw(fmaf(s[8 * G + e], c, -(e < 4 ? l0[e] : l1[e - 4])));
+            }
+            if ((qr0 + 32 > N) || (CAUSAL && qr0 < kw0 + 31)) {
+                // Offsets of N and of this lane's key from the first query of
+                // the lane's registers; kept opaque so that the compares
+                // below are not hoisted out of the query loop as 16
+                // loop-invariant thresholds.
+                int nq = N - qr0 - 8 * h, kq = key - qr0 - 8 * h;
+                asm volatile("" : "+v"(nq), "+v"(kq));
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int o = 16 * (r >> 3) + (r & 7);
+                    if (o >= nq || (CAUSAL && kq > o)) s[r] = 0.f;
+                }
+            }
+            // dV^T += dO^T P
+            const bf16x8 pb0 = half_bf16(s, 0), pb1 = half_bf16(s, 1);
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                dvt[dt] = mfma(cols_a<TQ::P>(ot_l, 32 * qs, 32 * dt, lane), pb0, dvt[dt]);
+                dvt[dt] = mfma(cols_a<TQ::P>(ot_l, 32 * qs + 16, 32 * dt, lane), pb1, dvt[dt]);
+            }
+            // dP = dO V^T, then dS = P (dP - D) in place
+            f32x16 dp = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+                dp = mfma(rows_a<TQ::P>(ot_l, 32 * qs, 16 * kk, j, h),
+                          *reinterpret_cast<const bf16x8*>(vrow + kk * 32), dp);
+#pragma unroll
+            for (int G = 0; G < 2; ++G) {
+                const int qi0 = 32 * qs + 16 * G + 8 * h;
                 const f32x4 d0 = *reinterpret_cast<const f32x4*>(dbv + qi0);
                 const f32x4 d1 = *reinterpret_cast<const f32x4*>(dbv + qi0 + 4);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int r = 8 * G + e;
-                    const float lq = e < 4 ? l0[e] : l1[e - 4];
-                    const float dq = e < 4 ? d0[e] : d1[e - 4];
-                    float pv = exp2_hw(fmaf(s[r], c, -lq));
-                    if (need_mask) {
-                        const int q = qt * BQ + qi0 + e;
-                        if (q >= N || (CAUSAL && key > q)) pv = 0.f;
-                    }
-                    p[r] = pv;
-                    ds[r] = pv * (dp[r] - dq);
-                }
+                for (int e = 0; e < 8; ++e)
+                    dp[8 * G + e] = s[8 * G + e] * (dp[8 * G + e] - (e < 4 ? d0[e] : d1[e - 4]));
             }
+            // dK^T += Q^T dS
+            const bf16x8 sb0 = half_bf16(dp, 0), sb1 = half_bf16(dp, 1);
 #pragma unroll
-            for (int G = 0; G < 2; ++G) {
-                const bf16x8 pb = half_bf16(p, G), sb = half_bf16(ds, G);
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    dvt[dt] = mfma(cols_a<TQ::P>(ot_l, 32 * qs + 16 * G, 32 * dt, lane), pb, dvt[dt]);
-                    dkt[dt] = mfma(cols_a<TQ::P>(qt_l, 32 * qs + 16 * G, 32 * dt, lane), sb, dkt[dt]);
-                }
+            for (int dt = 0; dt < D / 32; ++dt) {
+                dkt[dt] = mfma(cols_a<TQ::P>(qt_l, 32 * qs, 32 * dt, lane), sb0, dkt[dt]);
+                dkt[dt] = mfma(cols_a<TQ::P>(qt_l, 32 * qs + 16, 32 * dt, lane), sb1, dkt[dt]);
             }
         }
     };
@@ -329,14 +363,14 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 }
 
 // ------------------------------------------------------------------- dQ ----
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, int NW, bool CAUSAL>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                    const float* __restrict__ Lc, const float* __restrict__ Dl,
                    __bf16* __restrict__ dQ, int N, int BH, int nqb, float scale)
 {
-    constexpr int NW = 8, BR = NW * 32, BC = 64;
+    constexpr int BR = NW * 32, BC = 64;
     using TK = Tile<D, BC>;
     constexpr int LPW = (TK::INST + NW - 1) / NW;
     __shared__ __attribute__((aligned(1024))) char kb0[TK::BYTES];
@@ -455,6 +489,45 @@ attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     store_rows_t<D>(dQ + base, slice_b, q, h, acc, scale);
 }
 
+// Workgroups of 8 waves (256 keys or queries) while that still gives one per
+// CU (256) or more; smaller problems take workgroups of 4 or 2 waves so that
+// the grid covers more of the chip.
+constexpr long long kCUs = 256;
+
+template <int D, bool CAUSAL>
+hipError_t launch_dkdv(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* g,
+                       const float* Lc, const float* Dl, void* dK, void* dV, int BH, int N,
+                       float scale, hipStream_t stream)
+{
+    auto go = [&](auto nwc) {
+        constexpr int NW = decltype(nwc)::value;
+        const int nkb = (N + NW * 32 - 1) / (NW * 32);
+        attn_bwd_dkdv_kernel<D, NW, CAUSAL><<<dim3((unsigned)(nkb * BH)), dim3(NW * 64), 0, stream>>>(
+            q, k, v, g, Lc, Dl, static_cast<__bf16*>(dK), static_cast<__bf16*>(dV), N, BH, scale);
+        return hipGetLastError();
+    };
+    if ((long long)((N + 255) / 256) * BH >= kCUs) return go(std::integral_constant<int, 8>{});
+    if ((long long)((N + 127) / 128) * BH >= kCUs) return go(std::integral_constant<int, 4>{});
+    return go(std::integral_constant<int, 2>{});
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dq(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* g,
+                     const float* Lc, const float* Dl, void* dQ, int BH, int N, float scale,
+                     hipStream_t stream)
+{
+    auto go = [&](auto nwc) {
+        constexpr int NW = decltype(nwc)::value;
+        const int nqb = (N + NW * 32 - 1) / (NW * 32);
+        attn_bwd_dq_kernel<D, NW, CAUSAL><<<dim3((unsigned)(nqb * BH)), dim3(NW * 64), 0, stream>>>(
+            q, k, v, g, Lc, Dl, static_cast<__bf16*>(dQ), N, BH, nqb, scale);
+        return hipGetLastError();
+    };
+    if ((long long)((N + 255) / 256) * BH >= kCUs) return go(std::integral_constant<int, 8>{});
+    if ((long long)((N + 127) / 128) * BH >= kCUs) return go(std::integral_constant<int, 4>{});
+    return go(std::integral_constant<int, 2>{});
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                       const float* lse, void* dQ, void* dK, void* dV, int BH, int N, float scale,
@@ -473,17 +546,10 @@ hipError_t launch_bwd(const void* Q, const void* K, const void* V, const void* O
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    {
-        const int nkb = (N + 127) / 128;
-        attn_bwd_dkdv_kernel<D, CAUSAL><<<dim3((unsigned)(nkb * BH)), dim3(256), 0, stream>>>(
-            q, k, v, g, Lc, Dl, static_cast<__bf16*>(dK), static_cast<__bf16*>(dV), N, BH, scale);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    const int nqb = (N + 255) / 256;
-    attn_bwd_dq_kernel<D, CAUSAL><<<dim3((unsigned)(nqb * BH)), dim3(512), 0, stream>>>(
-        q, k, v, g, Lc, Dl, static_cast<__bf16*>(dQ), N, BH, nqb, scale);
-    return hipGetLastError();
+    if (const hipError_t e = launch_dkdv<D, CAUSAL>(q, k, v, g, Lc, Dl, dK, dV, BH, N, scale, stream);
+        e != hipSuccess)
+        return e;
+    return launch_dq<D, CAUSAL>(q, k, v, g, Lc, Dl, dQ, BH, N, scale, stream);
 }
 
 }  // namespace

@@ -18,8 +18,9 @@ Prints one JSON line:
                     of the same workload (and its parity on that sample)
   supplementary     measured after the timed region: the attention shape
                     without the mask, a plain device copy of the softmax
-                    input as the practical HBM ceiling, and the split-KV
-                    forward beside the single pass on long rows / few heads
+                    input as the practical HBM ceiling, the split-KV
+                    forward beside the single pass on long rows / few heads,
+                    and the backward pass of the headline workload
 """
 from __future__ import annotations
 
@@ -180,17 +181,21 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wa, ws, q_cpu, k_cpu, v_cpu, x_cpu, O, lse, y)
-    out["supplementary"] = supplementary(osm, wa, ws, q, k, v, x)
+    out["supplementary"] = supplementary(osm, wa, ws, q, k, v, x, O, lse)
     print(json.dumps(out), flush=True)
     return 0
 
 
-def supplementary(osm, wa, ws, q, k, v, x, reps=10):
+def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=10):
     """Figures measured after the timed region, not part of a step: the same
-    attention shape without the causal mask, and a plain device copy of the
+    attention shape without the causal mask, a plain device copy of the
     softmax input (the practical ceiling for a read-once / write-once
-    kernel on this GPU)."""
+    kernel on this GPU), the split-KV forward on long rows, and the backward
+    pass of the headline workload (its FLOPs counted as 2.5 times the
+    forward's, the five products of the gradient; the kernels compute seven)."""
     import torch
+
+    from online_softmax_08_amd import inputs
 
     def per_launch_ms(fn):
         for _ in range(2):
@@ -229,7 +234,17 @@ def supplementary(osm, wa, ws, q, k, v, x, reps=10):
             "nsplit": ns, "split_tflops": round(flops / (t_split * 1e-3) / 1e12, 1),
             "single_pass_tflops": round(flops / (t_one * 1e-3) / 1e12, 1),
             "split_ms": round(t_split, 4), "single_pass_ms": round(t_one, 4)}
+    # Backward of the headline workload, from the timed forward's O and lse.
+    go = inputs.grad_output(q.shape, wa.seed + 1).to(q.device)
+    wsb = torch.empty(osm.attn_bwd_workspace_bytes(wa.B, wa.H, wa.N), dtype=torch.uint8,
+                      device=q.device)
+    bwd_ms = per_launch_ms(lambda: osm.attention_backward(q, k, v, O, lse, go, causal=wa.causal,
+                                                          workspace=wsb))
+    bwd_flops = 2.5 * 4.0 * wa.B * wa.H * wa.N * wa.N * wa.d / (2 if wa.causal else 1)
     return {
+        "attn_backward": {"workload": f"{wa.name} backward (dQ, dK, dV)",
+                          "value": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 1), "unit": "TFLOPS",
+                          "flops_per_call": bwd_flops, "call_ms": round(bwd_ms, 4)},
         "attn_noncausal": {"workload": f"bf16 B={wa.B} H={wa.H} N={wa.N} d={wa.d}, no mask",
                            "value": round(nc_flops / (nc_ms * 1e-3) / 1e12, 2), "unit": "TFLOPS",
                            "kernel_ms": round(nc_ms, 4)},

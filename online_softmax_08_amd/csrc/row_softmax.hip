@@ -320,11 +320,11 @@ softmax_online(const float* x, float* y, int N)
 
 }  // namespace
 
-// Host-side dispatch.  Sizes were validated by the caller (B >= 1, N >= 1).
-hipError_t launch_row_softmax(const float* x, float* y, int B, int N, hipStream_t stream)
+namespace {
+
+// One dispatch over rows 0 .. B - 1 of x and y.
+hipError_t launch_rows(const float* x, float* y, int B, int N, bool vec, hipStream_t stream)
 {
-    const bool vec = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
-                     ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
     if (N <= kSoftmaxWaveMaxN) {
         const dim3 grid((B + 3) / 4), block(256);
         if (vec) {
@@ -364,6 +364,25 @@ hipError_t launch_row_softmax(const float* x, float* y, int B, int N, hipStream_
         else softmax_online<1024, false><<<grid, 1024, 0, stream>>>(x, y, N);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+// Host-side dispatch.  Sizes were validated by the caller (B >= 1, N >= 1).
+// A dispatch counts at most 2^32 - 1 work-items and the kernels use up to
+// 1024 per row, so rows go out in chunks of 2^21 (2^31 work-items at most).
+hipError_t launch_row_softmax(const float* x, float* y, int B, int N, hipStream_t stream)
+{
+    const bool vec = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
+    constexpr int kChunk = 1 << 21;
+    for (int r0 = 0; r0 < B; r0 += kChunk) {
+        const int rows = B - r0 < kChunk ? B - r0 : kChunk;
+        const hipError_t e = launch_rows(x + (size_t)r0 * N, y + (size_t)r0 * N, rows, N, vec, stream);
+        if (e != hipSuccess) return e;
+        if (B - r0 <= kChunk) break;
+    }
+    return hipSuccess;
 }
 
 }  // namespace osm

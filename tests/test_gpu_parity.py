@@ -269,3 +269,21 @@ def test_softmax_extreme_rows(osm):
     y = _gpu_softmax(osm, x)
     e = _maxabs(y, oracle.row_softmax(x))
     assert np.all(np.isfinite(y)) and e <= 1e-5
+
+
+@pytest.mark.parametrize("N", [3, 64])
+def test_softmax_more_rows_than_one_dispatch(osm, N):
+    # Rows go out in dispatches of 2^21 rows (the same loop for every row
+    # length); rows on both sides of the boundary and a random sample
+    # against the oracle, all rows finite.
+    B = (1 << 21) + 77
+    g = torch.Generator().manual_seed(N)
+    x = torch.randn((B, N), generator=g) * 3.0
+    y = _gpu_softmax(osm, x)
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(N)
+    rows = sorted({0, (1 << 21) - 2, (1 << 21) - 1, 1 << 21, (1 << 21) + 1, B - 1,
+                   *rng.choice(B, size=32, replace=False).tolist()})
+    e = _maxabs(y[rows], oracle.row_softmax(x[rows]))
+    print(f"softmax B={B} N={N}: {len(rows)} rows max|dy|={e:.3e}", flush=True)
+    assert e <= 1e-5

@@ -20,7 +20,8 @@ Prints one JSON line:
                     without the mask, a plain device copy of the softmax
                     input as the practical HBM ceiling, the split-KV
                     forward beside the single pass on long rows / few heads,
-                    and the backward pass of the headline workload
+                    packed variable-length sequences beside padding, and the
+                    backward pass of the headline workload
 """
 from __future__ import annotations
 
@@ -234,6 +235,25 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=10):
             "nsplit": ns, "split_tflops": round(flops / (t_split * 1e-3) / 1e12, 1),
             "single_pass_tflops": round(flops / (t_one * 1e-3) / 1e12, 1),
             "split_ms": round(t_split, 4), "single_pass_ms": round(t_one, 4)}
+    # Packed variable-length sequences (8 lengths from 387 to 7007, 16 heads,
+    # d = 128) beside the same sequences padded to the longest.
+    lengths = [7007, 5311, 4312, 2397, 2699, 581, 853, 387]
+    Hv, dv, Lmax, tot = 16, 128, max(lengths), sum(lengths)
+    g = torch.Generator().manual_seed(11)
+    qv, kv_, vv = (torch.randn((Hv, tot, dv), generator=g).to(torch.bfloat16).to(q.device)
+                   for _ in range(3))
+    qp, kp, vp = (torch.randn((len(lengths), Hv, Lmax, dv), generator=g).to(torch.bfloat16)
+                  .to(q.device) for _ in range(3))
+    cu = torch.tensor([0] + list(__import__("itertools").accumulate(lengths)), dtype=torch.int32,
+                      device=q.device)
+    varlen = {"workload": f"bf16 H={Hv} d={dv}, sequence lengths {lengths}"}
+    for causal in (False, True):
+        useful = sum(4.0 * Hv * n * n * dv / (2 if causal else 1) for n in lengths)
+        t_packed = per_launch_ms(lambda: osm.attention_varlen(qv, kv_, vv, cu, Lmax, causal=causal))
+        t_padded = per_launch_ms(lambda: osm.attention(qp, kp, vp, causal=causal))
+        varlen["causal" if causal else "noncausal"] = {
+            "packed_tflops_useful": round(useful / (t_packed * 1e-3) / 1e12, 1),
+            "packed_ms": round(t_packed, 4), "padded_ms": round(t_padded, 4)}
     # Backward of the headline workload, from the timed forward's O and lse.
     go = inputs.grad_output(q.shape, wa.seed + 1).to(q.device)
     wsb = torch.empty(osm.attn_bwd_workspace_bytes(wa.B, wa.H, wa.N), dtype=torch.uint8,
@@ -252,6 +272,7 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=10):
                      "value": round(ws.bytes / (cp_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                      "kernel_ms": round(cp_ms, 4)},
         "attn_splitkv": split,
+        "attn_varlen": varlen,
     }
 
 

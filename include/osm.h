@@ -15,6 +15,12 @@
  *    The computation is the fused, tiled online softmax of Lesson 22,
  *    sections 21-24 and 32: S and P are never written to memory.
  *
+ *  attn_fwd_varlen
+ *    The same attention over a batch of sequences of different lengths
+ *    packed end to end with no padding: the padding mask of Lesson 22,
+ *    section 35 (keys past a sequence's length get weight 0) realised as the
+ *    packed, variable-length layout that section recommends.
+ *
  *  attn_fwd_splitkv / attn_combine
  *    The same attention with the keys of each query block divided into
  *    several ranges computed in parallel, each yielding a normalised partial
@@ -99,6 +105,32 @@ int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* lse,
  */
 int attn_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* lse,
                  int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * attn_fwd_varlen -- attn_fwd over packed variable-length sequences.
+ *   Q, K, V, O : bf16 [H][total][d]: head h's rows of every sequence, the
+ *                sequences end to end (sequence b is rows cu_seqlens[b] ..
+ *                cu_seqlens[b+1] - 1 of each head)
+ *   lse        : fp32 [H][total]
+ *   cu_seqlens : DEVICE int32 [B + 1], cu_seqlens[0] = 0, nondecreasing,
+ *                cu_seqlens[B] = total; read by the kernels, so the host
+ *                cannot check it: the caller guarantees it.  Entries outside
+ *                [0, total] are clamped and a sequence is cut at max_seqlen,
+ *                so a malformed array gives wrong results but no access
+ *                outside the tensors.
+ *   B, H, total : sequences, heads, packed rows (all >= 0)
+ *   max_seqlen : an upper bound of every sequence length (sets the grid)
+ *   d, scale, causal, stream : as for attn_fwd; queries and keys of one
+ *                sequence only see each other, causal counts positions
+ *                within the sequence
+ * Alignment: Q, K, V, O 16 bytes; lse and cu_seqlens 4.  O and lse may not
+ * overlap the inputs, cu_seqlens or each other.  Empty problems (B, H,
+ * total or max_seqlen 0) are a no-op.  With equal lengths the result is
+ * bitwise that of attn_fwd on the same rows.  Returns an osm_status.
+ */
+int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* lse,
+                    const int* cu_seqlens, int B, int H, int total, int max_seqlen, int d,
+                    float scale, int causal, void* stream);
 
 /*
  * attn_fwd_splitkv_plan -- resolve a split count and size its workspace.

@@ -32,6 +32,8 @@ _lib.attn_fwd_f32.restype = _i
 _lib.row_softmax.argtypes = [_vp, _vp, _i, _i, _vp]
 _lib.row_softmax.restype = _i
 _sz = ctypes.c_size_t
+_lib.attn_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]
+_lib.attn_fwd_varlen.restype = _i
 _lib.attn_fwd_splitkv_plan.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(_i),
                                        ctypes.POINTER(_sz)]
 _lib.attn_fwd_splitkv_plan.restype = _i
@@ -48,7 +50,7 @@ _lib.attn_bwd.restype = _i
 _lib.osm_status_str.argtypes = [_i]
 _lib.osm_status_str.restype = ctypes.c_char_p
 
-EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_splitkv_plan", "attn_fwd_splitkv",
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_varlen", "attn_fwd_splitkv_plan", "attn_fwd_splitkv",
            "attn_combine", "attn_bwd_workspace_bytes", "attn_bwd", "row_softmax",
            "osm_status_str")
 
@@ -137,3 +139,11 @@ def attn_bwd(Q: int, K: int, V: int, O: int, dO: int, lse: int, dQ: int, dK: int
     """Backward pass of attn_fwd (dQ, dK, dV); see include/osm.h."""
     _call("attn_bwd", Q, K, V, O, dO, lse, dQ, dK, dV, B, H, N, d, scale, int(bool(causal)),
           workspace, workspace_bytes, stream)
+
+
+def attn_fwd_varlen(Q: int, K: int, V: int, O: int, lse: int, cu_seqlens: int, B: int, H: int,
+                    total: int, max_seqlen: int, d: int, scale: float, causal: bool,
+                    stream: int = 0) -> None:
+    """bf16 attention over packed variable-length sequences; see include/osm.h."""
+    _call("attn_fwd_varlen", Q, K, V, O, lse, cu_seqlens, B, H, total, max_seqlen, d, scale,
+          int(bool(causal)), stream)

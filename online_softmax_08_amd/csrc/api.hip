@@ -128,6 +128,34 @@ int row_softmax(const float* x, float* y, int B, int N, void* stream)
     return finish(osm::launch_row_softmax(x, y, B, N, static_cast<hipStream_t>(stream)));
 }
 
+int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* lse,
+                    const int* cu_seqlens, int B, int H, int total, int max_seqlen, int d,
+                    float scale, int causal, void* stream)
+{
+    if (B < 0 || H < 0 || total < 0 || max_seqlen < 0) return OSM_ERR_SIZE;
+    if (d != 64 && d != 128) return OSM_ERR_HEAD_DIM;
+    if (!(std::isfinite(scale) && scale > 0.f)) return OSM_ERR_SCALE;
+    if (B == 0 || H == 0 || total == 0 || max_seqlen == 0) return OSM_OK;
+    // Per-workgroup limits are those of a dense call with N = max_seqlen.
+    int st = check_attn_shape(B, H, max_seqlen, d, scale, 2);
+    if (st != OSM_OK) return st;
+    if (!Q || !K || !V || !O || !lse || !cu_seqlens) return OSM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+        !aligned(lse, 4) || !aligned(cu_seqlens, 4))
+        return OSM_ERR_ALIGN;
+    const size_t tb = (size_t)H * total * d * 2, lb = (size_t)H * total * sizeof(float);
+    const size_t cb = (size_t)(B + 1) * sizeof(int);
+    if (overlaps(O, tb, Q, tb) || overlaps(O, tb, K, tb) || overlaps(O, tb, V, tb) ||
+        overlaps(O, tb, cu_seqlens, cb) || overlaps(lse, lb, Q, tb) ||
+        overlaps(lse, lb, K, tb) || overlaps(lse, lb, V, tb) || overlaps(lse, lb, O, tb) ||
+        overlaps(lse, lb, cu_seqlens, cb))
+        return OSM_ERR_ALIAS;
+    if ((st = check_device()) != OSM_OK) return st;
+    return finish(osm::launch_attn_fwd_bf16_varlen(Q, K, V, O, lse, cu_seqlens, B, H, total,
+                                                   max_seqlen, d, scale, causal != 0,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 int attn_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int nsplit, int* nsplit_out,
                           size_t* workspace_bytes)
 {

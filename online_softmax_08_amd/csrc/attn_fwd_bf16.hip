@@ -98,6 +98,31 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, lds_void_t*
 #endif
 }
 
+// Where the (batch, head) slice of a workgroup lives: dense tensors
+// [B*H][N][D] (lse [B*H][N]), or packed variable-length sequences
+// [H][total][D] (lse [H][total]) whose batch b holds rows cu[b] .. cu[b+1]-1
+// of every head.  Packed lengths are clamped to [0, Nmax] and to the packed
+// extent, so a malformed cu cannot move an access outside the tensors.
+struct Slice {
+    size_t base;   // element offset of row 0 of the slice in Q, K, V, O
+    size_t lbase;  // element offset of row 0 in lse
+    int n;         // rows (queries = keys) of the slice
+};
+
+template <int D, bool VARLEN>
+__device__ __forceinline__ Slice slice_of(int bh, int Nmax, int H, const int* cu, int total)
+{
+    if constexpr (!VARLEN) {
+        return {(size_t)bh * Nmax * D, (size_t)bh * Nmax, Nmax};
+    } else {
+        const int b = bh / H, hh = bh - b * H;
+        const int start = min(max(__builtin_amdgcn_readfirstlane(cu[b]), 0), total);
+        const int end = min(max(__builtin_amdgcn_readfirstlane(cu[b + 1]), start), total);
+        const size_t row0 = (size_t)hh * total + start;
+        return {row0 * D, row0, min(end - start, Nmax)};
+    }
+}
+
 template <int D, int QT, int NW, int BC_>
 struct Cfg {
     static constexpr int BC = BC_;            // keys per tile
@@ -123,13 +148,15 @@ struct Cfg {
 // opart [nsplit][BH][N][D] and the partial logsumexp to lpart [nsplit][BH][N]
 // (-inf for a row that sees no key of the range); attn_combine_kernel merges
 // them.  O and lse are then unused.
-template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL, bool SPLIT>
+template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL, bool SPLIT, bool VARLEN>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, __bf16* __restrict__ O,
-                     float* __restrict__ lse, int N, int BH, int nqt, float scale,
-                     float* __restrict__ opart, float* __restrict__ lpart, int nsplit)
+                     float* __restrict__ lse, int Nmax, int BH, int nqt, float scale,
+                     float* __restrict__ opart, float* __restrict__ lpart, int nsplit,
+                     const int* __restrict__ cu, int H, int total)
 {
+    static_assert(!(SPLIT && VARLEN), "split-KV runs on dense tensors");
     using C = Cfg<D, QT, NW, BC>;
     constexpr int NMT = BC / 32;  // 32-key MFMA tiles per key tile
     // Four separate LDS objects (not slices of one array): the compiler can
@@ -158,7 +185,10 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
     const int qt = CAUSAL ? nqt - 1 - t : t;
     const int q0 = qt * C::BR;
-    const size_t base = (size_t)bh * N * D;
+    const Slice sl = slice_of<D, VARLEN>(bh, Nmax, H, cu, total);
+    const int N = sl.n;
+    if (VARLEN && q0 >= N) return;  // query block past this sequence (whole workgroup)
+    const size_t base = sl.base;
     const uint32_t slice_b = (uint32_t)N * D * 2;
     const int qw0 = q0 + wave * QT * 32;  // first query row of this wave
 
@@ -435,7 +465,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
     // ---- epilogue: O = acc / l in bf16 (rows past N dropped), lse = m scale + ln l ----
     const __amdgpu_buffer_rsrc_t ors = make_rsrc(O + base, slice_b);
-    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lse + (size_t)bh * N, (uint32_t)N * 4);
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lse + sl.lbase, (uint32_t)N * 4);
 #pragma unroll
     for (int nt = 0; nt < QT; ++nt) {
         const int q = qw0 + nt * 32 + j;
@@ -467,11 +497,12 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 // Tile i is read in phases 2i (waves 0-3) and 2i + 1 (waves 4-7); the loads
 // of K(i + 1) and V(i) start in phase 2i and are waited for before the
 // barrier that ends phase 2i + 1.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                         const __bf16* __restrict__ V, __bf16* __restrict__ O,
-                        float* __restrict__ lse, int N, int BH, int nqt, float scale)
+                        float* __restrict__ lse, int Nmax, int BH, int nqt, float scale,
+                        const int* __restrict__ cu, int H, int total)
 {
     constexpr int NW = 8, BC = 64;
     using C = Cfg<D, 1, NW, BC>;
@@ -489,7 +520,10 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     const int t = blockIdx.x / BH, bh = blockIdx.x - t * BH;
     const int qt = CAUSAL ? nqt - 1 - t : t;
     const int q0 = qt * C::BR;
-    const size_t base = (size_t)bh * N * D;
+    const Slice sl = slice_of<D, VARLEN>(bh, Nmax, H, cu, total);
+    const int N = sl.n;
+    if (VARLEN && q0 >= N) return;  // query block past this sequence (whole workgroup)
+    const size_t base = sl.base;
     const uint32_t slice_b = (uint32_t)N * D * 2;
     const int qw0 = q0 + wave * 32;
     const int qrow = qw0 + j;
@@ -718,7 +752,7 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         steps(std::false_type{});
 
     const __amdgpu_buffer_rsrc_t ors = make_rsrc(O + base, slice_b);
-    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lse + (size_t)bh * N, (uint32_t)N * 4);
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lse + sl.lbase, (uint32_t)N * 4);
     const float l_tot = combine_xor32(l, SumOp());
     const float inv = 1.0f / l_tot;
 #pragma unroll
@@ -736,29 +770,31 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
                                               (uint32_t)qrow * 4, 0, 0);
 }
 
-template <int D, bool CAUSAL>
+// N is the sequence length, or with cu (packed sequences) the longest
+// sequence; H and total describe the packed layout (unused when dense).
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_pp(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
-                     int N, float scale, hipStream_t stream)
+                     int N, float scale, const int* cu, int H, int total, hipStream_t stream)
 {
     constexpr int BR = 256;
     const int nqt = (N + BR - 1) / BR;
     const dim3 grid((unsigned)(nqt * BH)), block(512);
-    attn_fwd_bf16_pp_kernel<D, CAUSAL><<<grid, block, 0, stream>>>(
+    attn_fwd_bf16_pp_kernel<D, CAUSAL, VARLEN><<<grid, block, 0, stream>>>(
         static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
-        static_cast<__bf16*>(O), lse, N, BH, nqt, scale);
+        static_cast<__bf16*>(O), lse, N, BH, nqt, scale, cu, H, total);
     return hipGetLastError();
 }
 
-template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL>
+template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL, bool VARLEN>
 hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
-                  int N, float scale, hipStream_t stream)
+                  int N, float scale, const int* cu, int H, int total, hipStream_t stream)
 {
     using C = Cfg<D, QT, NW, BC>;
     const int nqt = (N + C::BR - 1) / C::BR;
     const dim3 grid((unsigned)(nqt * BH)), block(C::T);
-    attn_fwd_bf16_kernel<D, QT, NW, WPE, BC, CAUSAL, false><<<grid, block, 0, stream>>>(
+    attn_fwd_bf16_kernel<D, QT, NW, WPE, BC, CAUSAL, false, VARLEN><<<grid, block, 0, stream>>>(
         static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
-        static_cast<__bf16*>(O), lse, N, BH, nqt, scale, nullptr, nullptr, 1);
+        static_cast<__bf16*>(O), lse, N, BH, nqt, scale, nullptr, nullptr, 1, cu, H, total);
     return hipGetLastError();
 }
 
@@ -768,20 +804,21 @@ hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* l
 // With 8 waves the phase-staggered kernel serves the causal case (it
 // measures faster there); without the mask the two measure alike and the
 // plain kernel is kept.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN = false>
 hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
-                    int N, float scale, hipStream_t stream)
+                    int N, float scale, hipStream_t stream, const int* cu = nullptr, int H = 1,
+                    int total = 0)
 {
     constexpr long long kCUs = 256;
     if ((long long)((N + 255) / 256) * BH >= kCUs) {
         if constexpr (CAUSAL)
-            return launch_pp<D, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
+            return launch_pp<D, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, total, stream);
         else
-            return launch<D, 1, 8, 2, 64, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
+            return launch<D, 1, 8, 2, 64, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, total, stream);
     }
     if ((long long)((N + 127) / 128) * BH >= kCUs)
-        return launch<D, 1, 4, 2, 64, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
-    return launch<D, 1, 2, 2, 64, CAUSAL>(Q, K, V, O, lse, BH, N, scale, stream);
+        return launch<D, 1, 4, 2, 64, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, total, stream);
+    return launch<D, 1, 2, 2, 64, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, total, stream);
 }
 
 // Merge of split partials, one row per D / 4 lanes (four fp32 columns per
@@ -836,11 +873,11 @@ hipError_t launch_split(const void* Q, const void* K, const void* V, void* O, fl
 {
     using C = Cfg<D, 1, 8, 64>;
     const int nqt = (N + C::BR - 1) / C::BR;
-    attn_fwd_bf16_kernel<D, 1, 8, 2, 64, CAUSAL, true>
+    attn_fwd_bf16_kernel<D, 1, 8, 2, 64, CAUSAL, true, false>
         <<<dim3((unsigned)(nqt * nsplit * BH)), dim3(C::T), 0, stream>>>(
             static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K),
             static_cast<const __bf16*>(V), nullptr, nullptr, N, BH, nqt, scale, opart, lpart,
-            nsplit);
+            nsplit, nullptr, 1, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_attn_combine(opart, lpart, O, lse, nsplit, (long long)BH * N, D, stream);
@@ -892,6 +929,19 @@ hipError_t launch_attn_fwd_bf16_split(const void* Q, const void* K, const void* 
                       : launch_split<64, false>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, stream);
     return causal ? launch_split<128, true>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, stream)
                   : launch_split<128, false>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, stream);
+}
+
+hipError_t launch_attn_fwd_bf16_varlen(const void* Q, const void* K, const void* V, void* O,
+                                       float* lse, const int* cu, int B, int H, int total,
+                                       int max_seqlen, int d, float scale, bool causal,
+                                       hipStream_t stream)
+{
+    const int BH = B * H;
+    if (d == 64)
+        return causal ? dispatch<64, true, true>(Q, K, V, O, lse, BH, max_seqlen, scale, stream, cu, H, total)
+                      : dispatch<64, false, true>(Q, K, V, O, lse, BH, max_seqlen, scale, stream, cu, H, total);
+    return causal ? dispatch<128, true, true>(Q, K, V, O, lse, BH, max_seqlen, scale, stream, cu, H, total)
+                  : dispatch<128, false, true>(Q, K, V, O, lse, BH, max_seqlen, scale, stream, cu, H, total);
 }
 
 hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, void* O,

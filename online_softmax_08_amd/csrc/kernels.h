@@ -17,6 +17,12 @@ hipError_t launch_row_softmax(const float* x, float* y, int B, int N, hipStream_
 hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, void* O,
                                 float* lse, int BH, int N, int d, float scale, bool causal,
                                 hipStream_t stream);
+// Packed variable-length sequences: Q, K, V, O [H][total][d], lse [H][total],
+// cu: device int32 [B + 1] row offsets, sequences no longer than max_seqlen.
+hipError_t launch_attn_fwd_bf16_varlen(const void* Q, const void* K, const void* V, void* O,
+                                       float* lse, const int* cu, int B, int H, int total,
+                                       int max_seqlen, int d, float scale, bool causal,
+                                       hipStream_t stream);
 // Split-KV forward.  opart: fp32 [nsplit][B*H][N][d], lpart: fp32
 // [nsplit][B*H][N] (workspace); 1 <= nsplit <= kMaxSplits.
 constexpr int kMaxSplits = 64;

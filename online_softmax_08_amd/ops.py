@@ -49,6 +49,36 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     return out, lse
 
 
+def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = False,
+                     scale: float | None = None):
+    """Attention over packed variable-length sequences.
+
+    q, k, v: contiguous bf16 [H, total, d] (every head's rows of all sequences
+    end to end); cu_seqlens: int32 GPU tensor [B + 1] of row offsets;
+    max_seqlen: an upper bound of the lengths.  Returns (O bf16 [H, total, d],
+    lse fp32 [H, total]).
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 [H, total, d] GPU tensor")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [H, total, d] shape")
+    if (not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+            or not cu_seqlens.is_contiguous() or cu_seqlens.device != q.device):
+        raise ValueError("cu_seqlens must be a contiguous int32 [B + 1] tensor on q's device")
+    H, total, d = q.shape
+    B = cu_seqlens.numel() - 1
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q)
+    lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        _abi.attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), cu_seqlens.data_ptr(), max(B, 0), H, total,
+                             int(max_seqlen), d, scale, causal, _stream_handle(q.device))
+    return out, lse
+
+
 def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
                       scale: float | None = None, nsplit: int = 0,
                       workspace: torch.Tensor | None = None):

@@ -23,7 +23,8 @@ def abi():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_splitkv_plan",
+    assert _declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_varlen",
+                                            "attn_fwd_splitkv_plan",
                                             "attn_fwd_splitkv", "attn_combine",
                                             "attn_bwd_workspace_bytes", "attn_bwd", "row_softmax",
                                             "osm_status_str"])
@@ -212,3 +213,30 @@ def test_bwd_workspace_and_validation(abi):
     assert status(dK=ptr["lse"]) == abi.OSM_ERR_ALIAS        # dK is lse
     assert status(ws=ptr["dO"] + 32) == abi.OSM_ERR_ALIAS    # workspace inside dO
     abi.attn_bwd(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 2, 16, 64, 0.125, 1, 0, 0)  # empty: no-op
+
+
+def test_varlen_validation(abi):
+    ptr = {n: (i + 1) * FAKE for i, n in enumerate(("Q", "K", "V", "O", "lse", "cu"))}
+
+    def status(**kw):
+        a = dict(ptr, B=2, H=2, total=100, maxs=64, d=64, scale=0.125, causal=0)
+        a.update(kw)
+        with pytest.raises(abi.OsmError) as e:
+            abi.attn_fwd_varlen(a["Q"], a["K"], a["V"], a["O"], a["lse"], a["cu"], a["B"], a["H"],
+                                a["total"], a["maxs"], a["d"], a["scale"], a["causal"])
+        return e.value.status
+    assert status(B=-1) == abi.OSM_ERR_SIZE
+    assert status(total=-5) == abi.OSM_ERR_SIZE
+    assert status(maxs=-1) == abi.OSM_ERR_SIZE
+    assert status(d=80) == abi.OSM_ERR_HEAD_DIM
+    assert status(scale=float("inf")) == abi.OSM_ERR_SCALE
+    assert status(cu=0) == abi.OSM_ERR_NULL
+    assert status(cu=ptr["cu"] + 2) == abi.OSM_ERR_ALIGN
+    assert status(O=ptr["O"] + 8) == abi.OSM_ERR_ALIGN
+    assert status(O=ptr["V"] + 64) == abi.OSM_ERR_ALIAS        # O inside V
+    assert status(lse=ptr["cu"]) == abi.OSM_ERR_ALIAS          # lse on cu_seqlens
+    assert status(maxs=1 << 26, d=128) == abi.OSM_ERR_SIZE     # one sequence beyond 32-bit offsets
+    for empty in (dict(B=0), dict(H=0), dict(total=0), dict(maxs=0)):
+        a = dict(B=2, H=2, total=100, maxs=64)
+        a.update(empty)
+        abi.attn_fwd_varlen(0, 0, 0, 0, 0, 0, a["B"], a["H"], a["total"], a["maxs"], 64, 0.125, 1)

@@ -15,6 +15,14 @@
  *    The computation is the fused, tiled online softmax of Lesson 22,
  *    sections 21-24 and 32: S and P are never written to memory.
  *
+ *  attn_fwd_gqa
+ *    The same attention with fewer key/value heads than query heads
+ *    (grouped- and multi-query attention, among the variants a production
+ *    kernel must serve in "Operator fusion seen through FlashAttention",
+ *    the list of interface semantics): query head h attends with key/value
+ *    head h / (H / Hkv).  Every key/value-head argument below has this
+ *    meaning; Hkv = H is attn_fwd.
+ *
  *  attn_fwd_varlen
  *    The same attention over a batch of sequences of different lengths
  *    packed end to end with no padding: the padding mask of Lesson 22,
@@ -79,7 +87,8 @@ typedef enum {
     OSM_ERR_DEVICE = 7,   /* the current device is not a gfx950 GPU            */
     OSM_ERR_HIP = 8,      /* the HIP runtime reported an error at launch       */
     OSM_ERR_SPLITS = 9,   /* a split count is outside its documented range     */
-    OSM_ERR_WORKSPACE = 10 /* workspace_bytes is below what the plan requires  */
+    OSM_ERR_WORKSPACE = 10, /* workspace_bytes is below what the call requires */
+    OSM_ERR_HEADS = 11     /* Hkv is not a divisor of H in 1 .. H               */
 } osm_status;
 
 /*
@@ -107,10 +116,23 @@ int attn_fwd_f32(const float* Q, const float* K, const float* V, float* O, float
                  int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
+ * attn_fwd_gqa -- attn_fwd with Hkv key/value heads.
+ *   Q, O : bf16 [B][H][N][d];  K, V : bf16 [B][Hkv][N][d];  lse : fp32 [B][H][N]
+ *   Hkv  : 1 <= Hkv <= H, H % Hkv == 0 (else OSM_ERR_HEADS); query head h
+ *          reads key/value head h / (H / Hkv)
+ * Other arguments, alignment and errors as for attn_fwd.  With Hkv = H the
+ * result is bitwise that of attn_fwd.
+ */
+int attn_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* lse,
+                 int B, int H, int Hkv, int N, int d, float scale, int causal, void* stream);
+
+/*
  * attn_fwd_varlen -- attn_fwd over packed variable-length sequences.
- *   Q, K, V, O : bf16 [H][total][d]: head h's rows of every sequence, the
+ *   Q, O       : bf16 [H][total][d]: head h's rows of every sequence, the
  *                sequences end to end (sequence b is rows cu_seqlens[b] ..
  *                cu_seqlens[b+1] - 1 of each head)
+ *   K, V       : bf16 [Hkv][total][d], the same packing (Hkv as for
+ *                attn_fwd_gqa)
  *   lse        : fp32 [H][total]
  *   cu_seqlens : DEVICE int32 [B + 1], cu_seqlens[0] = 0, nondecreasing,
  *                cu_seqlens[B] = total; read by the kernels, so the host
@@ -129,8 +151,8 @@ int attn_fwd_f32(const float* Q, const float* K, const float* V, float* O, float
  * bitwise that of attn_fwd on the same rows.  Returns an osm_status.
  */
 int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* lse,
-                    const int* cu_seqlens, int B, int H, int total, int max_seqlen, int d,
-                    float scale, int causal, void* stream);
+                    const int* cu_seqlens, int B, int H, int Hkv, int total, int max_seqlen,
+                    int d, float scale, int causal, void* stream);
 
 /*
  * attn_fwd_splitkv_plan -- resolve a split count and size its workspace.
@@ -150,7 +172,8 @@ int attn_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int nsplit,
 
 /*
  * attn_fwd_splitkv -- attn_fwd computed as nsplit parallel key ranges plus a
- * merge.  Q, K, V, O, lse, B, H, N, d, scale, causal, stream as for attn_fwd.
+ * merge.  Q, K, V, O, lse, B, H, Hkv, N, d, scale, causal, stream as for
+ * attn_fwd_gqa (Hkv = H for plain multi-head attention).
  *   nsplit          : 0 (library's choice) or 1 .. 64.  Each 256-row query
  *                     block divides its visible key tiles (64 keys each)
  *                     into nsplit near-equal contiguous ranges; ranges past
@@ -168,7 +191,7 @@ int attn_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int nsplit,
  * OSM_ERR_SIZE if N * d * 4 does not fit in 32 bits).
  */
 int attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* lse,
-                     int B, int H, int N, int d, float scale, int causal, int nsplit,
+                     int B, int H, int Hkv, int N, int d, float scale, int causal, int nsplit,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -196,15 +219,19 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N);
 
 /*
  * attn_bwd -- backward pass of attn_fwd (bf16 inputs, fp32 accumulation).
- *   Q, K, V : const bf16 [B][H][N][d], the forward's inputs
+ *   Q       : const bf16 [B][H][N][d], K, V : const bf16 [B][Hkv][N][d], the
+ *             forward's inputs (Hkv as for attn_fwd_gqa; Hkv = H for
+ *             attn_fwd)
  *   O       : const bf16 [B][H][N][d], the forward's output
  *   dO      : const bf16 [B][H][N][d], the gradient of the loss w.r.t. O
  *   lse     : const fp32 [B][H][N], the forward's logsumexp
- *   dQ, dK, dV : bf16 [B][H][N][d], written (round-to-nearest-even):
- *             dV = P^T dO, dQ = scale dS K, dK = scale dS^T Q with
- *             P_ij = exp(scale q_i.k_j - lse_i) over the visible keys and
- *             dS_ij = P_ij (dO_i.v_j - sum_t dO_it O_it)
- *   B, H, N, d, scale, causal : as for the forward call that produced O, lse
+ *   dQ      : bf16 [B][H][N][d];  dK, dV : bf16 [B][Hkv][N][d], written
+ *             (round-to-nearest-even): dV = P^T dO, dQ = scale dS K,
+ *             dK = scale dS^T Q with P_ij = exp(scale q_i.k_j - lse_i) over
+ *             the visible keys and dS_ij = P_ij (dO_i.v_j - sum_t dO_it O_it);
+ *             a key/value head's dK and dV sum over the query heads that
+ *             read it
+ *   B, H, Hkv, N, d, scale, causal : as for the forward call
  *   workspace : device memory of at least attn_bwd_workspace_bytes(B, H, N),
  *             16-byte aligned, caller-owned, contents irrelevant on entry
  *   stream  : hipStream_t or NULL
@@ -215,7 +242,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N);
  * an osm_status (OSM_ERR_WORKSPACE if workspace_bytes is too small).
  */
 int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-             const float* lse, void* dQ, void* dK, void* dV, int B, int H, int N, int d,
+             const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N, int d,
              float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*

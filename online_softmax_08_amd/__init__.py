@@ -3,7 +3,8 @@
 The computation runs in hand-written HIP kernels inside ``libosm.so`` (built
 by ``online_softmax_08_amd.build``); this package only marshals arguments.
 
-* ``attn_fwd``, ``attn_fwd_f32``, ``attn_fwd_varlen``, ``attn_fwd_splitkv_plan``,
+* ``attn_fwd``, ``attn_fwd_f32``, ``attn_fwd_gqa``, ``attn_fwd_varlen``,
+  ``attn_fwd_splitkv_plan``,
   ``attn_fwd_splitkv``, ``attn_combine``, ``attn_bwd_workspace_bytes``,
   ``attn_bwd``, ``row_softmax``, ``osm_status_str`` are the C ABI of
   include/osm.h under the same names (device pointers as ints).
@@ -12,12 +13,14 @@ by ``online_softmax_08_amd.build``); this package only marshals arguments.
   allocate the outputs with torch and launch on torch's current stream.
 """
 from ._abi import (OsmError, attn_bwd, attn_bwd_workspace_bytes, attn_combine, attn_fwd,
-                   attn_fwd_f32, attn_fwd_splitkv, attn_fwd_splitkv_plan, attn_fwd_varlen,
+                   attn_fwd_f32, attn_fwd_gqa, attn_fwd_splitkv, attn_fwd_splitkv_plan,
+                   attn_fwd_varlen,
                    library_path, osm_status_str, row_softmax)
 from .ops import (attention, attention_backward, attention_combine, attention_splitkv,
                   attention_varlen, softmax)
 
-__all__ = ["OsmError", "attn_fwd", "attn_fwd_f32", "attn_fwd_varlen", "attn_fwd_splitkv_plan",
+__all__ = ["OsmError", "attn_fwd", "attn_fwd_f32", "attn_fwd_gqa", "attn_fwd_varlen",
+           "attn_fwd_splitkv_plan",
            "attn_fwd_splitkv",
            "attn_combine", "attn_bwd_workspace_bytes", "attn_bwd", "row_softmax",
            "osm_status_str", "library_path", "attention", "attention_varlen", "attention_splitkv",

@@ -32,25 +32,27 @@ _lib.attn_fwd_f32.restype = _i
 _lib.row_softmax.argtypes = [_vp, _vp, _i, _i, _vp]
 _lib.row_softmax.restype = _i
 _sz = ctypes.c_size_t
-_lib.attn_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]
+_lib.attn_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]
 _lib.attn_fwd_varlen.restype = _i
+_lib.attn_fwd_gqa.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]
+_lib.attn_fwd_gqa.restype = _i
 _lib.attn_fwd_splitkv_plan.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(_i),
                                        ctypes.POINTER(_sz)]
 _lib.attn_fwd_splitkv_plan.restype = _i
-_lib.attn_fwd_splitkv.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp, _sz,
-                                  _vp]
+_lib.attn_fwd_splitkv.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp,
+                                  _sz, _vp]
 _lib.attn_fwd_splitkv.restype = _i
 _lib.attn_combine.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
 _lib.attn_combine.restype = _i
 _lib.attn_bwd_workspace_bytes.argtypes = [_i, _i, _i]
 _lib.attn_bwd_workspace_bytes.restype = _sz
-_lib.attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i,
-                          _vp, _sz, _vp]
+_lib.attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
+                          _i, _vp, _sz, _vp]
 _lib.attn_bwd.restype = _i
 _lib.osm_status_str.argtypes = [_i]
 _lib.osm_status_str.restype = ctypes.c_char_p
 
-EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_varlen", "attn_fwd_splitkv_plan", "attn_fwd_splitkv",
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_gqa", "attn_fwd_varlen", "attn_fwd_splitkv_plan", "attn_fwd_splitkv",
            "attn_combine", "attn_bwd_workspace_bytes", "attn_bwd", "row_softmax",
            "osm_status_str")
 
@@ -65,6 +67,7 @@ OSM_ERR_DEVICE = 7
 OSM_ERR_HIP = 8
 OSM_ERR_SPLITS = 9
 OSM_ERR_WORKSPACE = 10
+OSM_ERR_HEADS = 11
 
 
 class OsmError(RuntimeError):
@@ -114,11 +117,11 @@ def attn_fwd_splitkv_plan(B: int, H: int, N: int, d: int, causal: bool,
     return n_out.value, ws.value
 
 
-def attn_fwd_splitkv(Q: int, K: int, V: int, O: int, lse: int, B: int, H: int, N: int, d: int,
-                     scale: float, causal: bool, nsplit: int, workspace: int,
+def attn_fwd_splitkv(Q: int, K: int, V: int, O: int, lse: int, B: int, H: int, Hkv: int,
+                     N: int, d: int, scale: float, causal: bool, nsplit: int, workspace: int,
                      workspace_bytes: int, stream: int = 0) -> None:
     """bf16 attention forward over nsplit parallel key ranges; see include/osm.h."""
-    _call("attn_fwd_splitkv", Q, K, V, O, lse, B, H, N, d, scale, int(bool(causal)), nsplit,
+    _call("attn_fwd_splitkv", Q, K, V, O, lse, B, H, Hkv, N, d, scale, int(bool(causal)), nsplit,
           workspace, workspace_bytes, stream)
 
 
@@ -134,16 +137,22 @@ def attn_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
 
 
 def attn_bwd(Q: int, K: int, V: int, O: int, dO: int, lse: int, dQ: int, dK: int, dV: int,
-             B: int, H: int, N: int, d: int, scale: float, causal: bool, workspace: int,
+             B: int, H: int, Hkv: int, N: int, d: int, scale: float, causal: bool, workspace: int,
              workspace_bytes: int, stream: int = 0) -> None:
-    """Backward pass of attn_fwd (dQ, dK, dV); see include/osm.h."""
-    _call("attn_bwd", Q, K, V, O, dO, lse, dQ, dK, dV, B, H, N, d, scale, int(bool(causal)),
+    """Backward pass of attn_fwd / attn_fwd_gqa (dQ, dK, dV); see include/osm.h."""
+    _call("attn_bwd", Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale, int(bool(causal)),
           workspace, workspace_bytes, stream)
 
 
 def attn_fwd_varlen(Q: int, K: int, V: int, O: int, lse: int, cu_seqlens: int, B: int, H: int,
-                    total: int, max_seqlen: int, d: int, scale: float, causal: bool,
+                    Hkv: int, total: int, max_seqlen: int, d: int, scale: float, causal: bool,
                     stream: int = 0) -> None:
     """bf16 attention over packed variable-length sequences; see include/osm.h."""
-    _call("attn_fwd_varlen", Q, K, V, O, lse, cu_seqlens, B, H, total, max_seqlen, d, scale,
+    _call("attn_fwd_varlen", Q, K, V, O, lse, cu_seqlens, B, H, Hkv, total, max_seqlen, d, scale,
           int(bool(causal)), stream)
+
+
+def attn_fwd_gqa(Q: int, K: int, V: int, O: int, lse: int, B: int, H: int, Hkv: int, N: int,
+                 d: int, scale: float, causal: bool, stream: int = 0) -> None:
+    """bf16 attention with Hkv key/value heads; see include/osm.h."""
+    _call("attn_fwd_gqa", Q, K, V, O, lse, B, H, Hkv, N, d, scale, int(bool(causal)), stream)

@@ -60,22 +60,30 @@ int check_attn_shape(int B, int H, int N, int d, float scale, size_t elem)
     return OSM_OK;
 }
 
-// Shared validation of attn_fwd / attn_fwd_f32.  *work is set to false for an
-// empty problem (valid, nothing to launch).
+// Key/value heads: 1 <= Hkv <= H and Hkv divides H (checked once H > 0).
+int check_heads(int H, int Hkv)
+{
+    return (Hkv >= 1 && Hkv <= H && H % Hkv == 0) ? OSM_OK : OSM_ERR_HEADS;
+}
+
+// Shared validation of the dense forward calls (K and V with Hkv heads).
+// *work is set to false for an empty problem (valid, nothing to launch).
 int validate_attn(const void* Q, const void* K, const void* V, const void* O, const float* lse,
-                  int B, int H, int N, int d, float scale, size_t elem, bool* work)
+                  int B, int H, int Hkv, int N, int d, float scale, size_t elem, bool* work)
 {
     *work = false;
     int st = check_attn_shape(B, H, N, d, scale, elem);
     if (st != OSM_OK || B == 0 || H == 0 || N == 0) return st;
+    if ((st = check_heads(H, Hkv)) != OSM_OK) return st;
     const long long bh = (long long)B * H;
     if (!Q || !K || !V || !O || !lse) return OSM_ERR_NULL;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(lse, 4))
         return OSM_ERR_ALIGN;
     const size_t tbytes = (size_t)bh * N * d * elem, lbytes = (size_t)bh * N * sizeof(float);
-    if (overlaps(O, tbytes, Q, tbytes) || overlaps(O, tbytes, K, tbytes) ||
-        overlaps(O, tbytes, V, tbytes) || overlaps(lse, lbytes, Q, tbytes) ||
-        overlaps(lse, lbytes, K, tbytes) || overlaps(lse, lbytes, V, tbytes) ||
+    const size_t kvbytes = (size_t)B * Hkv * N * d * elem;
+    if (overlaps(O, tbytes, Q, tbytes) || overlaps(O, tbytes, K, kvbytes) ||
+        overlaps(O, tbytes, V, kvbytes) || overlaps(lse, lbytes, Q, tbytes) ||
+        overlaps(lse, lbytes, K, kvbytes) || overlaps(lse, lbytes, V, kvbytes) ||
         overlaps(lse, lbytes, O, tbytes))
         return OSM_ERR_ALIAS;
     *work = true;
@@ -97,10 +105,21 @@ int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* lse, i
              int N, int d, float scale, int causal, void* stream)
 {
     bool work = false;
-    int st = validate_attn(Q, K, V, O, lse, B, H, N, d, scale, 2, &work);
+    int st = validate_attn(Q, K, V, O, lse, B, H, H, N, d, scale, 2, &work);
     if (st != OSM_OK || !work) return st;
     if ((st = check_device()) != OSM_OK) return st;
-    return finish(osm::launch_attn_fwd_bf16(Q, K, V, O, lse, B * H, N, d, scale, causal != 0,
+    return finish(osm::launch_attn_fwd_bf16(Q, K, V, O, lse, B, H, H, N, d, scale, causal != 0,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H,
+                 int Hkv, int N, int d, float scale, int causal, void* stream)
+{
+    bool work = false;
+    int st = validate_attn(Q, K, V, O, lse, B, H, Hkv, N, d, scale, 2, &work);
+    if (st != OSM_OK || !work) return st;
+    if ((st = check_device()) != OSM_OK) return st;
+    return finish(osm::launch_attn_fwd_bf16(Q, K, V, O, lse, B, H, Hkv, N, d, scale, causal != 0,
                                             static_cast<hipStream_t>(stream)));
 }
 
@@ -108,7 +127,7 @@ int attn_fwd_f32(const float* Q, const float* K, const float* V, float* O, float
                  int H, int N, int d, float scale, int causal, void* stream)
 {
     bool work = false;
-    int st = validate_attn(Q, K, V, O, lse, B, H, N, d, scale, 4, &work);
+    int st = validate_attn(Q, K, V, O, lse, B, H, H, N, d, scale, 4, &work);
     if (st != OSM_OK || !work) return st;
     if ((st = check_device()) != OSM_OK) return st;
     return finish(osm::launch_attn_fwd_f32(Q, K, V, O, lse, B * H, N, d, scale, causal != 0,
@@ -129,8 +148,8 @@ int row_softmax(const float* x, float* y, int B, int N, void* stream)
 }
 
 int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* lse,
-                    const int* cu_seqlens, int B, int H, int total, int max_seqlen, int d,
-                    float scale, int causal, void* stream)
+                    const int* cu_seqlens, int B, int H, int Hkv, int total, int max_seqlen,
+                    int d, float scale, int causal, void* stream)
 {
     if (B < 0 || H < 0 || total < 0 || max_seqlen < 0) return OSM_ERR_SIZE;
     if (d != 64 && d != 128) return OSM_ERR_HEAD_DIM;
@@ -139,19 +158,20 @@ int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float*
     // Per-workgroup limits are those of a dense call with N = max_seqlen.
     int st = check_attn_shape(B, H, max_seqlen, d, scale, 2);
     if (st != OSM_OK) return st;
+    if ((st = check_heads(H, Hkv)) != OSM_OK) return st;
     if (!Q || !K || !V || !O || !lse || !cu_seqlens) return OSM_ERR_NULL;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
         !aligned(lse, 4) || !aligned(cu_seqlens, 4))
         return OSM_ERR_ALIGN;
     const size_t tb = (size_t)H * total * d * 2, lb = (size_t)H * total * sizeof(float);
-    const size_t cb = (size_t)(B + 1) * sizeof(int);
-    if (overlaps(O, tb, Q, tb) || overlaps(O, tb, K, tb) || overlaps(O, tb, V, tb) ||
+    const size_t kvb = (size_t)Hkv * total * d * 2, cb = (size_t)(B + 1) * sizeof(int);
+    if (overlaps(O, tb, Q, tb) || overlaps(O, tb, K, kvb) || overlaps(O, tb, V, kvb) ||
         overlaps(O, tb, cu_seqlens, cb) || overlaps(lse, lb, Q, tb) ||
-        overlaps(lse, lb, K, tb) || overlaps(lse, lb, V, tb) || overlaps(lse, lb, O, tb) ||
+        overlaps(lse, lb, K, kvb) || overlaps(lse, lb, V, kvb) || overlaps(lse, lb, O, tb) ||
         overlaps(lse, lb, cu_seqlens, cb))
         return OSM_ERR_ALIAS;
     if ((st = check_device()) != OSM_OK) return st;
-    return finish(osm::launch_attn_fwd_bf16_varlen(Q, K, V, O, lse, cu_seqlens, B, H, total,
+    return finish(osm::launch_attn_fwd_bf16_varlen(Q, K, V, O, lse, cu_seqlens, B, H, Hkv, total,
                                                    max_seqlen, d, scale, causal != 0,
                                                    static_cast<hipStream_t>(stream)));
 }
@@ -172,11 +192,11 @@ int attn_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int nsplit, in
 }
 
 int attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* lse, int B,
-                     int H, int N, int d, float scale, int causal, int nsplit, void* workspace,
-                     size_t workspace_bytes, void* stream)
+                     int H, int Hkv, int N, int d, float scale, int causal, int nsplit,
+                     void* workspace, size_t workspace_bytes, void* stream)
 {
     bool work = false;
-    int st = validate_attn(Q, K, V, O, lse, B, H, N, d, scale, 2, &work);
+    int st = validate_attn(Q, K, V, O, lse, B, H, Hkv, N, d, scale, 2, &work);
     if (st != OSM_OK) return st;
     if (nsplit < 0 || nsplit > osm::kMaxSplits) return OSM_ERR_SPLITS;
     if (!work) return OSM_OK;
@@ -184,7 +204,7 @@ int attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float
     if (nsplit == 0) nsplit = osm::attn_splitkv_auto((int)bh, N, d, causal != 0);
     if (nsplit == 1) {
         if ((st = check_device()) != OSM_OK) return st;
-        return finish(osm::launch_attn_fwd_bf16(Q, K, V, O, lse, (int)bh, N, d, scale, causal != 0,
+        return finish(osm::launch_attn_fwd_bf16(Q, K, V, O, lse, B, H, Hkv, N, d, scale, causal != 0,
                                                 static_cast<hipStream_t>(stream)));
     }
     // The partial pass launches bh * ceil(N / 256) * nsplit workgroups of 512
@@ -197,14 +217,15 @@ int attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float
     if (workspace_bytes < need) return OSM_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return OSM_ERR_ALIGN;
     const size_t tbytes = (size_t)bh * N * d * 2, lbytes = (size_t)bh * N * sizeof(float);
-    if (overlaps(workspace, need, Q, tbytes) || overlaps(workspace, need, K, tbytes) ||
-        overlaps(workspace, need, V, tbytes) || overlaps(workspace, need, O, tbytes) ||
+    const size_t kvbytes = (size_t)B * Hkv * N * d * 2;
+    if (overlaps(workspace, need, Q, tbytes) || overlaps(workspace, need, K, kvbytes) ||
+        overlaps(workspace, need, V, kvbytes) || overlaps(workspace, need, O, tbytes) ||
         overlaps(workspace, need, lse, lbytes))
         return OSM_ERR_ALIAS;
     if ((st = check_device()) != OSM_OK) return st;
     float* opart = static_cast<float*>(workspace);
     float* lpart = opart + (size_t)nsplit * bh * N * d;
-    return finish(osm::launch_attn_fwd_bf16_split(Q, K, V, O, lse, (int)bh, N, d, scale,
+    return finish(osm::launch_attn_fwd_bf16_split(Q, K, V, O, lse, B, H, Hkv, N, d, scale,
                                                   causal != 0, nsplit, opart, lpart,
                                                   static_cast<hipStream_t>(stream)));
 }
@@ -240,11 +261,12 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N)
 }
 
 int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-             const float* lse, void* dQ, void* dK, void* dV, int B, int H, int N, int d,
+             const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N, int d,
              float scale, int causal, void* workspace, size_t workspace_bytes, void* stream)
 {
     int st = check_attn_shape(B, H, N, d, scale, 2);
     if (st != OSM_OK || B == 0 || H == 0 || N == 0) return st;
+    if ((st = check_heads(H, Hkv)) != OSM_OK) return st;
     if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || !workspace)
         return OSM_ERR_NULL;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
@@ -255,22 +277,24 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
     const size_t need = attn_bwd_workspace_bytes(B, H, N);
     if (workspace_bytes < need) return OSM_ERR_WORKSPACE;
     const size_t tb = (size_t)bh * N * d * 2, lb = (size_t)bh * N * sizeof(float);
+    const size_t kvb = (size_t)B * Hkv * N * d * 2;
     const void* outs[3] = {dQ, dK, dV};
+    const size_t out_bytes[3] = {tb, kvb, kvb};
     const void* ins[6] = {Q, K, V, O, dO, lse};
-    const size_t in_bytes[6] = {tb, tb, tb, tb, tb, lb};
+    const size_t in_bytes[6] = {tb, kvb, kvb, tb, tb, lb};
     for (int a = 0; a < 3; ++a) {
         for (int b = 0; b < 6; ++b)
-            if (overlaps(outs[a], tb, ins[b], in_bytes[b])) return OSM_ERR_ALIAS;
+            if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return OSM_ERR_ALIAS;
         for (int b = a + 1; b < 3; ++b)
-            if (overlaps(outs[a], tb, outs[b], tb)) return OSM_ERR_ALIAS;
-        if (overlaps(outs[a], tb, workspace, need)) return OSM_ERR_ALIAS;
+            if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return OSM_ERR_ALIAS;
+        if (overlaps(outs[a], out_bytes[a], workspace, need)) return OSM_ERR_ALIAS;
     }
     for (int b = 0; b < 6; ++b)
         if (overlaps(workspace, need, ins[b], in_bytes[b])) return OSM_ERR_ALIAS;
     if ((st = check_device()) != OSM_OK) return st;
     float* Dl = static_cast<float*>(workspace);
     float* Lc = Dl + (size_t)bh * N;
-    return finish(osm::launch_attn_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, (int)bh, N, d, scale,
+    return finish(osm::launch_attn_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale,
                                             causal != 0, Dl, Lc, static_cast<hipStream_t>(stream)));
 }
 
@@ -288,6 +312,7 @@ const char* osm_status_str(int status)
     case OSM_ERR_HIP: return "the HIP runtime reported an error";
     case OSM_ERR_SPLITS: return "the number of key splits is out of range";
     case OSM_ERR_WORKSPACE: return "the workspace is smaller than the call requires";
+    case OSM_ERR_HEADS: return "key/value heads must divide the query heads (1 <= Hkv <= H)";
     default: return "unknown status";
     }
 }

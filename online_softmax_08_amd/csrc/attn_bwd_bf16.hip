@@ -13,7 +13,8 @@
 //
 // gfx950 design -- three kernels, no atomics, bitwise deterministic:
 //  * attn_bwd_delta_kernel: D and L log2(e) per row (HBM bound, reads O, dO).
-//  * attn_bwd_dkdv_kernel: one workgroup per (batch*head, 256 keys), a wave
+//  * attn_bwd_dkdv_kernel: one workgroup per (batch*key/value head, 256 keys),
+//    summing over the query heads that share the key/value head, a wave
 //    per 32 keys (two per SIMD), the keys' K rows held in VGPRs and their V
 //    rows in LDS for the whole kernel as the B operands of S = Q K^T and
 //    dP = dO V^T (one key per lane, the queries of a 32-query step in the
@@ -171,7 +172,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
 attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                      const float* __restrict__ Lc, const float* __restrict__ Dl,
-                     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int BH, float scale)
+                     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int BHkv, int H,
+                     int Hkv, float scale)
 {
     constexpr int BK = NW * 32, BQ = 64;
     using TQ = Tile<D, BQ>;
@@ -192,10 +194,13 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 31, h = lane >> 5;
     // Key blocks in natural order: under the mask the first ones see the
-    // most queries, so the longest workgroups start first.
-    const int t = blockIdx.x / BH, bh = blockIdx.x - t * BH;
+    // most queries, so the longest workgroups start first.  The workgroup's
+    // key/value head kvbh serves the query heads b H + hkv G .. + G - 1
+    // (G = H / Hkv), whose contributions it sums.
+    const int t = blockIdx.x / BHkv, kvbh = blockIdx.x - t * BHkv;
     const int k0 = t * BK, kw0 = k0 + wave * 32;
-    const size_t base = (size_t)bh * N * D;
+    const int G = H / Hkv, qbh0 = (kvbh / Hkv) * H + (kvbh % Hkv) * G;
+    const size_t base = (size_t)kvbh * N * D;
     const uint32_t slice_b = (uint32_t)N * D * 2;
     const float c = scale * kLog2e;
 
@@ -231,11 +236,19 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     uint32_t src[LPW];
 #pragma unroll
     for (int u = 0; u < LPW; ++u) src[u] = TQ::src_offset((wave + u * NW) * 64 + lane);
-    auto issue = [&](auto bc, int qt) {
-        const int r0 = qt * BQ;
+    // Steps it = 0 .. G * nq - 1 walk query head g = it / nq of the group and
+    // its query tile qt0 + it % nq.
+    const int nqt = (N + BQ - 1) / BQ;
+    const int qt0 = CAUSAL ? k0 / BQ : 0;     // first query tile with a visible pair
+    const int nq = nqt - qt0;
+    auto tile_of = [&](int it) { return qt0 + it % nq; };
+    auto qbase_of = [&](int it) { return (size_t)(qbh0 + it / nq) * N; };  // row 0 of the query head
+    auto issue = [&](auto bc, int it) {
+        const int r0 = tile_of(it) * BQ;
+        const size_t qb = (qbase_of(it) + r0) * D;
         const uint32_t left = (uint32_t)(N - r0) * D * 2;
-        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base + (size_t)r0 * D, left);
-        const __amdgpu_buffer_rsrc_t ors = make_rsrc(dO + base + (size_t)r0 * D, left);
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + qb, left);
+        const __amdgpu_buffer_rsrc_t ors = make_rsrc(dO + qb, left);
 #pragma unroll
         for (int u = 0; u < LPW; ++u) {
             const int i = wave + u * NW;
@@ -247,9 +260,9 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     };
     // Row statistics of a query tile: threads 0-63 fetch L log2(e), 64-127
     // fetch D (zero past N); written to LDS before the tile's barrier.
-    auto stat_load = [&](int qt) -> float {
-        const int q = qt * BQ + (tid & 63);
-        if (tid < 2 * BQ && q < N) return (tid < BQ ? Lc : Dl)[(size_t)bh * N + q];
+    auto stat_load = [&](int it) -> float {
+        const int q = tile_of(it) * BQ + (tid & 63);
+        if (tid < 2 * BQ && q < N) return (tid < BQ ? Lc : Dl)[qbase_of(it) + q];
         return 0.f;
     };
     auto stat_store = [&](auto bc, float v) {
@@ -257,11 +270,10 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         else if (tid < 2 * BQ) db[decltype(bc)::value][tid - BQ] = v;
     };
 
-    const int nqt = (N + BQ - 1) / BQ;
-    const int qt0 = CAUSAL ? k0 / BQ : 0;     // first query tile with a visible pair
     const int key = kw0 + j;                  // this lane's key
 
-    auto compute = [&](auto bc, int qt) {
+    auto compute = [&](auto bc, int it) {
+        const int qt = tile_of(it);
         if (CAUSAL && qt * BQ + BQ - 1 < kw0) return;  // every query precedes every key
         const char* qt_l = qbuf(bc);
         const char* ot_l = obuf(bc);
@@ -335,25 +347,26 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    if (qt0 < nqt) {
-        issue(B0{}, qt0);
-        stat_store(B0{}, stat_load(qt0));
+    const int nit = G * nq;
+    if (nq > 0) {
+        issue(B0{}, 0);
+        stat_store(B0{}, stat_load(0));
         __syncthreads();
-        for (int qt = qt0; qt < nqt; qt += 2) {
+        for (int it = 0; it < nit; it += 2) {
             float st = 0.f;
-            if (qt + 1 < nqt) {
-                issue(B1{}, qt + 1);
-                st = stat_load(qt + 1);
+            if (it + 1 < nit) {
+                issue(B1{}, it + 1);
+                st = stat_load(it + 1);
             }
-            compute(B0{}, qt);
+            compute(B0{}, it);
             stat_store(B1{}, st);
             __syncthreads();
-            if (qt + 1 >= nqt) break;
-            if (qt + 2 < nqt) {
-                issue(B0{}, qt + 2);
-                st = stat_load(qt + 2);
+            if (it + 1 >= nit) break;
+            if (it + 2 < nit) {
+                issue(B0{}, it + 2);
+                st = stat_load(it + 2);
             }
-            compute(B1{}, qt + 1);
+            compute(B1{}, it + 1);
             stat_store(B0{}, st);
             __syncthreads();
         }
@@ -368,7 +381,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
 attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                    const float* __restrict__ Lc, const float* __restrict__ Dl,
-                   __bf16* __restrict__ dQ, int N, int BH, int nqb, float scale)
+                   __bf16* __restrict__ dQ, int N, int BH, int nqb, int H, int Hkv, float scale)
 {
     constexpr int BR = NW * 32, BC = 64;
     using TK = Tile<D, BC>;
@@ -387,6 +400,7 @@ attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int qb = CAUSAL ? nqb - 1 - t : t;  // longest first under the mask
     const int q0 = qb * BR, qw0 = q0 + wave * 32, q = qw0 + j;
     const size_t base = (size_t)bh * N * D;
+    const size_t kvbase = ((size_t)(bh / H) * Hkv + (bh % H) / (H / Hkv)) * N * D;
     const uint32_t slice_b = (uint32_t)N * D * 2;
     const float c = scale * kLog2e;
 
@@ -414,8 +428,8 @@ attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     auto issue = [&](auto bc, int kt) {
         const int kv0 = kt * BC;
         const uint32_t left = (uint32_t)(N - kv0) * D * 2;
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base + (size_t)kv0 * D, left);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base + (size_t)kv0 * D, left);
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kvbase + (size_t)kv0 * D, left);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kvbase + (size_t)kv0 * D, left);
 #pragma unroll
         for (int u = 0; u < LPW; ++u) {
             const int i = wave + u * NW;
@@ -496,31 +510,34 @@ constexpr long long kCUs = 256;
 
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* g,
-                       const float* Lc, const float* Dl, void* dK, void* dV, int BH, int N,
-                       float scale, hipStream_t stream)
+                       const float* Lc, const float* Dl, void* dK, void* dV, int B, int H,
+                       int Hkv, int N, float scale, hipStream_t stream)
 {
+    const int BHkv = B * Hkv;
     auto go = [&](auto nwc) {
         constexpr int NW = decltype(nwc)::value;
         const int nkb = (N + NW * 32 - 1) / (NW * 32);
-        attn_bwd_dkdv_kernel<D, NW, CAUSAL><<<dim3((unsigned)(nkb * BH)), dim3(NW * 64), 0, stream>>>(
-            q, k, v, g, Lc, Dl, static_cast<__bf16*>(dK), static_cast<__bf16*>(dV), N, BH, scale);
+        attn_bwd_dkdv_kernel<D, NW, CAUSAL><<<dim3((unsigned)(nkb * BHkv)), dim3(NW * 64), 0, stream>>>(
+            q, k, v, g, Lc, Dl, static_cast<__bf16*>(dK), static_cast<__bf16*>(dV), N, BHkv, H, Hkv,
+            scale);
         return hipGetLastError();
     };
-    if ((long long)((N + 255) / 256) * BH >= kCUs) return go(std::integral_constant<int, 8>{});
-    if ((long long)((N + 127) / 128) * BH >= kCUs) return go(std::integral_constant<int, 4>{});
+    if ((long long)((N + 255) / 256) * BHkv >= kCUs) return go(std::integral_constant<int, 8>{});
+    if ((long long)((N + 127) / 128) * BHkv >= kCUs) return go(std::integral_constant<int, 4>{});
     return go(std::integral_constant<int, 2>{});
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_dq(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* g,
-                     const float* Lc, const float* Dl, void* dQ, int BH, int N, float scale,
-                     hipStream_t stream)
+                     const float* Lc, const float* Dl, void* dQ, int B, int H, int Hkv, int N,
+                     float scale, hipStream_t stream)
 {
+    const int BH = B * H;
     auto go = [&](auto nwc) {
         constexpr int NW = decltype(nwc)::value;
         const int nqb = (N + NW * 32 - 1) / (NW * 32);
         attn_bwd_dq_kernel<D, NW, CAUSAL><<<dim3((unsigned)(nqb * BH)), dim3(NW * 64), 0, stream>>>(
-            q, k, v, g, Lc, Dl, static_cast<__bf16*>(dQ), N, BH, nqb, scale);
+            q, k, v, g, Lc, Dl, static_cast<__bf16*>(dQ), N, BH, nqb, H, Hkv, scale);
         return hipGetLastError();
     };
     if ((long long)((N + 255) / 256) * BH >= kCUs) return go(std::integral_constant<int, 8>{});
@@ -530,9 +547,10 @@ hipError_t launch_dq(const __bf16* q, const __bf16* k, const __bf16* v, const __
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                      const float* lse, void* dQ, void* dK, void* dV, int BH, int N, float scale,
-                      float* Dl, float* Lc, hipStream_t stream)
+                      const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
+                      float scale, float* Dl, float* Lc, hipStream_t stream)
 {
+    const int BH = B * H;
     const __bf16* q = static_cast<const __bf16*>(Q);
     const __bf16* k = static_cast<const __bf16*>(K);
     const __bf16* v = static_cast<const __bf16*>(V);
@@ -546,24 +564,24 @@ hipError_t launch_bwd(const void* Q, const void* K, const void* V, const void* O
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (const hipError_t e = launch_dkdv<D, CAUSAL>(q, k, v, g, Lc, Dl, dK, dV, BH, N, scale, stream);
+    if (const hipError_t e = launch_dkdv<D, CAUSAL>(q, k, v, g, Lc, Dl, dK, dV, B, H, Hkv, N, scale, stream);
         e != hipSuccess)
         return e;
-    return launch_dq<D, CAUSAL>(q, k, v, g, Lc, Dl, dQ, BH, N, scale, stream);
+    return launch_dq<D, CAUSAL>(q, k, v, g, Lc, Dl, dQ, B, H, Hkv, N, scale, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* lse, void* dQ, void* dK, void* dV,
-                                int BH, int N, int d, float scale, bool causal, float* Dl,
-                                float* Lc, hipStream_t stream)
+                                int B, int H, int Hkv, int N, int d, float scale, bool causal,
+                                float* Dl, float* Lc, hipStream_t stream)
 {
     if (d == 64)
-        return causal ? launch_bwd<64, true>(Q, K, V, O, dO, lse, dQ, dK, dV, BH, N, scale, Dl, Lc, stream)
-                      : launch_bwd<64, false>(Q, K, V, O, dO, lse, dQ, dK, dV, BH, N, scale, Dl, Lc, stream);
-    return causal ? launch_bwd<128, true>(Q, K, V, O, dO, lse, dQ, dK, dV, BH, N, scale, Dl, Lc, stream)
-                  : launch_bwd<128, false>(Q, K, V, O, dO, lse, dQ, dK, dV, BH, N, scale, Dl, Lc, stream);
+        return causal ? launch_bwd<64, true>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, Dl, Lc, stream)
+                      : launch_bwd<64, false>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, Dl, Lc, stream);
+    return causal ? launch_bwd<128, true>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, Dl, Lc, stream)
+                  : launch_bwd<128, false>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, Dl, Lc, stream);
 }
 
 }  // namespace osm

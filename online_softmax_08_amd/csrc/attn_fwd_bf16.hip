@@ -101,25 +101,30 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, lds_void_t*
 // Where the (batch, head) slice of a workgroup lives: dense tensors
 // [B*H][N][D] (lse [B*H][N]), or packed variable-length sequences
 // [H][total][D] (lse [H][total]) whose batch b holds rows cu[b] .. cu[b+1]-1
-// of every head.  Packed lengths are clamped to [0, Nmax] and to the packed
-// extent, so a malformed cu cannot move an access outside the tensors.
+// of every head.  K and V have Hkv heads (Hkv divides H; query head h reads
+// key/value head h / (H / Hkv)).  Packed lengths are clamped to [0, Nmax]
+// and to the packed extent, so a malformed cu cannot move an access outside
+// the tensors.
 struct Slice {
-    size_t base;   // element offset of row 0 of the slice in Q, K, V, O
-    size_t lbase;  // element offset of row 0 in lse
-    int n;         // rows (queries = keys) of the slice
+    size_t base;    // element offset of row 0 of the slice in Q and O
+    size_t kvbase;  // element offset of row 0 of its key/value slice in K and V
+    size_t lbase;   // element offset of row 0 in lse
+    int n;          // rows (queries = keys) of the slice
 };
 
 template <int D, bool VARLEN>
-__device__ __forceinline__ Slice slice_of(int bh, int Nmax, int H, const int* cu, int total)
+__device__ __forceinline__ Slice slice_of(int bh, int Nmax, int H, int Hkv, const int* cu, int total)
 {
+    const int b = bh / H, hh = bh - b * H;
+    const int hkv = hh / (H / Hkv);
     if constexpr (!VARLEN) {
-        return {(size_t)bh * Nmax * D, (size_t)bh * Nmax, Nmax};
+        const size_t kvbh = (size_t)b * Hkv + hkv;
+        return {(size_t)bh * Nmax * D, kvbh * Nmax * D, (size_t)bh * Nmax, Nmax};
     } else {
-        const int b = bh / H, hh = bh - b * H;
         const int start = min(max(__builtin_amdgcn_readfirstlane(cu[b]), 0), total);
         const int end = min(max(__builtin_amdgcn_readfirstlane(cu[b + 1]), start), total);
         const size_t row0 = (size_t)hh * total + start;
-        return {row0 * D, row0, min(end - start, Nmax)};
+        return {row0 * D, ((size_t)hkv * total + start) * D, row0, min(end - start, Nmax)};
     }
 }
 
@@ -154,7 +159,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, __bf16* __restrict__ O,
                      float* __restrict__ lse, int Nmax, int BH, int nqt, float scale,
                      float* __restrict__ opart, float* __restrict__ lpart, int nsplit,
-                     const int* __restrict__ cu, int H, int total)
+                     const int* __restrict__ cu, int H, int Hkv, int total)
 {
     static_assert(!(SPLIT && VARLEN), "split-KV runs on dense tensors");
     using C = Cfg<D, QT, NW, BC>;
@@ -185,7 +190,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
     const int qt = CAUSAL ? nqt - 1 - t : t;
     const int q0 = qt * C::BR;
-    const Slice sl = slice_of<D, VARLEN>(bh, Nmax, H, cu, total);
+    const Slice sl = slice_of<D, VARLEN>(bh, Nmax, H, Hkv, cu, total);
     const int N = sl.n;
     if (VARLEN && q0 >= N) return;  // query block past this sequence (whole workgroup)
     const size_t base = sl.base;
@@ -239,8 +244,8 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         const int row = p / C::VCPR, ch = min(p % C::VCPR, D / 8 - 1);
         vsrc[u] = (uint32_t)(row * D + ch * 8) * 2;
     }
-    const __bf16* Kb = K + base;
-    const __bf16* Vb = V + base;
+    const __bf16* Kb = K + sl.kvbase;
+    const __bf16* Vb = V + sl.kvbase;
     auto issue_k = [&](auto bufc, int kt) {
         const int kv0 = kt * BC;
         const uint32_t left = (uint32_t)(N - kv0) * D * 2;  // bytes of this slice from kv0 on
@@ -502,7 +507,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                         const __bf16* __restrict__ V, __bf16* __restrict__ O,
                         float* __restrict__ lse, int Nmax, int BH, int nqt, float scale,
-                        const int* __restrict__ cu, int H, int total)
+                        const int* __restrict__ cu, int H, int Hkv, int total)
 {
     constexpr int NW = 8, BC = 64;
     using C = Cfg<D, 1, NW, BC>;
@@ -520,7 +525,7 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     const int t = blockIdx.x / BH, bh = blockIdx.x - t * BH;
     const int qt = CAUSAL ? nqt - 1 - t : t;
     const int q0 = qt * C::BR;
-    const Slice sl = slice_of<D, VARLEN>(bh, Nmax, H, cu, total);
+    const Slice sl = slice_of<D, VARLEN>(bh, Nmax, H, Hkv, cu, total);
     const int N = sl.n;
     if (VARLEN && q0 >= N) return;  // query block past this sequence (whole workgroup)
     const size_t base = sl.base;
@@ -580,7 +585,7 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     auto load_part = [&](auto bufc, int kt) {
         const int kv0 = kt * BC;
         const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc((late ? V : K) + base + (size_t)kv0 * D, (uint32_t)(N - kv0) * D * 2);
+            make_rsrc((late ? V : K) + sl.kvbase + (size_t)kv0 * D, (uint32_t)(N - kv0) * D * 2);
         char* dst = late ? vbuf(bufc) : kbuf(bufc);
 #pragma unroll
         for (int u = 0; u < LPW; ++u) {
@@ -774,27 +779,29 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 // sequence; H and total describe the packed layout (unused when dense).
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_pp(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
-                     int N, float scale, const int* cu, int H, int total, hipStream_t stream)
+                     int N, float scale, const int* cu, int H, int Hkv, int total,
+                     hipStream_t stream)
 {
     constexpr int BR = 256;
     const int nqt = (N + BR - 1) / BR;
     const dim3 grid((unsigned)(nqt * BH)), block(512);
     attn_fwd_bf16_pp_kernel<D, CAUSAL, VARLEN><<<grid, block, 0, stream>>>(
         static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
-        static_cast<__bf16*>(O), lse, N, BH, nqt, scale, cu, H, total);
+        static_cast<__bf16*>(O), lse, N, BH, nqt, scale, cu, H, Hkv, total);
     return hipGetLastError();
 }
 
 template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL, bool VARLEN>
 hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
-                  int N, float scale, const int* cu, int H, int total, hipStream_t stream)
+                  int N, float scale, const int* cu, int H, int Hkv, int total,
+                  hipStream_t stream)
 {
     using C = Cfg<D, QT, NW, BC>;
     const int nqt = (N + C::BR - 1) / C::BR;
     const dim3 grid((unsigned)(nqt * BH)), block(C::T);
     attn_fwd_bf16_kernel<D, QT, NW, WPE, BC, CAUSAL, false, VARLEN><<<grid, block, 0, stream>>>(
         static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
-        static_cast<__bf16*>(O), lse, N, BH, nqt, scale, nullptr, nullptr, 1, cu, H, total);
+        static_cast<__bf16*>(O), lse, N, BH, nqt, scale, nullptr, nullptr, 1, cu, H, Hkv, total);
     return hipGetLastError();
 }
 
@@ -806,19 +813,19 @@ hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* l
 // plain kernel is kept.
 template <int D, bool CAUSAL, bool VARLEN = false>
 hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
-                    int N, float scale, hipStream_t stream, const int* cu = nullptr, int H = 1,
-                    int total = 0)
+                    int N, float scale, hipStream_t stream, int H = 1, int Hkv = 1,
+                    const int* cu = nullptr, int total = 0)
 {
     constexpr long long kCUs = 256;
     if ((long long)((N + 255) / 256) * BH >= kCUs) {
         if constexpr (CAUSAL)
-            return launch_pp<D, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, total, stream);
+            return launch_pp<D, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
         else
-            return launch<D, 1, 8, 2, 64, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, total, stream);
+            return launch<D, 1, 8, 2, 64, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
     }
     if ((long long)((N + 127) / 128) * BH >= kCUs)
-        return launch<D, 1, 4, 2, 64, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, total, stream);
-    return launch<D, 1, 2, 2, 64, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, total, stream);
+        return launch<D, 1, 4, 2, 64, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
+    return launch<D, 1, 2, 2, 64, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
 }
 
 // Merge of split partials, one row per D / 4 lanes (four fp32 columns per
@@ -868,7 +875,7 @@ attn_combine_kernel(const float* __restrict__ opart, const float* __restrict__ l
 // each, then the merge.
 template <int D, bool CAUSAL>
 hipError_t launch_split(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
-                        int N, float scale, int nsplit, float* opart, float* lpart,
+                        int N, float scale, int nsplit, float* opart, float* lpart, int H, int Hkv,
                         hipStream_t stream)
 {
     using C = Cfg<D, 1, 8, 64>;
@@ -877,7 +884,7 @@ hipError_t launch_split(const void* Q, const void* K, const void* V, void* O, fl
         <<<dim3((unsigned)(nqt * nsplit * BH)), dim3(C::T), 0, stream>>>(
             static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K),
             static_cast<const __bf16*>(V), nullptr, nullptr, N, BH, nqt, scale, opart, lpart,
-            nsplit, nullptr, 1, 0);
+            nsplit, nullptr, H, Hkv, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_attn_combine(opart, lpart, O, lse, nsplit, (long long)BH * N, D, stream);
@@ -921,38 +928,41 @@ int attn_splitkv_auto(int BH, int N, int d, bool causal)
 }
 
 hipError_t launch_attn_fwd_bf16_split(const void* Q, const void* K, const void* V, void* O,
-                                      float* lse, int BH, int N, int d, float scale, bool causal,
-                                      int nsplit, float* opart, float* lpart, hipStream_t stream)
+                                      float* lse, int B, int H, int Hkv, int N, int d, float scale,
+                                      bool causal, int nsplit, float* opart, float* lpart,
+                                      hipStream_t stream)
 {
+    const int BH = B * H;
     if (d == 64)
-        return causal ? launch_split<64, true>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, stream)
-                      : launch_split<64, false>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, stream);
-    return causal ? launch_split<128, true>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, stream)
-                  : launch_split<128, false>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, stream);
+        return causal ? launch_split<64, true>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, H, Hkv, stream)
+                      : launch_split<64, false>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, H, Hkv, stream);
+    return causal ? launch_split<128, true>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, H, Hkv, stream)
+                  : launch_split<128, false>(Q, K, V, O, lse, BH, N, scale, nsplit, opart, lpart, H, Hkv, stream);
 }
 
 hipError_t launch_attn_fwd_bf16_varlen(const void* Q, const void* K, const void* V, void* O,
-                                       float* lse, const int* cu, int B, int H, int total,
+                                       float* lse, const int* cu, int B, int H, int Hkv, int total,
                                        int max_seqlen, int d, float scale, bool causal,
                                        hipStream_t stream)
 {
     const int BH = B * H;
     if (d == 64)
-        return causal ? dispatch<64, true, true>(Q, K, V, O, lse, BH, max_seqlen, scale, stream, cu, H, total)
-                      : dispatch<64, false, true>(Q, K, V, O, lse, BH, max_seqlen, scale, stream, cu, H, total);
-    return causal ? dispatch<128, true, true>(Q, K, V, O, lse, BH, max_seqlen, scale, stream, cu, H, total)
-                  : dispatch<128, false, true>(Q, K, V, O, lse, BH, max_seqlen, scale, stream, cu, H, total);
+        return causal ? dispatch<64, true, true>(Q, K, V, O, lse, BH, max_seqlen, scale, stream, H, Hkv, cu, total)
+                      : dispatch<64, false, true>(Q, K, V, O, lse, BH, max_seqlen, scale, stream, H, Hkv, cu, total);
+    return causal ? dispatch<128, true, true>(Q, K, V, O, lse, BH, max_seqlen, scale, stream, H, Hkv, cu, total)
+                  : dispatch<128, false, true>(Q, K, V, O, lse, BH, max_seqlen, scale, stream, H, Hkv, cu, total);
 }
 
 hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, void* O,
-                                float* lse, int BH, int N, int d, float scale, bool causal,
-                                hipStream_t stream)
+                                float* lse, int B, int H, int Hkv, int N, int d, float scale,
+                                bool causal, hipStream_t stream)
 {
+    const int BH = B * H;
     if (d == 64)
-        return causal ? dispatch<64, true>(Q, K, V, O, lse, BH, N, scale, stream)
-                      : dispatch<64, false>(Q, K, V, O, lse, BH, N, scale, stream);
-    return causal ? dispatch<128, true>(Q, K, V, O, lse, BH, N, scale, stream)
-                  : dispatch<128, false>(Q, K, V, O, lse, BH, N, scale, stream);
+        return causal ? dispatch<64, true>(Q, K, V, O, lse, BH, N, scale, stream, H, Hkv)
+                      : dispatch<64, false>(Q, K, V, O, lse, BH, N, scale, stream, H, Hkv);
+    return causal ? dispatch<128, true>(Q, K, V, O, lse, BH, N, scale, stream, H, Hkv)
+                  : dispatch<128, false>(Q, K, V, O, lse, BH, N, scale, stream, H, Hkv);
 }
 
 }  // namespace osm

@@ -13,34 +13,37 @@ constexpr int kSoftmaxBlockMaxN = 32768;
 
 hipError_t launch_row_softmax(const float* x, float* y, int B, int N, hipStream_t stream);
 
-// Q, K, V, O: [B*H][N][d] row-major; lse: [B*H][N].  d is 64 or 128.
+// Q, O: [B*H][N][d] row-major; K, V: [B*Hkv][N][d] (Hkv divides H; query
+// head h reads key/value head h / (H / Hkv)); lse: [B*H][N].  d is 64 or 128.
 hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, void* O,
-                                float* lse, int BH, int N, int d, float scale, bool causal,
-                                hipStream_t stream);
+                                float* lse, int B, int H, int Hkv, int N, int d, float scale,
+                                bool causal, hipStream_t stream);
 // Packed variable-length sequences: Q, K, V, O [H][total][d], lse [H][total],
 // cu: device int32 [B + 1] row offsets, sequences no longer than max_seqlen.
 hipError_t launch_attn_fwd_bf16_varlen(const void* Q, const void* K, const void* V, void* O,
-                                       float* lse, const int* cu, int B, int H, int total,
+                                       float* lse, const int* cu, int B, int H, int Hkv, int total,
                                        int max_seqlen, int d, float scale, bool causal,
                                        hipStream_t stream);
 // Split-KV forward.  opart: fp32 [nsplit][B*H][N][d], lpart: fp32
 // [nsplit][B*H][N] (workspace); 1 <= nsplit <= kMaxSplits.
 constexpr int kMaxSplits = 64;
 hipError_t launch_attn_fwd_bf16_split(const void* Q, const void* K, const void* V, void* O,
-                                      float* lse, int BH, int N, int d, float scale, bool causal,
-                                      int nsplit, float* opart, float* lpart, hipStream_t stream);
+                                      float* lse, int B, int H, int Hkv, int N, int d, float scale,
+                                      bool causal, int nsplit, float* opart, float* lpart,
+                                      hipStream_t stream);
 // The number of key ranges the split-KV forward picks when asked to choose.
 int attn_splitkv_auto(int BH, int N, int d, bool causal);
 // Merge of S partials (opart [S][rows][d] fp32, lpart [S][rows]) into O (bf16
 // [rows][d]) and lse ([rows]).
 hipError_t launch_attn_combine(const float* opart, const float* lpart, void* O, float* lse, int S,
                                long long rows, int d, hipStream_t stream);
-// Backward: dQ, dK, dV (bf16 [B*H][N][d]) from Q, K, V, O, dO (bf16) and the
-// forward's lse; Dl and Lc are fp32 [B*H][N] workspace rows.
+// Backward: dQ (bf16 [B*H][N][d]), dK, dV (bf16 [B*Hkv][N][d]) from Q, O, dO
+// ([B*H][N][d]), K, V ([B*Hkv][N][d]) and the forward's lse; Dl and Lc are
+// fp32 [B*H][N] workspace rows.
 hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* lse, void* dQ, void* dK, void* dV,
-                                int BH, int N, int d, float scale, bool causal, float* Dl,
-                                float* Lc, hipStream_t stream);
+                                int B, int H, int Hkv, int N, int d, float scale, bool causal,
+                                float* Dl, float* Lc, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const float* Q, const float* K, const float* V, float* O,
                                float* lse, int BH, int N, int d, float scale, bool causal,
                                hipStream_t stream);

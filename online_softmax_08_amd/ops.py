@@ -13,10 +13,15 @@ def _stream_handle(device: torch.device) -> int:
 
 
 def _check_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+    """q [B, H, N, d]; k, v [B, Hkv, N, d] with Hkv dividing H (grouped-query
+    attention; Hkv = H is plain multi-head attention)."""
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors")
-    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, H, N, d] and k, v one [B, Hkv, N, d] shape")
+    B, H, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d or k.shape[1] < 1 or H % k.shape[1]:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hkv dividing q's H")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("q, k, v must all be bfloat16 or all float32")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
@@ -28,11 +33,16 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
               lse: torch.Tensor | None = None):
     """O = softmax(scale q k^T) v per (batch, head), and the row logsumexp.
 
-    q, k, v: contiguous [B, H, N, d] bf16 (fp32 accumulation) or fp32.
-    Returns (O with q's dtype, lse fp32 [B, H, N]).  scale defaults to 1/sqrt(d).
+    q: contiguous [B, H, N, d], k, v: [B, Hkv, N, d] (Hkv dividing H; query
+    head h reads key/value head h // (H // Hkv)), bf16 (fp32 accumulation) or
+    fp32 (Hkv = H only).  Returns (O with q's dtype, lse fp32 [B, H, N]).
+    scale defaults to 1/sqrt(d).
     """
     _check_attn(q, k, v)
     B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if q.dtype == torch.float32 and Hkv != H:
+        raise ValueError("the fp32 path takes as many key/value heads as query heads")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
@@ -42,10 +52,14 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
         raise ValueError("out must be a contiguous tensor like q")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
-    fn = _abi.attn_fwd if q.dtype == torch.bfloat16 else _abi.attn_fwd_f32
     with torch.cuda.device(q.device):
-        fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-           B, H, N, d, scale, causal, _stream_handle(q.device))
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+        if q.dtype == torch.float32:
+            _abi.attn_fwd_f32(*args, B, H, N, d, scale, causal, _stream_handle(q.device))
+        elif Hkv == H:
+            _abi.attn_fwd(*args, B, H, N, d, scale, causal, _stream_handle(q.device))
+        else:
+            _abi.attn_fwd_gqa(*args, B, H, Hkv, N, d, scale, causal, _stream_handle(q.device))
     return out, lse
 
 
@@ -54,16 +68,17 @@ def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      scale: float | None = None):
     """Attention over packed variable-length sequences.
 
-    q, k, v: contiguous bf16 [H, total, d] (every head's rows of all sequences
-    end to end); cu_seqlens: int32 GPU tensor [B + 1] of row offsets;
+    q: contiguous bf16 [H, total, d] (every head's rows of all sequences end
+    to end), k, v: [Hkv, total, d]; cu_seqlens: int32 GPU tensor [B + 1] of row offsets;
     max_seqlen: an upper bound of the lengths.  Returns (O bf16 [H, total, d],
     lse fp32 [H, total]).
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous bfloat16 [H, total, d] GPU tensor")
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [H, total, d] shape")
+            raise ValueError(f"{name} must be a contiguous bfloat16 [heads, total, d] GPU tensor")
+    if (k.shape != v.shape or k.shape[1:] != q.shape[1:] or k.shape[0] < 1
+            or q.shape[0] % k.shape[0]):
+        raise ValueError("q must be [H, total, d] and k, v [Hkv, total, d], Hkv dividing H")
     if (not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
             or not cu_seqlens.is_contiguous() or cu_seqlens.device != q.device):
         raise ValueError("cu_seqlens must be a contiguous int32 [B + 1] tensor on q's device")
@@ -74,8 +89,8 @@ def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
     with torch.cuda.device(q.device):
         _abi.attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                             lse.data_ptr(), cu_seqlens.data_ptr(), max(B, 0), H, total,
-                             int(max_seqlen), d, scale, causal, _stream_handle(q.device))
+                             lse.data_ptr(), cu_seqlens.data_ptr(), max(B, 0), H, k.shape[0],
+                             total, int(max_seqlen), d, scale, causal, _stream_handle(q.device))
     return out, lse
 
 
@@ -102,7 +117,7 @@ def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal:
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     with torch.cuda.device(q.device):
         _abi.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                              lse.data_ptr(), B, H, N, d, scale, causal, ns,
+                              lse.data_ptr(), B, H, k.shape[1], N, d, scale, causal, ns,
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                               _stream_handle(q.device))
     return out, lse
@@ -137,8 +152,8 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
                        scale: float | None = None, workspace: torch.Tensor | None = None):
     """Gradients (dq, dk, dv) of sum(grad_out * out) for out, lse = attention(q, k, v).
 
-    All of q, k, v, out, grad_out: contiguous bf16 [B, H, N, d]; lse: fp32
-    [B, H, N] from the same forward call.  ``workspace`` (optional) is a device
+    q, out, grad_out: contiguous bf16 [B, H, N, d]; k, v: [B, Hkv, N, d]; lse:
+    fp32 [B, H, N] from the same forward call.  dk, dv have k's shape.  ``workspace`` (optional) is a device
     uint8 tensor of at least attn_bwd_workspace_bytes(B, H, N) bytes.
     """
     _check_attn(q, k, v)
@@ -154,11 +169,11 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
     ws_bytes = _abi.attn_bwd_workspace_bytes(B, H, N)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     with torch.cuda.device(q.device):
         _abi.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                       grad_out.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                      dv.data_ptr(), B, H, N, d, scale, causal, workspace.data_ptr(),
+                      dv.data_ptr(), B, H, k.shape[1], N, d, scale, causal, workspace.data_ptr(),
                       workspace.numel() * workspace.element_size(), _stream_handle(q.device))
     return dq, dk, dv
 

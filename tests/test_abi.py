@@ -23,7 +23,8 @@ def abi():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_varlen",
+    assert _declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_gqa",
+                                            "attn_fwd_varlen",
                                             "attn_fwd_splitkv_plan",
                                             "attn_fwd_splitkv", "attn_combine",
                                             "attn_bwd_workspace_bytes", "attn_bwd", "row_softmax",
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol(abi):
 
 
 def test_status_strings(abi):
-    for st in range(0, 11):
+    for st in range(0, 12):
         assert abi.osm_status_str(st) and abi.osm_status_str(st) != "unknown status"
     assert abi.osm_status_str(99) == "unknown status"
 
@@ -134,15 +135,15 @@ def test_splitkv_plan(abi):
 
 
 def _splitkv_status(abi, nsplit=2, ws=6 * FAKE, ws_bytes=None, **kw):
-    args = dict(Q=FAKE, K=2 * FAKE, V=3 * FAKE, O=4 * FAKE, lse=5 * FAKE, B=1, H=1, N=16, d=64,
-                scale=0.125, causal=0)
+    args = dict(Q=FAKE, K=2 * FAKE, V=3 * FAKE, O=4 * FAKE, lse=5 * FAKE, B=1, H=1, Hkv=1, N=16,
+                d=64, scale=0.125, causal=0)
     args.update(kw)
     if ws_bytes is None:
         ws_bytes = 1 << 40  # ample; the overlap checks use the bytes actually needed
     with pytest.raises(abi.OsmError) as e:
         abi.attn_fwd_splitkv(args["Q"], args["K"], args["V"], args["O"], args["lse"], args["B"],
-                             args["H"], args["N"], args["d"], args["scale"], args["causal"],
-                             nsplit, ws, ws_bytes)
+                             args["H"], args["Hkv"], args["N"], args["d"], args["scale"],
+                             args["causal"], nsplit, ws, ws_bytes)
     return e.value.status
 
 
@@ -165,7 +166,8 @@ def test_splitkv_validation(abi):
     assert _splitkv_status(abi, N=1 << 23, d=128, ws=6 << 40, ws_bytes=1 << 45,
                            **far) == abi.OSM_ERR_SIZE
     # Empty problems are a no-op with any pointers.
-    abi.attn_fwd_splitkv(0, 0, 0, 0, 0, 0, 4, 128, 64, 0.125, 1, 4, 0, 0)
+    abi.attn_fwd_splitkv(0, 0, 0, 0, 0, 0, 4, 4, 128, 64, 0.125, 1, 4, 0, 0)
+    assert _splitkv_status(abi, H=4, Hkv=3) == abi.OSM_ERR_HEADS
 
 
 def test_combine_validation(abi):
@@ -193,12 +195,12 @@ def test_bwd_workspace_and_validation(abi):
                                                       "dV", "ws"))}
 
     def status(ws_bytes=ws_need, **kw):
-        a = dict(ptr, B=1, H=1, N=16, d=64, scale=0.125, causal=0)
+        a = dict(ptr, B=1, H=1, Hkv=1, N=16, d=64, scale=0.125, causal=0)
         a.update(kw)
         with pytest.raises(abi.OsmError) as e:
             abi.attn_bwd(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["lse"], a["dQ"], a["dK"],
-                         a["dV"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
-                         a["ws"], ws_bytes)
+                         a["dV"], a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"],
+                         a["causal"], a["ws"], ws_bytes)
         return e.value.status
     assert status(d=96) == abi.OSM_ERR_HEAD_DIM
     assert status(scale=0.0) == abi.OSM_ERR_SCALE
@@ -212,18 +214,20 @@ def test_bwd_workspace_and_validation(abi):
     assert status(dV=ptr["dK"] + 64) == abi.OSM_ERR_ALIAS    # dV runs into dK
     assert status(dK=ptr["lse"]) == abi.OSM_ERR_ALIAS        # dK is lse
     assert status(ws=ptr["dO"] + 32) == abi.OSM_ERR_ALIAS    # workspace inside dO
-    abi.attn_bwd(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 2, 16, 64, 0.125, 1, 0, 0)  # empty: no-op
+    assert status(H=2, Hkv=0) == abi.OSM_ERR_HEADS
+    assert status(H=2, Hkv=4) == abi.OSM_ERR_HEADS
+    abi.attn_bwd(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 2, 2, 16, 64, 0.125, 1, 0, 0)  # empty: no-op
 
 
 def test_varlen_validation(abi):
     ptr = {n: (i + 1) * FAKE for i, n in enumerate(("Q", "K", "V", "O", "lse", "cu"))}
 
     def status(**kw):
-        a = dict(ptr, B=2, H=2, total=100, maxs=64, d=64, scale=0.125, causal=0)
+        a = dict(ptr, B=2, H=2, Hkv=2, total=100, maxs=64, d=64, scale=0.125, causal=0)
         a.update(kw)
         with pytest.raises(abi.OsmError) as e:
             abi.attn_fwd_varlen(a["Q"], a["K"], a["V"], a["O"], a["lse"], a["cu"], a["B"], a["H"],
-                                a["total"], a["maxs"], a["d"], a["scale"], a["causal"])
+                                a["Hkv"], a["total"], a["maxs"], a["d"], a["scale"], a["causal"])
         return e.value.status
     assert status(B=-1) == abi.OSM_ERR_SIZE
     assert status(total=-5) == abi.OSM_ERR_SIZE
@@ -239,4 +243,23 @@ def test_varlen_validation(abi):
     for empty in (dict(B=0), dict(H=0), dict(total=0), dict(maxs=0)):
         a = dict(B=2, H=2, total=100, maxs=64)
         a.update(empty)
-        abi.attn_fwd_varlen(0, 0, 0, 0, 0, 0, a["B"], a["H"], a["total"], a["maxs"], 64, 0.125, 1)
+        abi.attn_fwd_varlen(0, 0, 0, 0, 0, 0, a["B"], a["H"], a["H"], a["total"], a["maxs"], 64,
+                            0.125, 1)
+    assert status(Hkv=3) == abi.OSM_ERR_HEADS
+
+
+def test_gqa_validation(abi):
+    def status(H=4, Hkv=2, **kw):
+        a = dict(Q=FAKE, K=2 * FAKE, V=3 * FAKE, O=4 * FAKE, lse=5 * FAKE, B=1, N=16, d=64)
+        a.update(kw)
+        with pytest.raises(abi.OsmError) as e:
+            abi.attn_fwd_gqa(a["Q"], a["K"], a["V"], a["O"], a["lse"], a["B"], H, Hkv, a["N"],
+                             a["d"], 0.125, 0)
+        return e.value.status
+    assert status(Hkv=3) == abi.OSM_ERR_HEADS      # does not divide H
+    assert status(Hkv=0) == abi.OSM_ERR_HEADS
+    assert status(Hkv=8) == abi.OSM_ERR_HEADS      # more than H
+    assert status(d=32) == abi.OSM_ERR_HEAD_DIM
+    assert status(K=0) == abi.OSM_ERR_NULL
+    assert status(O=2 * FAKE + 512) == abi.OSM_ERR_ALIAS  # O inside K
+    abi.attn_fwd_gqa(0, 0, 0, 0, 0, 0, 4, 2, 16, 64, 0.125, 0)  # empty: no-op

@@ -246,6 +246,22 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
              float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_bwd_varlen -- attn_bwd for attn_fwd_varlen: packed sequences.
+ *   Q, O, dO, dQ : bf16 [H][total][d];  K, V, dK, dV : bf16 [Hkv][total][d];
+ *   lse : fp32 [H][total]; cu_seqlens, B, H, Hkv, total, max_seqlen, d,
+ *   scale, causal : as for the attn_fwd_varlen call that produced O and lse
+ *   workspace : at least attn_bwd_workspace_bytes(1, H, total) bytes,
+ *              16-byte aligned, caller-owned
+ * Gradients, rounding, alignment (cu_seqlens 4 bytes) and overlap rules as
+ * for attn_bwd; a sequence's gradients depend on its own rows only.
+ * Returns an osm_status.
+ */
+int attn_bwd_varlen(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                    const float* lse, void* dQ, void* dK, void* dV, const int* cu_seqlens,
+                    int B, int H, int Hkv, int total, int max_seqlen, int d, float scale,
+                    int causal, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * row_softmax -- stable softmax of each fp32 row.
  *   x : const fp32 [B][N];  y : fp32 [B][N]
  *   y may be exactly x (in place); any other overlap is OSM_ERR_ALIAS.

@@ -49,11 +49,14 @@ _lib.attn_bwd_workspace_bytes.restype = _sz
 _lib.attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                           _i, _vp, _sz, _vp]
 _lib.attn_bwd.restype = _i
+_lib.attn_bwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                                 _i, _i, _i, _f, _i, _vp, _sz, _vp]
+_lib.attn_bwd_varlen.restype = _i
 _lib.osm_status_str.argtypes = [_i]
 _lib.osm_status_str.restype = ctypes.c_char_p
 
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_gqa", "attn_fwd_varlen", "attn_fwd_splitkv_plan", "attn_fwd_splitkv",
-           "attn_combine", "attn_bwd_workspace_bytes", "attn_bwd", "row_softmax",
+           "attn_combine", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_varlen", "row_softmax",
            "osm_status_str")
 
 OSM_OK = 0
@@ -156,3 +159,12 @@ def attn_fwd_gqa(Q: int, K: int, V: int, O: int, lse: int, B: int, H: int, Hkv: 
                  d: int, scale: float, causal: bool, stream: int = 0) -> None:
     """bf16 attention with Hkv key/value heads; see include/osm.h."""
     _call("attn_fwd_gqa", Q, K, V, O, lse, B, H, Hkv, N, d, scale, int(bool(causal)), stream)
+
+
+def attn_bwd_varlen(Q: int, K: int, V: int, O: int, dO: int, lse: int, dQ: int, dK: int, dV: int,
+                    cu_seqlens: int, B: int, H: int, Hkv: int, total: int, max_seqlen: int, d: int,
+                    scale: float, causal: bool, workspace: int, workspace_bytes: int,
+                    stream: int = 0) -> None:
+    """Backward pass of attn_fwd_varlen; see include/osm.h."""
+    _call("attn_bwd_varlen", Q, K, V, O, dO, lse, dQ, dK, dV, cu_seqlens, B, H, Hkv, total,
+          max_seqlen, d, scale, int(bool(causal)), workspace, workspace_bytes, stream)

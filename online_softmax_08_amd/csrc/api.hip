@@ -298,6 +298,50 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
                                             causal != 0, Dl, Lc, static_cast<hipStream_t>(stream)));
 }
 
+int attn_bwd_varlen(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                    const float* lse, void* dQ, void* dK, void* dV, const int* cu_seqlens, int B,
+                    int H, int Hkv, int total, int max_seqlen, int d, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (B < 0 || H < 0 || total < 0 || max_seqlen < 0) return OSM_ERR_SIZE;
+    if (d != 64 && d != 128) return OSM_ERR_HEAD_DIM;
+    if (!(std::isfinite(scale) && scale > 0.f)) return OSM_ERR_SCALE;
+    if (B == 0 || H == 0 || total == 0 || max_seqlen == 0) return OSM_OK;
+    int st = check_attn_shape(B, H, max_seqlen, d, scale, 2);
+    if (st != OSM_OK) return st;
+    if ((st = check_heads(H, Hkv)) != OSM_OK) return st;
+    if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || !cu_seqlens || !workspace)
+        return OSM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+        !aligned(dO, 16) || !aligned(lse, 4) || !aligned(dQ, 16) || !aligned(dK, 16) ||
+        !aligned(dV, 16) || !aligned(cu_seqlens, 4) || !aligned(workspace, 16))
+        return OSM_ERR_ALIGN;
+    const size_t need = attn_bwd_workspace_bytes(1, H, total);
+    if (workspace_bytes < need) return OSM_ERR_WORKSPACE;
+    const size_t tb = (size_t)H * total * d * 2, kvb = (size_t)Hkv * total * d * 2;
+    const size_t lb = (size_t)H * total * sizeof(float), cb = (size_t)(B + 1) * sizeof(int);
+    const void* outs[3] = {dQ, dK, dV};
+    const size_t out_bytes[3] = {tb, kvb, kvb};
+    const void* ins[7] = {Q, K, V, O, dO, lse, cu_seqlens};
+    const size_t in_bytes[7] = {tb, kvb, kvb, tb, tb, lb, cb};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = 0; b < 7; ++b)
+            if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return OSM_ERR_ALIAS;
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return OSM_ERR_ALIAS;
+        if (overlaps(outs[a], out_bytes[a], workspace, need)) return OSM_ERR_ALIAS;
+    }
+    for (int b = 0; b < 7; ++b)
+        if (overlaps(workspace, need, ins[b], in_bytes[b])) return OSM_ERR_ALIAS;
+    if ((st = check_device()) != OSM_OK) return st;
+    float* Dl = static_cast<float*>(workspace);
+    float* Lc = Dl + (size_t)H * total;
+    return finish(osm::launch_attn_bwd_bf16_varlen(Q, K, V, O, dO, lse, dQ, dK, dV, cu_seqlens, B,
+                                                   H, Hkv, total, max_seqlen, d, scale,
+                                                   causal != 0, Dl, Lc,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 const char* osm_status_str(int status)
 {
     switch (status) {

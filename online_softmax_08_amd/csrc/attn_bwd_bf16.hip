@@ -112,6 +112,33 @@ __device__ __forceinline__ bf16x8 cols_a(const char* tile, int row0, int col0, i
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Rows of one (sequence, head) slice.  Dense tensors [B][Hx][N][D] (Hx = H
+// for Q, O, dO and the row statistics, Hkv for K and V): the slice of
+// (b, hx) starts at row (b Hx + hx) N and has N rows.  Packed sequences
+// [Hx][total][D]: it starts at row hx total + cu[b] and has cu[b+1] - cu[b]
+// rows, clamped to [0, Nmax] and to the packed extent.
+template <bool VARLEN>
+struct Seq {
+    int b, start, n, total;
+    __device__ Seq(int b_, int Nmax, const int* cu, int total_) : b(b_), total(total_)
+    {
+        if constexpr (VARLEN) {
+            start = min(max(__builtin_amdgcn_readfirstlane(cu[b]), 0), total);
+            const int end = min(max(__builtin_amdgcn_readfirstlane(cu[b + 1]), start), total);
+            n = min(end - start, Nmax);
+        } else {
+            start = 0;
+            n = Nmax;
+        }
+    }
+    // First row of head hx of a tensor with Hx heads (dense stride: n rows).
+    __device__ size_t row0(int hx, int Hx) const
+    {
+        if constexpr (VARLEN) return (size_t)hx * total + start;
+        else return ((size_t)b * Hx + hx) * n;
+    }
+};
+
 // bf16 of registers 8 G .. 8 G + 7 of an accumulator.
 __device__ __forceinline__ bf16x8 half_bf16(const f32x16& v, int G)
 {
@@ -167,13 +194,13 @@ attn_bwd_delta_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ d
 }
 
 // ------------------------------------------------------------ dK and dV ----
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                      const float* __restrict__ Lc, const float* __restrict__ Dl,
-                     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int BHkv, int H,
-                     int Hkv, float scale)
+                     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int Nmax, int BHkv, int H,
+                     int Hkv, float scale, const int* __restrict__ cu, int total)
 {
     constexpr int BK = NW * 32, BQ = 64;
     using TQ = Tile<D, BQ>;
@@ -199,8 +226,11 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // (G = H / Hkv), whose contributions it sums.
     const int t = blockIdx.x / BHkv, kvbh = blockIdx.x - t * BHkv;
     const int k0 = t * BK, kw0 = k0 + wave * 32;
-    const int G = H / Hkv, qbh0 = (kvbh / Hkv) * H + (kvbh % Hkv) * G;
-    const size_t base = (size_t)kvbh * N * D;
+    const int G = H / Hkv, hkv = kvbh % Hkv;
+    const Seq<VARLEN> sq(kvbh / Hkv, Nmax, cu, total);
+    const int N = sq.n;
+    if (VARLEN && k0 >= N) return;  // key block past this sequence (whole workgroup)
+    const size_t base = sq.row0(hkv, Hkv) * D;
     const uint32_t slice_b = (uint32_t)N * D * 2;
     const float c = scale * kLog2e;
 
@@ -242,7 +272,7 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int qt0 = CAUSAL ? k0 / BQ : 0;     // first query tile with a visible pair
     const int nq = nqt - qt0;
     auto tile_of = [&](int it) { return qt0 + it % nq; };
-    auto qbase_of = [&](int it) { return (size_t)(qbh0 + it / nq) * N; };  // row 0 of the query head
+    auto qbase_of = [&](int it) { return sq.row0(hkv * G + it / nq, H); };  // row 0 of the query head
     auto issue = [&](auto bc, int it) {
         const int r0 = tile_of(it) * BQ;
         const size_t qb = (qbase_of(it) + r0) * D;
@@ -376,12 +406,13 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 }
 
 // ------------------------------------------------------------------- dQ ----
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                    const float* __restrict__ Lc, const float* __restrict__ Dl,
-                   __bf16* __restrict__ dQ, int N, int BH, int nqb, int H, int Hkv, float scale)
+                   __bf16* __restrict__ dQ, int Nmax, int BH, int nqb, int H, int Hkv,
+                   float scale, const int* __restrict__ cu, int total)
 {
     constexpr int BR = NW * 32, BC = 64;
     using TK = Tile<D, BC>;
@@ -399,8 +430,13 @@ attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int t = blockIdx.x / BH, bh = blockIdx.x - t * BH;
     const int qb = CAUSAL ? nqb - 1 - t : t;  // longest first under the mask
     const int q0 = qb * BR, qw0 = q0 + wave * 32, q = qw0 + j;
-    const size_t base = (size_t)bh * N * D;
-    const size_t kvbase = ((size_t)(bh / H) * Hkv + (bh % H) / (H / Hkv)) * N * D;
+    const int hq = bh % H;
+    const Seq<VARLEN> sq(bh / H, Nmax, cu, total);
+    const int N = sq.n;
+    if (VARLEN && q0 >= N) return;  // query block past this sequence (whole workgroup)
+    const size_t qrow0 = sq.row0(hq, H);
+    const size_t base = qrow0 * D;
+    const size_t kvbase = sq.row0(hq / (H / Hkv), Hkv) * D;
     const uint32_t slice_b = (uint32_t)N * D * 2;
     const float c = scale * kLog2e;
 
@@ -416,8 +452,8 @@ attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             gf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0));
         }
     }
-    const float lq = q < N ? Lc[(size_t)bh * N + q] : 0.f;
-    const float dq = q < N ? Dl[(size_t)bh * N + q] : 0.f;
+    const float lq = q < N ? Lc[qrow0 + q] : 0.f;
+    const float dq = q < N ? Dl[qrow0 + q] : 0.f;
     f32x16 acc[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
@@ -508,18 +544,19 @@ attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 // the grid covers more of the chip.
 constexpr long long kCUs = 256;
 
-template <int D, bool CAUSAL>
+// N is the sequence length, or with cu (packed sequences) the longest one.
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_dkdv(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* g,
                        const float* Lc, const float* Dl, void* dK, void* dV, int B, int H,
-                       int Hkv, int N, float scale, hipStream_t stream)
+                       int Hkv, int N, float scale, const int* cu, int total, hipStream_t stream)
 {
     const int BHkv = B * Hkv;
     auto go = [&](auto nwc) {
         constexpr int NW = decltype(nwc)::value;
         const int nkb = (N + NW * 32 - 1) / (NW * 32);
-        attn_bwd_dkdv_kernel<D, NW, CAUSAL><<<dim3((unsigned)(nkb * BHkv)), dim3(NW * 64), 0, stream>>>(
+        attn_bwd_dkdv_kernel<D, NW, CAUSAL, VARLEN><<<dim3((unsigned)(nkb * BHkv)), dim3(NW * 64), 0, stream>>>(
             q, k, v, g, Lc, Dl, static_cast<__bf16*>(dK), static_cast<__bf16*>(dV), N, BHkv, H, Hkv,
-            scale);
+            scale, cu, total);
         return hipGetLastError();
     };
     if ((long long)((N + 255) / 256) * BHkv >= kCUs) return go(std::integral_constant<int, 8>{});
@@ -527,17 +564,17 @@ hipError_t launch_dkdv(const __bf16* q, const __bf16* k, const __bf16* v, const 
     return go(std::integral_constant<int, 2>{});
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_dq(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* g,
                      const float* Lc, const float* Dl, void* dQ, int B, int H, int Hkv, int N,
-                     float scale, hipStream_t stream)
+                     float scale, const int* cu, int total, hipStream_t stream)
 {
     const int BH = B * H;
     auto go = [&](auto nwc) {
         constexpr int NW = decltype(nwc)::value;
         const int nqb = (N + NW * 32 - 1) / (NW * 32);
-        attn_bwd_dq_kernel<D, NW, CAUSAL><<<dim3((unsigned)(nqb * BH)), dim3(NW * 64), 0, stream>>>(
-            q, k, v, g, Lc, Dl, static_cast<__bf16*>(dQ), N, BH, nqb, H, Hkv, scale);
+        attn_bwd_dq_kernel<D, NW, CAUSAL, VARLEN><<<dim3((unsigned)(nqb * BH)), dim3(NW * 64), 0, stream>>>(
+            q, k, v, g, Lc, Dl, static_cast<__bf16*>(dQ), N, BH, nqb, H, Hkv, scale, cu, total);
         return hipGetLastError();
     };
     if ((long long)((N + 255) / 256) * BH >= kCUs) return go(std::integral_constant<int, 8>{});
@@ -545,17 +582,19 @@ hipError_t launch_dq(const __bf16* q, const __bf16* k, const __bf16* v, const __
     return go(std::integral_constant<int, 2>{});
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                       const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
-                      float scale, float* Dl, float* Lc, hipStream_t stream)
+                      float scale, float* Dl, float* Lc, const int* cu, int total,
+                      hipStream_t stream)
 {
     const int BH = B * H;
     const __bf16* q = static_cast<const __bf16*>(Q);
     const __bf16* k = static_cast<const __bf16*>(K);
     const __bf16* v = static_cast<const __bf16*>(V);
     const __bf16* g = static_cast<const __bf16*>(dO);
-    const long long rows = (long long)BH * N;
+    // Row statistics for every query row: B H N dense rows, or H total packed.
+    const long long rows = VARLEN ? (long long)H * total : (long long)BH * N;
     {
         constexpr int RPB = 256 / (D / 8);
         const long long need = (rows + RPB - 1) / RPB;
@@ -564,10 +603,11 @@ hipError_t launch_bwd(const void* Q, const void* K, const void* V, const void* O
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (const hipError_t e = launch_dkdv<D, CAUSAL>(q, k, v, g, Lc, Dl, dK, dV, B, H, Hkv, N, scale, stream);
+    if (const hipError_t e = launch_dkdv<D, CAUSAL, VARLEN>(q, k, v, g, Lc, Dl, dK, dV, B, H, Hkv, N,
+                                                            scale, cu, total, stream);
         e != hipSuccess)
         return e;
-    return launch_dq<D, CAUSAL>(q, k, v, g, Lc, Dl, dQ, B, H, Hkv, N, scale, stream);
+    return launch_dq<D, CAUSAL, VARLEN>(q, k, v, g, Lc, Dl, dQ, B, H, Hkv, N, scale, cu, total, stream);
 }
 
 }  // namespace
@@ -578,10 +618,23 @@ hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, con
                                 float* Dl, float* Lc, hipStream_t stream)
 {
     if (d == 64)
-        return causal ? launch_bwd<64, true>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, Dl, Lc, stream)
-                      : launch_bwd<64, false>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, Dl, Lc, stream);
-    return causal ? launch_bwd<128, true>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, Dl, Lc, stream)
-                  : launch_bwd<128, false>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, Dl, Lc, stream);
+        return causal ? launch_bwd<64, true, false>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, Dl, Lc, nullptr, 0, stream)
+                      : launch_bwd<64, false, false>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, Dl, Lc, nullptr, 0, stream);
+    return causal ? launch_bwd<128, true, false>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, Dl, Lc, nullptr, 0, stream)
+                  : launch_bwd<128, false, false>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, Dl, Lc, nullptr, 0, stream);
+}
+
+hipError_t launch_attn_bwd_bf16_varlen(const void* Q, const void* K, const void* V, const void* O,
+                                       const void* dO, const float* lse, void* dQ, void* dK,
+                                       void* dV, const int* cu, int B, int H, int Hkv, int total,
+                                       int max_seqlen, int d, float scale, bool causal, float* Dl,
+                                       float* Lc, hipStream_t stream)
+{
+    if (d == 64)
+        return causal ? launch_bwd<64, true, true>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, max_seqlen, scale, Dl, Lc, cu, total, stream)
+                      : launch_bwd<64, false, true>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, max_seqlen, scale, Dl, Lc, cu, total, stream);
+    return causal ? launch_bwd<128, true, true>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, max_seqlen, scale, Dl, Lc, cu, total, stream)
+                  : launch_bwd<128, false, true>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, max_seqlen, scale, Dl, Lc, cu, total, stream);
 }
 
 }  // namespace osm

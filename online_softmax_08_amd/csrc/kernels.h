@@ -44,6 +44,13 @@ hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, con
                                 const void* dO, const float* lse, void* dQ, void* dK, void* dV,
                                 int B, int H, int Hkv, int N, int d, float scale, bool causal,
                                 float* Dl, float* Lc, hipStream_t stream);
+// Backward over packed sequences: Q, O, dO, dQ [H][total][d], K, V, dK, dV
+// [Hkv][total][d], lse, Dl, Lc [H][total].
+hipError_t launch_attn_bwd_bf16_varlen(const void* Q, const void* K, const void* V, const void* O,
+                                       const void* dO, const float* lse, void* dQ, void* dK,
+                                       void* dV, const int* cu, int B, int H, int Hkv, int total,
+                                       int max_seqlen, int d, float scale, bool causal, float* Dl,
+                                       float* Lc, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const float* Q, const float* K, const float* V, float* O,
                                float* lse, int BH, int N, int d, float scale, bool causal,
                                hipStream_t stream);

@@ -178,6 +178,37 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
     return dq, dk, dv
 
 
+def attention_varlen_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                              out: torch.Tensor, lse: torch.Tensor, grad_out: torch.Tensor,
+                              cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = False,
+                              scale: float | None = None):
+    """Gradients (dq, dk, dv) of sum(grad_out * out) for out, lse =
+    attention_varlen(q, k, v, cu_seqlens, max_seqlen, causal, scale)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("grad_out", grad_out)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 [heads, total, d] GPU tensor")
+    if out.shape != q.shape or grad_out.shape != q.shape or k.shape != v.shape or \
+            k.shape[1:] != q.shape[1:] or q.shape[0] % k.shape[0]:
+        raise ValueError("q, out, grad_out must be [H, total, d] and k, v [Hkv, total, d]")
+    H, total, d = q.shape
+    if lse.shape != (H, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [H, total] tensor")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device:
+        raise ValueError("cu_seqlens must be an int32 [B + 1] tensor on q's device")
+    B = cu_seqlens.numel() - 1
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    ws_bytes = _abi.attn_bwd_workspace_bytes(1, H, total)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    with torch.cuda.device(q.device):
+        _abi.attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             grad_out.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), cu_seqlens.data_ptr(), max(B, 0), H, k.shape[0],
+                             total, int(max_seqlen), d, scale, causal, workspace.data_ptr(),
+                             ws_bytes, _stream_handle(q.device))
+    return dq, dk, dv
+
+
 def softmax(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Stable softmax over the last dimension of a contiguous fp32 [B, N] GPU tensor.
     ``out`` may be ``x`` itself (in place)."""

@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
                                             "attn_fwd_varlen",
                                             "attn_fwd_splitkv_plan",
                                             "attn_fwd_splitkv", "attn_combine",
-                                            "attn_bwd_workspace_bytes", "attn_bwd", "row_softmax",
+                                            "attn_bwd_workspace_bytes", "attn_bwd",
+                                            "attn_bwd_varlen", "row_softmax",
                                             "osm_status_str"])
 
 
@@ -263,3 +264,26 @@ def test_gqa_validation(abi):
     assert status(K=0) == abi.OSM_ERR_NULL
     assert status(O=2 * FAKE + 512) == abi.OSM_ERR_ALIAS  # O inside K
     abi.attn_fwd_gqa(0, 0, 0, 0, 0, 0, 4, 2, 16, 64, 0.125, 0)  # empty: no-op
+
+
+def test_bwd_varlen_validation(abi):
+    ptr = {n: (i + 1) * FAKE for i, n in enumerate(("Q", "K", "V", "O", "dO", "lse", "dQ", "dK",
+                                                      "dV", "cu", "ws"))}
+    need = abi.attn_bwd_workspace_bytes(1, 2, 100)
+
+    def status(ws_bytes=need, **kw):
+        a = dict(ptr, B=2, H=2, Hkv=1, total=100, maxs=64, d=64, scale=0.125, causal=1)
+        a.update(kw)
+        with pytest.raises(abi.OsmError) as e:
+            abi.attn_bwd_varlen(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["lse"], a["dQ"], a["dK"],
+                                a["dV"], a["cu"], a["B"], a["H"], a["Hkv"], a["total"], a["maxs"],
+                                a["d"], a["scale"], a["causal"], a["ws"], ws_bytes)
+        return e.value.status
+    assert status(total=-1) == abi.OSM_ERR_SIZE
+    assert status(d=16) == abi.OSM_ERR_HEAD_DIM
+    assert status(Hkv=3) == abi.OSM_ERR_HEADS
+    assert status(cu=0) == abi.OSM_ERR_NULL
+    assert status(ws_bytes=need - 1) == abi.OSM_ERR_WORKSPACE
+    assert status(dK=ptr["cu"]) == abi.OSM_ERR_ALIAS
+    assert status(ws=ptr["dQ"] + 16) == abi.OSM_ERR_ALIAS
+    abi.attn_bwd_varlen(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 2, 2, 2, 0, 64, 64, 0.125, 1, 0, 0)

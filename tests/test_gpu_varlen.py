@@ -105,3 +105,47 @@ def test_varlen_long_mixed_sampled(osm):
         el = max(el, float(np.max(np.abs(lse[bh, a + qi] - lref))))
     print(f"varlen long: max|dO|={eo:.3e} max|dlse|={el:.3e}", flush=True)
     assert eo <= TOL_O and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("heads", [(2, 2), (4, 2)])
+def test_varlen_backward_against_per_sequence_oracle(osm, heads, causal):
+    # Gradients of packed sequences (from the packed forward's own O and lse)
+    # against the oracle's gradients of each sequence alone; with fewer
+    # key/value heads the oracle repeats them and sums the gradient copies.
+    H, Hkv = heads
+    G = H // Hkv
+    lengths = [130, 1, 0, 257, 64, 500]
+    d = 64
+    total = sum(lengths)
+    base = inputs.ATTN["attn_bf16_B2H8N1024d64"]
+    q = inputs.attn_inputs(base, B=1, H=H, N=total, d=d, seed=950)[0][0]
+    _, k, v = inputs.attn_inputs(base, B=1, H=Hkv, N=total, d=d, seed=951)
+    k, v = k[0], v[0]
+    g = inputs.grad_output(q.shape, 952)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, g))
+    cu_t = torch.from_numpy(cu).to(dev)
+    O, lse = osm.attention_varlen(qd, kd, vd, cu_t, max(lengths), causal=causal)
+    dq, dk, dv = osm.attention_varlen_backward(qd, kd, vd, O, lse, gd, cu_t, max(lengths),
+                                               causal=causal)
+    torch.cuda.synchronize()
+    got = [t.float().cpu().numpy() for t in (dq, dk, dv)]
+    errs, scales = [0.0] * 3, [1.0] * 3
+    for b in range(len(lengths)):
+        a, e = int(cu[b]), int(cu[b + 1])
+        if a == e:
+            continue
+        rq, rk, rv = oracle.attn_bwd(q[None, :, a:e], k[None, :, a:e].repeat_interleave(G, dim=1),
+                                     v[None, :, a:e].repeat_interleave(G, dim=1), g[None, :, a:e],
+                                     1 / math.sqrt(d), causal)
+        rk = rk[0].reshape(Hkv, G, e - a, d).sum(axis=1)
+        rv = rv[0].reshape(Hkv, G, e - a, d).sum(axis=1)
+        for i, (x, r) in enumerate(zip(got, (rq[0], rk, rv))):
+            errs[i] = max(errs[i], float(np.max(np.abs(x[:, a:e] - r))))
+            scales[i] = max(scales[i], float(np.max(np.abs(r))))
+    print(f"varlen bwd H{H}Hkv{Hkv} causal={causal}: errs={[f'{x:.3e}' for x in errs]} "
+          f"bars={[f'{2e-2 * s:.3e}' for s in scales]}", flush=True)
+    assert all(np.isfinite(x).all() for x in got)
+    assert all(e <= 2e-2 * s for e, s in zip(errs, scales))

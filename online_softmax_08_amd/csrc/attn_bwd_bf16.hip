@@ -34,7 +34,16 @@
 //  * Q/dO (dK/dV kernel) and K (dQ kernel) tiles are read both row-wise
 //    (ds_read_b128, rows permuted at read time so that each 8-register group
 //    of an accumulator holds 8 consecutive tile rows) and transposed
-//    (ds_read_b64_tr_b16), so they stay in natural row order in LDS.
+//    (ds_read_b64_tr_b16).  No row pitch is free of bank conflicts for both:
+//    a b128 read serves 16 lanes (16 rows) per cycle and wants rows 16 bytes
+//    apart modulo 256, the transposed read serves 32 lanes (64 bytes of each
+//    of 4 rows) and wants them 64 bytes apart.  So tiles keep pitch d + 8 and
+//    store the rows of each 16-row group in the order that swaps the two
+//    2-bit halves of the row index: the 4 rows of a transposed read then
+//    lie 4 physical rows (64 bytes modulo 256) apart, while the 16 rows of a
+//    row-wise read are still 16 distinct rows of one group.  The permutation
+//    is its own inverse and costs nothing: the DMA source offsets and the
+//    lanes' LDS addresses are computed once.
 
 #include <type_traits>
 
@@ -52,6 +61,12 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 __device__ __forceinline__ int swap_bits23(int i)
 {
     return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+// Physical LDS row of tile row r: bits 0-1 and 2-3 of r swapped.
+__device__ __forceinline__ int lds_row(int r)
+{
+    return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
@@ -74,8 +89,9 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
 
 // Tile of R rows x D bf16 in LDS with row pitch D + 8 elements, filled by
 // 1 KiB wave loads: load i writes chunk positions 64 i .. 64 i + 63; chunk
-// position p holds row p / (D/8 + 1), column chunk p % (D/8 + 1) (the last
-// chunk of a row is padding and re-fetches the row's last real chunk).
+// position p holds tile row lds_row(p / (D/8 + 1)), column chunk
+// p % (D/8 + 1) (the last chunk of a row is padding and re-fetches the row's
+// last real chunk).
 template <int D, int R>
 struct Tile {
     static constexpr int P = D + 8;          // row pitch (elements)
@@ -83,32 +99,37 @@ struct Tile {
     static constexpr int BYTES = R * P * 2;
     static constexpr int INST = BYTES / 1024;
     static_assert(BYTES % 1024 == 0, "tile is whole wave loads");
+    static_assert(R % 16 == 0, "rows are permuted in groups of 16");
     __device__ static uint32_t src_offset(int p)
     {
-        const int row = p / CPR, ch = min(p % CPR, D / 8 - 1);
+        const int row = lds_row(p / CPR), ch = min(p % CPR, D / 8 - 1);
         return (uint32_t)(row * D + ch * 8) * 2;
     }
 };
 
 // A operand of a 32x32x16 product from a row-major LDS tile, row-wise: lane
-// (i, h) supplies tile row row0 + swap_bits23(i), columns col0 + 8 h .. + 7.
+// (i, h) supplies tile row row0 + swap_bits23(i), columns col0 + 8 h .. + 7
+// (row0 a multiple of 16).
 template <int PITCH>
 __device__ __forceinline__ bf16x8 rows_a(const char* tile, int row0, int col0, int i, int h)
 {
-    return *reinterpret_cast<const bf16x8*>(tile + ((row0 + swap_bits23(i)) * PITCH + col0 + 8 * h) * 2);
+    return *reinterpret_cast<const bf16x8*>(
+        tile + ((row0 + lds_row(swap_bits23(i))) * PITCH + col0 + 8 * h) * 2);
 }
 
 // A operand from a row-major LDS tile, transposed: operand row i is tile
 // column col0 + i, operand column k (= 8 h + e) is tile row row0 + k, via
 // two ds_read_b64_tr_b16 (lane 16 g + 4 e + a reads 4 columns
-// 16 (g % 2) + 4 a of tile row 8 (g / 2) + e, and 4 rows further).
+// 16 (g % 2) + 4 a of tile row 8 (g / 2) + e, and of the row 4 further,
+// which are physical rows 4 e + 2 (g / 2) and the next one; row0 a multiple
+// of 16).
 template <int PITCH>
 __device__ __forceinline__ bf16x8 cols_a(const char* tile, int row0, int col0, int lane)
 {
     const int g16 = lane >> 4, e4 = (lane >> 2) & 3, a4 = lane & 3;
-    const char* p = tile + ((row0 + 8 * (g16 >> 1) + e4) * PITCH + col0 + 16 * (g16 & 1) + 4 * a4) * 2;
+    const char* p = tile + ((row0 + 4 * e4 + 2 * (g16 >> 1)) * PITCH + col0 + 16 * (g16 & 1) + 4 * a4) * 2;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * PITCH * 2));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + PITCH * 2));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -255,7 +276,7 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 lds_dma16(vrs, (lds_void_t*)(vblk + i * 1024), TV::src_offset(i * 64 + lane));
         }
     }
-    const char* vrow = vblk + ((wave * 32 + j) * TV::P + 8 * h) * 2;
+    const char* vrow = vblk + ((wave * 32 + lds_row(j)) * TV::P + 8 * h) * 2;
     f32x16 dvt[D / 32], dkt[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {

@@ -42,8 +42,12 @@
 //    the row-major V tile through ds_read_b64_tr_b16, the gfx950 transposing
 //    LDS read: in each group of 16 lanes, lane 4a + b receives element b of
 //    the 8-byte reads of lanes a, a + 4, a + 8 and a + 12.
-//  * Row pitches (K: d + 8, V: d + 16 elements) make both LDS read patterns
-//    bank-conflict free.
+//  * Row pitches (K: d + 8, V: d + 32 elements) make both LDS read patterns
+//    bank-conflict free.  A 16-byte row read serves 16 lanes per cycle, so
+//    rows 16 bytes apart modulo 256 fill all 64 banks; the 8-byte transposed
+//    read serves 32 lanes per cycle, which take 64 contiguous bytes from each
+//    of 4 rows, so those rows must start 64 bytes apart modulo 256, which a
+//    pitch of d + 32 gives (d + 16 leaves 2-way conflicts).
 //  * p = 2^(s c - m c) with c = scale log2(e): one FMA and one v_exp_f32 per
 //    score.  The reference m only moves when some row of the wave has a tile
 //    maximum more than 8 (in log2 units) above it; otherwise every p <= 2^8
@@ -134,9 +138,9 @@ struct Cfg {
     static constexpr int T = NW * 64;         // threads per workgroup
     static constexpr int BR = NW * QT * 32;   // query rows per workgroup
     static constexpr int KP = D + 8;          // K row pitch in LDS (elements)
-    static constexpr int VP = D + 16;         // V row pitch in LDS (elements)
+    static constexpr int VP = D + 32;         // V row pitch in LDS (elements)
     static constexpr int KCPR = KP / 8;       // 16-byte chunks per K row (last is padding)
-    static constexpr int VCPR = VP / 8;       // 16-byte chunks per V row (last two padding)
+    static constexpr int VCPR = VP / 8;       // 16-byte chunks per V row (last four padding)
     static constexpr int KTILE_B = BC * KP * 2;
     static constexpr int VTILE_B = BC * VP * 2;
     static constexpr int KINST = KTILE_B / 1024;  // 1 KiB wave loads per K tile

@@ -6,7 +6,11 @@ one stable row softmax over fp32 [32768, 8192].  Inputs are seeded synthetic
 tensors already resident in HBM.  W untimed warm-up steps, then K timed steps
 between device synchronisations; HIP events recorded on the launch stream
 (torch's current stream) around each launch give each kernel's mean launch
-duration.
+duration.  The defaults (50 warm-up, 100 timed steps, about 80 ms of GPU
+work) measure the sustained state: once the softmax starts alternating with
+the attention, the GPU's clock management lowers the attention kernel's
+clock for roughly the first 30 steps (its launches run up to 15% longer)
+before it settles.
 
 Prints one JSON line:
   value             attention TFLOPS, counted FLOPs 4*B*H*N^2*d / 2 (causal)
@@ -72,8 +76,8 @@ def measured_traffic(tag: str, sources) -> float | None:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing leg (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",

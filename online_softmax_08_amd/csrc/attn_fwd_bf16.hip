@@ -49,10 +49,14 @@
 //    of 4 rows, so those rows must start 64 bytes apart modulo 256, which a
 //    pitch of d + 32 gives (d + 16 leaves 2-way conflicts).
 //  * p = 2^(s c - m c) with c = scale log2(e): one FMA and one v_exp_f32 per
-//    score.  The reference m only moves when some row of the wave has a tile
-//    maximum more than 8 (in log2 units) above it; otherwise every p <= 2^8
-//    and neither l nor the accumulators are touched.  The result is the same
-//    exact quantity: l and the accumulators share the reference.
+//    score.  The reference m is not moved on every new maximum: in
+//    attn_fwd_bf16_kernel it moves when some row of the wave has a tile
+//    maximum more than 8 (in log2 units) above it, so every p <= 2^8; in
+//    attn_fwd_bf16_pp_kernel the tile's probabilities are computed first and
+//    the reference moves only when some lane's partial row sum exceeds 2^16
+//    (which bounds every p), so the common tile needs no row maximum.  Either
+//    way the result is the same exact quantity: l and the accumulators share
+//    the reference.
 //  * Two schedules share these pieces.  attn_fwd_bf16_kernel runs each tile
 //    as S^T, softmax, P V in every wave; the two waves of a SIMD then mostly
 //    use the matrix core and the vector unit at the same time and wait for
@@ -69,6 +73,10 @@ namespace osm {
 namespace {
 
 constexpr float kRescaleLog2 = 8.0f;  // move the reference beyond 2^8 growth
+// Phase-staggered kernel: keep the reference while every lane's partial row
+// sum of a tile stays within 2^16 (so every p <= 2^16, far inside bf16 and
+// fp32 range).
+constexpr float kSumLimit = 65536.0f;
 
 typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
@@ -688,8 +696,8 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
     };
-    // Vector phase of step i: mask (last tile only), row maxima, the rare
-    // move of the exponent reference, probabilities and row sums.
+    // Vector phase of step i: mask (last tile only), probabilities and row
+    // sums, and the rare move of the exponent reference.
     auto vector_phase = [&](int i) {
         if (i < 0 || i >= T) return;
         if (i == T - 1 && mask_last) {
@@ -704,43 +712,52 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
                 for (int r = 0; r < 16; ++r)
                     if (mt * 32 + 16 * (r >> 3) + (r & 7) >= thr) s[mt][r] = kNegInf;
         }
-        float v[4];
+        // Probabilities against the current reference m (one FMA and one
+        // v_exp_f32 each), their bf16 copies (the B operand of P V) and this
+        // lane's partial row sum.  s keeps the scores for a recomputation.
+        auto probs = [&](float mc) {
+            float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = fmaxf(s[0][u], s[0][u + 4]);
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 8; r < 16; ++r) v[r & 3] = fmaxf(v[r & 3], s[0][r]);
+                for (int half = 0; half < 2; ++half) {
+                    f32x8 p8;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v[r & 3] = fmaxf(v[r & 3], s[1][r]);
-        const float mx = combine_xor32(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), MaxOp());
-        if (__builtin_amdgcn_ballot_w64((mx - m) * c > kRescaleLog2) != 0) {
-            // Tile 0 holds key 0, visible to every row, so m_new is finite;
-            // an empty history (m = -inf, l = acc = 0) gets factor 0.
+                    for (int r8 = 0; r8 < 8; ++r8) {
+                        p8[r8] = exp2_hw(fmaf(s[mt][8 * half + r8], c, -mc));
+                        ps[r8 & 3] += p8[r8];
+                    }
+                    pf[2 * mt + half] = __builtin_convertvector(p8, bf16x8);
+                }
+            return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        };
+        float lsum = probs(m * c);
+        // No p exceeds its lane's sum, so while every lane's sum stays within
+        // kSumLimit the reference can stay where it is: the tile needs no row
+        // maximum at all.  Otherwise, and on a row's first tile (m = -inf,
+        // where the probabilities above are inf or NaN), the reference moves
+        // to the row maximum, l and the accumulators are rescaled by
+        // 2^((m_old - m_new) c) (0 for an empty history), and the tile's
+        // probabilities are recomputed.  Tile 0 holds key 0, visible to every
+        // row, so the new reference is finite.
+        if (__builtin_amdgcn_ballot_w64(m == kNegInf || lsum > kSumLimit) != 0) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = fmaxf(s[0][u], s[0][u + 4]);
+#pragma unroll
+            for (int r = 8; r < 16; ++r) v[r & 3] = fmaxf(v[r & 3], s[0][r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) v[r & 3] = fmaxf(v[r & 3], s[1][r]);
+            const float mx = combine_xor32(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), MaxOp());
             const float m_new = fmaxf(m, mx);
             const float alpha = (m_new == kNegInf) ? 1.f : exp2_hw((m - m_new) * c);
             l *= alpha;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
             m = m_new;
+            lsum = probs(m * c);
         }
-        const float mc = m * c;
-        float ps[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = exp2_hw(fmaf(s[mt][r], c, -mc));
-                s[mt][r] = p;
-                ps[r & 3] += p;
-            }
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const f32x16& sv = s[mt];
-                const f32x8 p8 = half ? __builtin_shufflevector(sv, sv, 8, 9, 10, 11, 12, 13, 14, 15)
-                                      : __builtin_shufflevector(sv, sv, 0, 1, 2, 3, 4, 5, 6, 7);
-                pf[2 * mt + half] = __builtin_convertvector(p8, bf16x8);
-            }
-        }
-        l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        l += lsum;
     };
 
     using B0 = std::integral_constant<int, 0>;

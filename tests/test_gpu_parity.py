@@ -149,6 +149,44 @@ def test_attn_rescale_stress(osm):
                     f"rising scores f32 causal={causal}")
 
 
+def test_attn_rescale_stress_full_grid(osm):
+    # Scores built to move the exponent reference in every way, on a grid
+    # large enough for the 8-wave kernels (256 query blocks of 256 rows).
+    # Eight kinds of head (score = q_0 k_0 plus small noise): keys rising by
+    # 12, 2 or 0.16 (log2 units) per 64-key tile, rising by 13 per tile for
+    # queries boosted x16, falling scores, and jumps of ~150 log2 units in
+    # mid-tile or at a tile boundary, where every probability of the tile
+    # overflows against the old reference and must be recomputed.  Scaled
+    # scores stay below ~150 so that fp32 resolves lse to 1e-3.  Every row of
+    # the eight head kinds is compared with the oracle.
+    B, H, N, d = 1, 64, 1024, 128
+    j = torch.arange(N, dtype=torch.float32)
+    kind = [1.5 * j, 0.25 * j, 0.1 * j, 1200.0 * (j >= 300), 1200.0 * (j >= 512), -0.5 * j,
+            0.02 * j, 400.0 * (j >= 200) + 800.0 * (j >= 700)]
+    qboost = [1.0, 1.0, 16.0, 1.0, 1.0, 1.0, 1.0, 1.0]
+    g = torch.Generator().manual_seed(15)
+    q = 0.25 * torch.randn(B, H, N, d, generator=g)
+    k = 0.25 * torch.randn(B, H, N, d, generator=g)
+    v = torch.randn(B, H, N, d, generator=g)
+    for h in range(H):
+        q[0, h, :, 0] = qboost[h % 8]
+        k[0, h, :, 0] = kind[h % 8]
+    q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
+    scale = 1.0 / math.sqrt(d)
+    heads = list(range(8)) + [45, 63]
+    bh = np.repeat(np.array(heads), N)
+    qi = np.tile(np.arange(N), len(heads))
+    for causal in (False, True):
+        O, lse = _gpu_attn(osm, q, k, v, causal, scale)
+        assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse))
+        Oref, lref = oracle.attn_rows(q, k, v, scale, causal, bh, qi)
+        eo = _maxabs(O.reshape(B * H, N, d)[bh, qi], Oref)
+        el = _maxabs(lse.reshape(B * H, N)[bh, qi], lref)
+        print(f"rescale stress, 8-wave grid, causal={causal}: max|dO|={eo:.3e} max|dlse|={el:.3e} "
+              f"(max |lse| {np.max(np.abs(lref)):.1f})", flush=True)
+        assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1]
+
+
 def test_attn_constant_values(osm):
     # All value rows equal to c: O must equal c (up to bf16 rounding of c's
     # products, here exact because p sums to 1 and c is a small grid value).

@@ -652,6 +652,8 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) pf[ks] = bf16x8{};
 
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
     auto qk = [&](auto kbc) {
         s[0] = f32x16{};
         s[1] = f32x16{};
@@ -678,12 +680,12 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     };
 
 
-    // Matrix phase of step i: P V of tile i - 1, then S^T of tile i, as one
-    // block whose LDS reads the scheduler keeps several MFMAs ahead of their
-    // use (48 reads feed 32 MFMAs).  One code path for steps 0 .. T keeps
-    // the accumulators in fixed registers: step 0 multiplies P = 0 with the
-    // zeroed V buffer (adds exactly 0), and the scores step T computes are
-    // never used.
+    // Matrix phase of step i (1 <= i <= T): P V of tile i - 1, then S^T of
+    // tile i, as one block whose LDS reads the scheduler keeps several MFMAs
+    // ahead of their use (48 reads feed 32 MFMAs).  One code path for steps
+    // 1 .. T keeps the accumulators in fixed registers: the scores step T
+    // computes are never used (a separate P V-only path for it costs more
+    // registers than the 16 products save).
     auto matrix_phase = [&](auto kbc, auto vbc, int i) {
         if (i > T) return;
         pv(vbc);
@@ -695,6 +697,17 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    };
+    // Step 0 has no probabilities yet: its matrix phase is S^T of tile 0.
+    auto first_matrix_phase = [&]() {
+        qk(B0{});
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int u = 0; u < 12; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     };
     // Vector phase of step i: mask (last tile only), probabilities and row
     // sums, and the rare move of the exponent reference.
@@ -760,16 +773,12 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         l += lsum;
     };
 
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
-    // Prologue: K(0) (waves 0-3), and zeros into vbuf1 (V(-1), read by step
-    // 0, so that 0 * V stays 0).
+    // Prologue: K(0) (waves 0-3).
     if (!late) load_part(B0{}, 0);
-    for (int o = tid * 16; o < C::VTILE_B; o += NW * 64 * 16)
-        *reinterpret_cast<u32x4*>(vbuf1 + o) = u32x4{};
     __syncthreads();
-    // Steps i = 0 .. ntiles (step ntiles only finishes P V); two steps per
-    // loop trip so every LDS buffer is a compile-time choice: K(i) sits in
+    // Steps i = 0 .. ntiles (step ntiles only finishes P V); step 0 (S^T of
+    // tile 0 alone) is peeled, then two steps per loop trip so that every
+    // LDS buffer is a compile-time choice: K(i) sits in
     // kbuf[i % 2], V(i) in vbuf[i % 2].  K(i + 1) (loaded at the start of
     // phase 2i) and V(i) (start of phase 2i + 1) are waited for at the
     // barrier that ends phase 2i + 1.  No barrier separates phase 2i from
@@ -780,32 +789,42 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     // keeps each copy's live registers to those of one phase order.
     auto steps = [&](auto latec) {
         constexpr bool LATE = decltype(latec)::value;
-        for (int i = 0; i <= ntiles; i += 2) {
+        // step 0
+        if constexpr (!LATE) {
+            if (1 < ntiles) load_part(B1{}, 1);
+            first_matrix_phase();
+            vector_phase(0);
+        } else {
+            load_part(B0{}, 0);
+            first_matrix_phase();
+        }
+        __syncthreads();  // K(1) and V(0) have landed
+        for (int i = 1; i <= ntiles; i += 2) {
             if constexpr (!LATE) {
-                if (i + 1 < ntiles) load_part(B1{}, i + 1);
-                matrix_phase(B0{}, B1{}, i);
+                if (i + 1 < ntiles) load_part(B0{}, i + 1);
+                matrix_phase(B1{}, B0{}, i);
             } else {
                 vector_phase(i - 1);
             }
             if constexpr (!LATE) {
                 vector_phase(i);
             } else {
-                if (i < ntiles) load_part(B0{}, i);
-                matrix_phase(B0{}, B1{}, i);
+                if (i < ntiles) load_part(B1{}, i);
+                matrix_phase(B1{}, B0{}, i);
             }
             if (i + 1 > ntiles) break;
             __syncthreads();  // K(i + 1) and V(i) have landed
             if constexpr (!LATE) {
-                if (i + 2 < ntiles) load_part(B0{}, i + 2);
-                matrix_phase(B1{}, B0{}, i + 1);
+                if (i + 2 < ntiles) load_part(B1{}, i + 2);
+                matrix_phase(B0{}, B1{}, i + 1);
             } else {
                 vector_phase(i);
             }
             if constexpr (!LATE) {
                 vector_phase(i + 1);
             } else {
-                if (i + 1 < ntiles) load_part(B1{}, i + 1);
-                matrix_phase(B1{}, B0{}, i + 1);
+                if (i + 1 < ntiles) load_part(B0{}, i + 1);
+                matrix_phase(B0{}, B1{}, i + 1);
             }
             __syncthreads();  // K(i + 2) and V(i + 1) have landed
         }

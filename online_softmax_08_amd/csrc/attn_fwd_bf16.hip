@@ -42,12 +42,19 @@
 //    the row-major V tile through ds_read_b64_tr_b16, the gfx950 transposing
 //    LDS read: in each group of 16 lanes, lane 4a + b receives element b of
 //    the 8-byte reads of lanes a, a + 4, a + 8 and a + 12.
-//  * Row pitches (K: d + 8, V: d + 32 elements) make both LDS read patterns
-//    bank-conflict free.  A 16-byte row read serves 16 lanes per cycle, so
-//    rows 16 bytes apart modulo 256 fill all 64 banks; the 8-byte transposed
+//  * In attn_fwd_bf16_kernel, row pitches (K: d + 8, V: d + 32 elements)
+//    make both LDS read patterns bank-conflict free; attn_fwd_bf16_pp_kernel
+//    keeps the tiles unpadded and permutes 16-byte chunks (K) or 64-byte
+//    blocks (V) inside each row by an XOR with row bits instead, which needs
+//    no padding chunks and so five fewer tile loads per step.  Either way:
+//    a 16-byte row read serves 16 lanes per cycle, so its 16 rows must hit
+//    16 different 16-byte bank groups (pitch d + 8 puts rows 16 bytes apart
+//    modulo 256; the XOR sends chunk c of row r to slot c ^ r); the 8-byte transposed
 //    read serves 32 lanes per cycle, which take 64 contiguous bytes from each
 //    of 4 rows, so those rows must start 64 bytes apart modulo 256, which a
-//    pitch of d + 32 gives (d + 16 leaves 2-way conflicts).
+//    pitch of d + 32 gives (d + 16 leaves 2-way conflicts), or sit in
+//    different 64-byte block slots, which the XOR of the row's low bits into
+//    the block index gives.
 //  * p = 2^(s c - m c) with c = scale log2(e): one FMA and one v_exp_f32 per
 //    score.  The reference m is not moved on every new maximum: in
 //    attn_fwd_bf16_kernel it moves when some row of the wave has a tile
@@ -605,29 +612,37 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     // Tile loads.  The four waves that are about to run their matrix phase
     // load one part of a tile right before it: waves 0-3 load K(i + 1) at
     // the start of phase 2i, waves 4-7 load V(i) at the start of phase
-    // 2i + 1 (each part 17 or 18 1 KiB loads, about five per wave).  An
-    // LDS-bound load costs its wave some 30 cycles of issue and the CU
-    // accepts about one per 10 cycles, so four waves issuing one part cost
-    // half of what all eight waves issuing both parts at once would.  Load n
-    // of a part fills LDS positions 64 n .. 64 n + 63; the lane at position p
-    // fetches row p / CPR, column chunk p % CPR (padding chunks re-fetch the
-    // row's last real chunk).  K rows are permuted inside each 32-row group
-    // (swap_bits23); V rows keep key order.
+    // 2i + 1.  Tiles sit in LDS unpadded (row pitch D elements) with their
+    // 16-byte chunks permuted inside each row by an XOR with a few bits of
+    // the row index, so that every LDS read below is conflict-free and a
+    // part is exactly D / 8 wave loads of 1 KiB (four per wave at D = 128).
+    // Load n of a part fills LDS positions 64 n .. 64 n + 63; the lane at
+    // position p holds LDS row p / CPR, slot p % CPR, and fetches the global
+    // chunk that belongs there.  K rows are also permuted inside each 32-row
+    // group (swap_bits23); V rows keep key order.
+    //   K: chunk c of row r sits in slot c ^ kkey(r), kkey(r) = (r / RPQ) &
+    //      (CPR - 1), RPQ = rows per 256 bytes: the 16 rows a ds_read_b128
+    //      serves per cycle then hit 16 different 16-byte bank groups.
+    //   V: 64-byte block b of row r sits in block slot b ^ vkey(r), vkey(r) =
+    //      (r / RPQ) & (D / 32 - 1): the 4 rows x 64 bytes that 32 lanes of a
+    //      ds_read_b64_tr_b16 take per cycle then hit all 64 banks once.
     constexpr int NG = NW / 2;  // waves per group
-    constexpr int LPW = ((C::KINST > C::VINST ? C::KINST : C::VINST) + NG - 1) / NG;
+    constexpr int CPR = D / 8, RPQ = 256 / (2 * D), NB = D / 32;
+    constexpr int LPW = (BC * D * 2 / 1024) / NG;
+    static_assert((BC * D * 2 / 1024) % NG == 0, "tile parts split evenly over the group");
     const int g = wave % NG;
-    const int ninst = late ? C::VINST : C::KINST;
     uint32_t src[LPW];
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
         const int p = (g + u * NG) * 64 + lane;
+        const int r = p / CPR, slot = p % CPR;
         if (!late) {
-            const int lrow = p / C::KCPR, ch = min(p % C::KCPR, D / 8 - 1);
-            const int row = (lrow & ~31) | swap_bits23(lrow & 31);
-            src[u] = (uint32_t)(row * D + ch * 8) * 2;
+            const int c = slot ^ ((r / RPQ) & (CPR - 1));
+            const int row = (r & ~31) | swap_bits23(r & 31);
+            src[u] = (uint32_t)(row * D + c * 8) * 2;
         } else {
-            const int row = p / C::VCPR, ch = min(p % C::VCPR, D / 8 - 1);
-            src[u] = (uint32_t)(row * D + ch * 8) * 2;
+            const int blk = (slot / 4) ^ ((r / RPQ) & (NB - 1));
+            src[u] = (uint32_t)(r * D + blk * 32 + (slot % 4) * 8) * 2;
         }
     }
     // This wave's share of tile kt of its group's part into buffer BUFC.
@@ -637,15 +652,20 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
             make_rsrc((late ? V : K) + sl.kvbase + (size_t)kv0 * D, (uint32_t)(N - kv0) * D * 2);
         char* dst = late ? vbuf(bufc) : kbuf(bufc);
 #pragma unroll
-        for (int u = 0; u < LPW; ++u) {
-            const int n = g + u * NG;
-            if (n < ninst) lds_dma16(rs, (lds_void_t*)(dst + n * 1024), src[u]);
-        }
+        for (int u = 0; u < LPW; ++u)
+            lds_dma16(rs, (lds_void_t*)(dst + (g + u * NG) * 1024), src[u]);
     };
 
-    const int kread = (j * C::KP + 8 * h) * 2;
+    // Lane addresses of the operand reads.  K: row j (+ 32 mt), chunk
+    // 2 kk + h at slot (2 kk + h) ^ kkey(j): kbase ^ (kk << 5).  V (the
+    // transposing read): row 16 ks + 8 (g16 >> 1) + e4 (+ 4 for the upper
+    // half), 8 bytes at column 32 dt + 16 (g16 & 1) + 4 a4 of block dt, which
+    // sits in block slot dt ^ vkey: vbase ^ (dt << 6).
+    const int kj = (j / RPQ) & (CPR - 1);
+    const int kbase = j * D * 2 + (h ^ (kj & 1)) * 16 + ((kj >> 1) << 5);
     const int g16 = lane >> 4, e4 = (lane >> 2) & 3, a4 = lane & 3;
-    const int vread = ((8 * (g16 >> 1) + e4) * C::VP + 16 * (g16 & 1) + 4 * a4) * 2;
+    const int vrow = 8 * (g16 >> 1) + e4;
+    const int vbase = vrow * D * 2 + (16 * (g16 & 1) + 4 * a4) * 2 + (((vrow / RPQ) & (NB - 1)) << 6);
 
     f32x16 s[2];    // scores of the current tile, 32 keys each
     bf16x8 pf[4];   // its probabilities, bf16, 16 keys each
@@ -662,7 +682,7 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    kbuf(kbc) + kread + (mt * 32 * C::KP + kk * 16) * 2);
+                    kbuf(kbc) + mt * 64 * D + (kbase ^ (kk << 5)));
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mt], 0, 0, 0);
             }
     };
@@ -671,9 +691,9 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-                const char* vp = vbuf(vbc) + vread + (16 * ks * C::VP + 32 * dt) * 2;
+                const char* vp = vbuf(vbc) + 16 * ks * D * 2 + (vbase ^ (dt << 6));
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)vp);
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 4 * C::VP * 2));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 4 * D * 2));
                 const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], acc[dt], 0, 0, 0);
             }

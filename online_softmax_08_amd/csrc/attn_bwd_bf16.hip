@@ -53,7 +53,6 @@
 namespace osm {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
@@ -166,25 +165,6 @@ __device__ __forceinline__ bf16x8 half_bf16(const f32x16& v, int G)
     const f32x8 p8 = G ? __builtin_shufflevector(v, v, 8, 9, 10, 11, 12, 13, 14, 15)
                        : __builtin_shufflevector(v, v, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_convertvector(p8, bf16x8);
-}
-
-// Store of a transposed accumulator set acc[D/32] (operand row = column t of
-// the output, operand column = output row) as bf16 rows of [N][D], times mul.
-template <int D>
-__device__ __forceinline__ void store_rows_t(__bf16* out, uint32_t slice_bytes, int row, int h,
-                                             const f32x16 (&acc)[D / 32], float mul)
-{
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(out, slice_bytes);
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f32x4 o4 = {acc[dt][4 * g] * mul, acc[dt][4 * g + 1] * mul,
-                              acc[dt][4 * g + 2] * mul, acc[dt][4 * g + 3] * mul};
-            const bf16x4 ob = __builtin_convertvector(o4, bf16x4);
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), rs,
-                                                  (uint32_t)(row * D + dt * 32 + 8 * g + 4 * h) * 2, 0, 0);
-        }
 }
 
 // ---------------------------------------------------------------- delta ----
@@ -422,8 +402,12 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             __syncthreads();
         }
     }
-    store_rows_t<D>(dK + base, slice_b, key, h, dkt, scale);
-    store_rows_t<D>(dV + base, slice_b, key, h, dvt, 1.0f);
+    // Both gradients leave through the wave's 32-row slice of the V block
+    // (BK x (D + 8) elements, 32 rows per wave), which no wave reads any more.
+    __syncthreads();
+    char* const ost = vblk + wave * 32 * (D + 8) * 2;
+    store_tile_rows<D>(dkt, scale, ost, make_rsrc(dK + base, slice_b), key - j, lane);
+    store_tile_rows<D>(dvt, 1.0f, ost, make_rsrc(dV + base, slice_b), key - j, lane);
 }
 
 // ------------------------------------------------------------------- dQ ----
@@ -437,6 +421,7 @@ attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 {
     constexpr int BR = NW * 32, BC = 64;
     using TK = Tile<D, BC>;
+    static_assert(NW <= 8 && TK::BYTES >= 2 * 32 * (D + 8) * 2, "dQ staging fits the tile buffers");
     constexpr int LPW = (TK::INST + NW - 1) / NW;
     __shared__ __attribute__((aligned(1024))) char kb0[TK::BYTES];
     __shared__ __attribute__((aligned(1024))) char kb1[TK::BYTES];
@@ -557,7 +542,12 @@ attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         compute(B1{}, kt + 1);
         __syncthreads();
     }
-    store_rows_t<D>(dQ + base, slice_b, q, h, acc, scale);
+    // dQ leaves through LDS: the wave's half of one of the four K/V tile
+    // buffers (waves 2b, 2b + 1 share buffer b; each holds 2 x 32 rows of
+    // pitch D + 8), which no wave reads any more.
+    __syncthreads();
+    char* const ost = (wave < 2 ? kb0 : wave < 4 ? kb1 : wave < 6 ? vb0 : vb1) + (wave & 1) * (32 * (D + 8) * 2);
+    store_tile_rows<D>(acc, scale, ost, make_rsrc(dQ + base, slice_b), qw0, lane);
 }
 
 // Workgroups of 8 waves (256 keys or queries) while that still gives one per

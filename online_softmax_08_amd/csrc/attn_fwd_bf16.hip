@@ -85,7 +85,6 @@ constexpr float kRescaleLog2 = 8.0f;  // move the reference beyond 2^8 growth
 // fp32 range).
 constexpr float kSumLimit = 65536.0f;
 
-typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
@@ -147,47 +146,15 @@ __device__ __forceinline__ Slice slice_of(int bh, int Nmax, int H, int Hkv, cons
     }
 }
 
-// Output tile of one wave (32 query rows) through LDS.  The accumulators
-// hold O^T (lane j owns query row j, and its lane half h owns columns
-// 32 dt + 8 g + 4 h .. + 3), so direct stores would write 16-byte pieces of
-// 32 different rows per instruction.  Instead each wave writes its rows,
-// scaled by 1 / l and rounded to bf16, into an LDS region of 32 rows of pitch
-// D + 8 elements (2-way bank conflicts at most), and then stores whole rows:
-// 64 lanes x 16 bytes = 64 / (D / 8) full rows per instruction.  The region is
-// the wave's half of one of the four key/value tile buffers (waves 2b, 2b + 1
-// share buffer b), each of which holds at least 2 x 32 x (D + 8) x 2 bytes;
-// the caller makes sure no wave still reads the tiles.  Only the writing wave
-// reads its region back, so a wave-local wait suffices.
+// LDS staging region of a wave's output tile (store_tile_rows): the wave's
+// half of one of the four key/value tile buffers (waves 2b, 2b + 1 share
+// buffer b), each of which holds at least 2 x 32 x (D + 8) x 2 bytes.  The
+// caller makes sure no wave still reads the tiles.
 template <int D>
 __device__ __forceinline__ char* out_stage(int wave, char* k0, char* k1, char* v0, char* v1)
 {
     char* const b = wave < 2 ? k0 : wave < 4 ? k1 : wave < 6 ? v0 : v1;
     return b + (wave & 1) * (32 * (D + 8) * 2);
-}
-
-template <int D>
-__device__ __forceinline__ void store_out_tile(const f32x16 (&acc)[D / 32], float inv, char* ost,
-                                               __amdgpu_buffer_rsrc_t ors, int row0, int lane)
-{
-    const int j = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f32x4 o4 = {acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv,
-                              acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv};
-            *reinterpret_cast<bf16x4*>(ost + (j * (D + 8) + dt * 32 + 8 * g + 4 * h) * 2) =
-                __builtin_convertvector(o4, bf16x4);
-        }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes have landed
-    __builtin_amdgcn_wave_barrier();
-    constexpr int CPR = D / 8, RPI = 64 / CPR;
-#pragma unroll
-    for (int u = 0; u < 32 / RPI; ++u) {
-        const int row = u * RPI + lane / CPR, ch = lane % CPR;
-        const u32x4 v4 = *reinterpret_cast<const u32x4*>(ost + (row * (D + 8) + ch * 8) * 2);
-        __builtin_amdgcn_raw_buffer_store_b128(v4, ors, (uint32_t)((row0 + row) * D + ch * 8) * 2, 0, 0);
-    }
 }
 
 template <int D, int QT, int NW, int BC_>
@@ -540,7 +507,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int nt = 0; nt < QT; ++nt) {
         const float l_tot = combine_xor32(l[nt], SumOp());
         const float inv = 1.0f / l_tot;
-        store_out_tile<D>(acc[nt], inv, ost, ors, qw0 + nt * 32, lane);
+        store_tile_rows<D>(acc[nt], inv, ost, ors, qw0 + nt * 32, lane);
         if (h == 0)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m[nt] * scale + logf(l_tot)), lrs,
                                                   (uint32_t)(qw0 + nt * 32 + j) * 4, 0, 0);
@@ -858,7 +825,7 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lse + sl.lbase, (uint32_t)N * 4);
     const float l_tot = combine_xor32(l, SumOp());
     __syncthreads();  // every wave is done with the tile buffers
-    store_out_tile<D>(acc, 1.0f / l_tot, out_stage<D>(wave, kbuf0, kbuf1, vbuf0, vbuf1), ors, qw0, lane);
+    store_tile_rows<D>(acc, 1.0f / l_tot, out_stage<D>(wave, kbuf0, kbuf1, vbuf0, vbuf1), ors, qw0, lane);
     if (h == 0)
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m * scale + logf(l_tot)), lrs,
                                               (uint32_t)qrow * 4, 0, 0);

@@ -12,6 +12,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
@@ -93,6 +94,42 @@ __device__ __forceinline__ float wave_reduce(float v, Op op)
     v = combine_xor16(v, op);  // combine 16-lane rows pairwise
     v = combine_xor32(v, op);  // combine the two 32-lane halves
     return v;
+}
+
+// Output tile of one wave, 32 rows x D, from transposed MFMA accumulators
+// acc[D / 32] (lane j owns output row row0 + j, and its lane half h owns
+// columns 32 dt + 8 g + 4 h .. + 3 in registers 4 g .. 4 g + 3 of acc[dt]),
+// times mul, rounded to bf16 and stored to the [rows][D] tensor of buffer
+// resource ors.  Direct stores would write 16-byte pieces of 32 different
+// rows per instruction; instead the wave writes its rows into the LDS region
+// ost (32 rows of pitch D + 8 elements, 2-way bank conflicts at most) and
+// then stores whole rows, 64 lanes x 16 bytes = 64 / (D / 8) rows per
+// instruction.  Rows past the resource's range are dropped.  Only the
+// calling wave touches ost, so a wave-local wait orders the two halves; a
+// second call may reuse the same region.
+template <int D>
+__device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[D / 32], float mul, char* ost,
+                                                __amdgpu_buffer_rsrc_t ors, int row0, int lane)
+{
+    const int j = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 o4 = {acc[dt][4 * g] * mul, acc[dt][4 * g + 1] * mul,
+                              acc[dt][4 * g + 2] * mul, acc[dt][4 * g + 3] * mul};
+            *reinterpret_cast<bf16x4*>(ost + (j * (D + 8) + dt * 32 + 8 * g + 4 * h) * 2) =
+                __builtin_convertvector(o4, bf16x4);
+        }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes have landed
+    __builtin_amdgcn_wave_barrier();
+    constexpr int CPR = D / 8, RPI = 64 / CPR;
+#pragma unroll
+    for (int u = 0; u < 32 / RPI; ++u) {
+        const int row = u * RPI + lane / CPR, ch = lane % CPR;
+        const u32x4 v4 = *reinterpret_cast<const u32x4*>(ost + (row * (D + 8) + ch * 8) * 2);
+        __builtin_amdgcn_raw_buffer_store_b128(v4, ors, (uint32_t)((row0 + row) * D + ch * 8) * 2, 0, 0);
+    }
 }
 
 }  // namespace osm

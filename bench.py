@@ -191,7 +191,7 @@ def main() -> int:
     return 0
 
 
-def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=10):
+def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10):
     """Figures measured after the timed region, not part of a step: the same
     attention shape without the causal mask, a plain device copy of the
     softmax input (the practical ceiling for a read-once / write-once
@@ -203,7 +203,7 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=10):
     from online_softmax_08_amd import inputs
 
     def per_launch_ms(fn):
-        for _ in range(2):
+        for _ in range(warm):
             fn()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]

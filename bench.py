@@ -184,9 +184,11 @@ def main() -> int:
                              "algorithmic_bytes": ws.bytes},
         "cpu_baseline": None,
     }
+    # The supplementary figures run while the GPU is still warm; the CPU
+    # baseline (seconds of host work, GPU idle) comes last.
+    out["supplementary"] = supplementary(osm, wa, ws, q, k, v, x, O, lse)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wa, ws, q_cpu, k_cpu, v_cpu, x_cpu, O, lse, y)
-    out["supplementary"] = supplementary(osm, wa, ws, q, k, v, x, O, lse)
     print(json.dumps(out), flush=True)
     return 0
 

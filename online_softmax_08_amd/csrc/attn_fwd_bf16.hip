@@ -26,12 +26,12 @@
 //  * Q stays in VGPRs as the B operand of S^T = K Q^T for the whole kernel.
 //  * K and V tiles of 64 keys move HBM -> LDS by buffer loads that write LDS
 //    directly (no VGPR staging), double-buffered: tile j+1 is in flight while
-//    tile j is computed, one barrier per tile.  Both tiles stay row-major with
-//    padded rows; each wave load instruction fills 1 KiB of LDS, and every
-//    lane picks the global 16 bytes that belong at its LDS position (lanes
-//    landing on row padding fetch a harmless duplicate).  The tile loop is
-//    unrolled by two, so every LDS read address is a loop-invariant register
-//    plus an immediate.
+//    tile j is computed, one barrier per tile.  Both tiles stay row-major;
+//    each wave load instruction fills 1 KiB of LDS, and every lane picks the
+//    global 16 bytes that belong at its LDS position (in the padded layout,
+//    lanes landing on row padding fetch a harmless duplicate).  The tile loop
+//    is unrolled by two, so every LDS read address is a loop-invariant
+//    register plus an immediate.
 //  * S^T puts one query per lane (lane % 32) and 16 keys per lane in each
 //    32x32 accumulator, so the row max and row sum are in-lane reductions plus
 //    one v_permlane32_swap; the row sum is kept per lane and the halves are
@@ -49,12 +49,12 @@
 //    no padding chunks and so five fewer tile loads per step.  Either way:
 //    a 16-byte row read serves 16 lanes per cycle, so its 16 rows must hit
 //    16 different 16-byte bank groups (pitch d + 8 puts rows 16 bytes apart
-//    modulo 256; the XOR sends chunk c of row r to slot c ^ r); the 8-byte transposed
-//    read serves 32 lanes per cycle, which take 64 contiguous bytes from each
-//    of 4 rows, so those rows must start 64 bytes apart modulo 256, which a
-//    pitch of d + 32 gives (d + 16 leaves 2-way conflicts), or sit in
-//    different 64-byte block slots, which the XOR of the row's low bits into
-//    the block index gives.
+//    modulo 256; the XOR sends chunk c of row r to slot c ^ r); the 8-byte
+//    transposed read serves 32 lanes per cycle, which take 64 contiguous
+//    bytes from each of 4 rows, so those rows must start 64 bytes apart
+//    modulo 256, which a pitch of d + 32 gives (d + 16 leaves 2-way
+//    conflicts), or sit in different 64-byte block slots, which the XOR of
+//    the row's low bits into the block index gives.
 //  * p = 2^(s c - m c) with c = scale log2(e): one FMA and one v_exp_f32 per
 //    score.  The reference m is not moved on every new maximum: in
 //    attn_fwd_bf16_kernel it moves when some row of the wave has a tile
@@ -67,9 +67,13 @@
 //  * Two schedules share these pieces.  attn_fwd_bf16_kernel runs each tile
 //    as S^T, softmax, P V in every wave; the two waves of a SIMD then mostly
 //    use the matrix core and the vector unit at the same time and wait for
-//    each other.  attn_fwd_bf16_pp_kernel (used under the causal mask, where
-//    it measures faster) staggers the two waves of each SIMD by half a tile
-//    step, so that one issues only MFMAs while the other runs the softmax.
+//    each other.  It serves the grids of 4- and 2-wave workgroups and the
+//    split-KV partial pass.  attn_fwd_bf16_pp_kernel (8-wave workgroups, both
+//    masks) staggers the two waves of each SIMD by half a tile step, so that
+//    one issues only MFMAs while the other runs the softmax.
+//  * The output tile of each wave leaves through LDS as whole rows
+//    (store_tile_rows): the accumulators hold O^T, whose direct stores would
+//    write 16-byte pieces of 32 rows per instruction.
 
 #include <type_traits>
 

@@ -93,10 +93,12 @@ typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-// Inside a 32-key MFMA tile, LDS row i holds key swap_bits23(i) (bits 2 and 3
-// exchanged; the map is its own inverse).  With A-operand row i read by lane
-// i, the 32x32 accumulator layout (row 8g + 4h + t lands in register 4g + t
-// of lane half h) then leaves key 16*(r/8) + 8*h + r%8 in register r of half h.
+// Inside a 32-key MFMA tile, A-operand row i (read by lane i) is key
+// swap_bits23(i) (bits 2 and 3 exchanged; the map is its own inverse): the
+// plain kernel stores the keys in that order in LDS, the phase-staggered kernel
+// stores them in key order and lets lane i read row swap_bits23(i).  The 32x32
+// accumulator layout (row 8g + 4h + t lands in register 4g + t of lane half h)
+// then leaves key 16*(r/8) + 8*h + r%8 in register r of half h.
 __device__ __forceinline__ int swap_bits23(int i)
 {
     return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
@@ -110,13 +112,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                              0x00020000);
 }
 
-// 16 bytes per lane from a buffer straight into LDS: lane L of the wave writes
-// dst + 16 L.  The builtin sits in a device-only body because clang's host pass
-// otherwise drops the launch stubs of kernels that contain it.
+// 16 bytes per lane from a buffer straight into LDS: lane L of the wave reads
+// buffer offset voff + OFF and writes dst + OFF + 16 L.  The instruction's
+// immediate offset OFF moves both addresses, and the range check applies to
+// voff + OFF (measured: lanes whose sum passes the range read zero), so loads
+// that share one LDS base (M0) can still fill different LDS blocks.  The
+// builtin sits in a device-only body because clang's host pass otherwise drops
+// the launch stubs of kernels that contain it.
+template <int OFF = 0>
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, lds_void_t* dst, uint32_t voff)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, OFF, 0);
 #endif
 }
 
@@ -588,9 +595,12 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     // the row index, so that every LDS read below is conflict-free and a
     // part is exactly D / 8 wave loads of 1 KiB (four per wave at D = 128).
     // Load n of a part fills LDS positions 64 n .. 64 n + 63; the lane at
-    // position p holds LDS row p / CPR, slot p % CPR, and fetches the global
-    // chunk that belongs there.  K rows are also permuted inside each 32-row
-    // group (swap_bits23); V rows keep key order.
+    // position p holds LDS row p / CPR (key order, for K and V), slot
+    // p % CPR, and fetches the global chunk that belongs there.  Wave g of
+    // the group issues loads n = g LPW .. g LPW + LPW - 1: one LDS base for
+    // all of them, load u placed by the immediate offset u KiB, which
+    // src[u] has subtracted (it stays >= 0: the block starts at byte
+    // n KiB of the tile).
     //   K: chunk c of row r sits in slot c ^ kkey(r), kkey(r) = (r / RPQ) &
     //      (CPR - 1), RPQ = rows per 256 bytes: the 16 rows a ds_read_b128
     //      serves per cycle then hit 16 different 16-byte bank groups.
@@ -605,35 +615,42 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     uint32_t src[LPW];
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
-        const int p = (g + u * NG) * 64 + lane;
+        const int p = (g * LPW + u) * 64 + lane;
         const int r = p / CPR, slot = p % CPR;
         if (!late) {
             const int c = slot ^ ((r / RPQ) & (CPR - 1));
-            const int row = (r & ~31) | swap_bits23(r & 31);
-            src[u] = (uint32_t)(row * D + c * 8) * 2;
+            src[u] = (uint32_t)(r * D + c * 8) * 2 - 1024u * u;
         } else {
             const int blk = (slot / 4) ^ ((r / RPQ) & (NB - 1));
-            src[u] = (uint32_t)(r * D + blk * 32 + (slot % 4) * 8) * 2;
+            src[u] = (uint32_t)(r * D + blk * 32 + (slot % 4) * 8) * 2 - 1024u * u;
         }
     }
-    // This wave's share of tile kt of its group's part into buffer BUFC.
-    auto load_part = [&](auto bufc, int kt) {
+    // This wave's share of tile kt of X (K or V) into the LDS buffer dst.
+    // Both are named at each call site, so the compiler sees which LDS
+    // object every load writes.  A tile past the last one (kt >= ntiles)
+    // gets an empty range: its loads read nothing and fill dst with zeros,
+    // which no later step reads, so the loads need no branch.
+    static_assert(LPW >= 1 && LPW <= 4, "one to four loads per wave");
+    auto load_part = [&](const __bf16* X, char* dst, int kt) {
         const int kv0 = kt * BC;
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc((late ? V : K) + sl.kvbase + (size_t)kv0 * D, (uint32_t)(N - kv0) * D * 2);
-        char* dst = late ? vbuf(bufc) : kbuf(bufc);
-#pragma unroll
-        for (int u = 0; u < LPW; ++u)
-            lds_dma16(rs, (lds_void_t*)(dst + (g + u * NG) * 1024), src[u]);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+            X + sl.kvbase + (size_t)kv0 * D, kt < ntiles ? (uint32_t)(N - kv0) * D * 2 : 0u);
+        lds_void_t* const d = (lds_void_t*)(dst + g * LPW * 1024);
+        lds_dma16<0>(rs, d, src[0]);
+        if constexpr (LPW > 1) lds_dma16<1024>(rs, d, src[1]);
+        if constexpr (LPW > 2) lds_dma16<2048>(rs, d, src[2]);
+        if constexpr (LPW > 3) lds_dma16<3072>(rs, d, src[3]);
     };
 
-    // Lane addresses of the operand reads.  K: row j (+ 32 mt), chunk
-    // 2 kk + h at slot (2 kk + h) ^ kkey(j): kbase ^ (kk << 5).  V (the
+    // Lane addresses of the operand reads.  K: row jr = swap_bits23(j)
+    // (+ 32 mt), chunk 2 kk + h at slot (2 kk + h) ^ kkey(jr): kbase ^
+    // (kk << 5).  V (the
     // transposing read): row 16 ks + 8 (g16 >> 1) + e4 (+ 4 for the upper
     // half), 8 bytes at column 32 dt + 16 (g16 & 1) + 4 a4 of block dt, which
     // sits in block slot dt ^ vkey: vbase ^ (dt << 6).
-    const int kj = (j / RPQ) & (CPR - 1);
-    const int kbase = j * D * 2 + (h ^ (kj & 1)) * 16 + ((kj >> 1) << 5);
+    const int jr = swap_bits23(j);
+    const int kj = (jr / RPQ) & (CPR - 1);
+    const int kbase = jr * D * 2 + (h ^ (kj & 1)) * 16 + ((kj >> 1) << 5);
     const int g16 = lane >> 4, e4 = (lane >> 2) & 3, a4 = lane & 3;
     const int vrow = 8 * (g16 >> 1) + e4;
     const int vbase = vrow * D * 2 + (16 * (g16 & 1) + 4 * a4) * 2 + (((vrow / RPQ) & (NB - 1)) << 6);
@@ -671,14 +688,19 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     };
 
 
-    // Matrix phase of step i (1 <= i <= T): P V of tile i - 1, then S^T of
-    // tile i, as one block whose LDS reads the scheduler keeps several MFMAs
-    // ahead of their use (48 reads feed 32 MFMAs).  One code path for steps
-    // 1 .. T keeps the accumulators in fixed registers: the scores step T
-    // computes are never used (a separate P V-only path for it costs more
-    // registers than the 16 products save).
-    auto matrix_phase = [&](auto kbc, auto vbc, int i) {
-        if (i > T) return;
+    // Matrix phase of step i (1 <= i <= T): the wave's tile loads (tile kt
+    // of X into ldst), P V of tile i - 1, then S^T of tile i, as one block
+    // whose LDS reads the scheduler keeps several MFMAs ahead of their use
+    // (48 reads feed 32 MFMAs).  A wave past its last tile (i > T) only
+    // loads.  One code path for steps 1 .. T keeps the accumulators in fixed
+    // registers: the scores step T computes are never used (a separate P
+    // V-only path for it costs more registers than the 16 products save).
+    auto matrix_phase = [&](auto kbc, auto vbc, const __bf16* X, char* ldst, int kt, int i) {
+        if (i > T) {
+            load_part(X, ldst, kt);
+            return;
+        }
+        load_part(X, ldst, kt);
         pv(vbc);
         qk(kbc);
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
@@ -765,7 +787,7 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     };
 
     // Prologue: K(0) (waves 0-3).
-    if (!late) load_part(B0{}, 0);
+    if (!late) load_part(K, kbuf0, 0);
     __syncthreads();
     // Steps i = 0 .. ntiles (step ntiles only finishes P V); step 0 (S^T of
     // tile 0 alone) is peeled, then two steps per loop trip so that every
@@ -782,40 +804,36 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         constexpr bool LATE = decltype(latec)::value;
         // step 0
         if constexpr (!LATE) {
-            if (1 < ntiles) load_part(B1{}, 1);
+            if (1 < ntiles) load_part(K, kbuf1, 1);
             first_matrix_phase();
             vector_phase(0);
         } else {
-            load_part(B0{}, 0);
+            load_part(V, vbuf0, 0);
             first_matrix_phase();
         }
         __syncthreads();  // K(1) and V(0) have landed
         for (int i = 1; i <= ntiles; i += 2) {
             if constexpr (!LATE) {
-                if (i + 1 < ntiles) load_part(B0{}, i + 1);
-                matrix_phase(B1{}, B0{}, i);
+                matrix_phase(B1{}, B0{}, K, kbuf0, i + 1, i);
             } else {
                 vector_phase(i - 1);
             }
             if constexpr (!LATE) {
                 vector_phase(i);
             } else {
-                if (i < ntiles) load_part(B1{}, i);
-                matrix_phase(B1{}, B0{}, i);
+                matrix_phase(B1{}, B0{}, V, vbuf1, i, i);
             }
             if (i + 1 > ntiles) break;
             __syncthreads();  // K(i + 1) and V(i) have landed
             if constexpr (!LATE) {
-                if (i + 2 < ntiles) load_part(B1{}, i + 2);
-                matrix_phase(B0{}, B1{}, i + 1);
+                matrix_phase(B0{}, B1{}, K, kbuf1, i + 2, i + 1);
             } else {
                 vector_phase(i);
             }
             if constexpr (!LATE) {
                 vector_phase(i + 1);
             } else {
-                if (i + 1 < ntiles) load_part(B0{}, i + 1);
-                matrix_phase(B0{}, B1{}, i + 1);
+                matrix_phase(B0{}, B1{}, V, vbuf0, i + 1, i + 1);
             }
             __syncthreads();  // K(i + 2) and V(i + 1) have landed
         }

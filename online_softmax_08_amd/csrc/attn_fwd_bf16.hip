@@ -696,11 +696,14 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     // registers: the scores step T computes are never used (a separate P
     // V-only path for it costs more registers than the 16 products save).
     auto matrix_phase = [&](auto kbc, auto vbc, const __bf16* X, char* ldst, int kt, int i) {
-        if (i > T) {
+        if (CAUSAL && i > T) {  // without the mask every wave computes every step
             load_part(X, ldst, kt);
             return;
         }
         load_part(X, ldst, kt);
+        // Keep the loads first: issued at the end of the block they would
+        // leave no time before the barrier that waits for them.
+        __builtin_amdgcn_sched_barrier(0);
         pv(vbc);
         qk(kbc);
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads

@@ -35,9 +35,12 @@
 //  * S^T puts one query per lane (lane % 32) and 16 keys per lane in each
 //    32x32 accumulator, so the row max and row sum are in-lane reductions plus
 //    one v_permlane32_swap; the row sum is kept per lane and the halves are
-//    added once at the end.  K rows are placed in LDS so that each group of 8
-//    accumulator registers holds 8 consecutive keys: the bf16 probabilities
-//    are, register for register, the B operand of O^T += V^T P^T.
+//    added once at the end.  Lane i reads K row swap_bits23(i) of each
+//    32-key group (attn_fwd_bf16_kernel stores the rows in that order,
+//    attn_fwd_bf16_pp_kernel permutes the read address), so that each group
+//    of 8 accumulator registers holds 8 consecutive keys: the bf16
+//    probabilities are, register for register, the B operand of
+//    O^T += V^T P^T.
 //  * The V^T A operand (8 consecutive keys of one column per lane) comes from
 //    the row-major V tile through ds_read_b64_tr_b16, the gfx950 transposing
 //    LDS read: in each group of 16 lanes, lane 4a + b receives element b of

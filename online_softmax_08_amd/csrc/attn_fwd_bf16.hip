@@ -537,8 +537,9 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 // unit serves the other.  One workgroup barrier per tile step (after the
 // odd phase) keeps the groups half a step apart; it is also the only one
 // the LDS buffers need.  Tile i is read in phases 2i (waves 0-3) and 2i + 1
-// (waves 4-7); the loads of K(i + 1) and V(i) start in phase 2i and 2i + 1
-// and are waited for before the barrier that ends phase 2i + 1.
+// (waves 4-7); the loads of K(i + 1) start in phase 2i, those of V(i) in
+// phase 2i + 1 (phase 2i at D = 64), and both are waited for before the
+// barrier that ends phase 2i + 1.
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
@@ -593,7 +594,8 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     // Tile loads.  The four waves that are about to run their matrix phase
     // load one part of a tile right before it: waves 0-3 load K(i + 1) at
     // the start of phase 2i, waves 4-7 load V(i) at the start of phase
-    // 2i + 1.  Tiles sit in LDS unpadded (row pitch D elements) with their
+    // 2i + 1 (at D = 64 at the start of their vector phase 2i instead, see
+    // steps below).  Tiles sit in LDS unpadded (row pitch D elements) with their
     // 16-byte chunks permuted inside each row by an XOR with a few bits of
     // the row index, so that every LDS read below is conflict-free and a
     // part is exactly D / 8 wave loads of 1 KiB (four per wave at D = 128).
@@ -698,15 +700,19 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     // loads.  One code path for steps 1 .. T keeps the accumulators in fixed
     // registers: the scores step T computes are never used (a separate P
     // V-only path for it costs more registers than the 16 products save).
-    auto matrix_phase = [&](auto kbc, auto vbc, const __bf16* X, char* ldst, int kt, int i) {
+    auto matrix_phase = [&](auto kbc, auto vbc, auto ldc, const __bf16* X, char* ldst, int kt,
+                            int i) {
+        constexpr bool LD = decltype(ldc)::value;  // this phase issues the loads
         if (CAUSAL && i > T) {  // without the mask every wave computes every step
-            load_part(X, ldst, kt);
+            if constexpr (LD) load_part(X, ldst, kt);
             return;
         }
-        load_part(X, ldst, kt);
-        // Keep the loads first: issued at the end of the block they would
-        // leave no time before the barrier that waits for them.
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (LD) {
+            load_part(X, ldst, kt);
+            // Keep the loads first: issued at the end of the block they would
+            // leave no time before the barrier that waits for them.
+            __builtin_amdgcn_sched_barrier(0);
+        }
         pv(vbc);
         qk(kbc);
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
@@ -799,13 +805,21 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     // tile 0 alone) is peeled, then two steps per loop trip so that every
     // LDS buffer is a compile-time choice: K(i) sits in
     // kbuf[i % 2], V(i) in vbuf[i % 2].  K(i + 1) (loaded at the start of
-    // phase 2i) and V(i) (start of phase 2i + 1) are waited for at the
-    // barrier that ends phase 2i + 1.  No barrier separates phase 2i from
+    // phase 2i) and V(i) (start of phase 2i + 1, or of 2i) are waited for at
+    // the barrier that ends phase 2i + 1.  No barrier separates phase 2i from
     // 2i + 1: each buffer a phase fills was last read before the previous
     // barrier, and each buffer it reads was filled before it (measured 1-2%
     // faster than a barrier between every two phases).  The two wave groups
     // run separate copies of the loop (same barriers, phases swapped), which
     // keeps each copy's live registers to those of one phase order.
+    // Where waves 4-7 load V(i): at D = 128 at the start of their matrix
+    // phase 2i + 1; at D = 64, whose matrix phase is half as long, a load
+    // issued there has not landed by the barrier that ends the phase, so it
+    // moves to the start of their vector phase 2i (V(i)'s buffer was last
+    // read in phase 2i - 1).  Measured: +6% at D = 64 (both masks), -4% for
+    // causal D = 128.
+    using VEarly = std::integral_constant<bool, D == 64>;
+    using VInMatrix = std::integral_constant<bool, D != 64>;
     auto steps = [&](auto latec) {
         constexpr bool LATE = decltype(latec)::value;
         // step 0
@@ -820,26 +834,28 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         __syncthreads();  // K(1) and V(0) have landed
         for (int i = 1; i <= ntiles; i += 2) {
             if constexpr (!LATE) {
-                matrix_phase(B1{}, B0{}, K, kbuf0, i + 1, i);
+                matrix_phase(B1{}, B0{}, std::true_type{}, K, kbuf0, i + 1, i);
             } else {
+                if constexpr (VEarly::value) load_part(V, vbuf1, i);
                 vector_phase(i - 1);
             }
             if constexpr (!LATE) {
                 vector_phase(i);
             } else {
-                matrix_phase(B1{}, B0{}, V, vbuf1, i, i);
+                matrix_phase(B1{}, B0{}, VInMatrix{}, V, vbuf1, i, i);
             }
             if (i + 1 > ntiles) break;
             __syncthreads();  // K(i + 1) and V(i) have landed
             if constexpr (!LATE) {
-                matrix_phase(B0{}, B1{}, K, kbuf1, i + 2, i + 1);
+                matrix_phase(B0{}, B1{}, std::true_type{}, K, kbuf1, i + 2, i + 1);
             } else {
+                if constexpr (VEarly::value) load_part(V, vbuf0, i + 1);
                 vector_phase(i);
             }
             if constexpr (!LATE) {
                 vector_phase(i + 1);
             } else {
-                matrix_phase(B0{}, B1{}, V, vbuf0, i + 1, i + 1);
+                matrix_phase(B0{}, B1{}, VInMatrix{}, V, vbuf0, i + 1, i + 1);
             }
             __syncthreads();  // K(i + 2) and V(i + 1) have landed
         }

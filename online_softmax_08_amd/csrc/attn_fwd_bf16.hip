@@ -171,11 +171,15 @@ __device__ __forceinline__ char* out_stage(int wave, char* k0, char* k1, char* v
     return b + (wave & 1) * (32 * (D + 8) * 2);
 }
 
-template <int D, int QT, int NW, int BC_>
+// KS > 1 splits the key tiles of a workgroup over KS groups of NW / KS waves
+// that share the same query rows (see attn_fwd_bf16_kernel).
+template <int D, int QT, int NW, int BC_, int KS_ = 1>
 struct Cfg {
     static constexpr int BC = BC_;            // keys per tile
+    static constexpr int KS = KS_;            // key groups
+    static constexpr int NWR = NW / KS;       // waves per key group
     static constexpr int T = NW * 64;         // threads per workgroup
-    static constexpr int BR = NW * QT * 32;   // query rows per workgroup
+    static constexpr int BR = NWR * QT * 32;  // query rows per workgroup
     static constexpr int KP = D + 8;          // K row pitch in LDS (elements)
     static constexpr int VP = D + 32;         // V row pitch in LDS (elements)
     static constexpr int KCPR = KP / 8;       // 16-byte chunks per K row (last is padding)
@@ -184,10 +188,13 @@ struct Cfg {
     static constexpr int VTILE_B = BC * VP * 2;
     static constexpr int KINST = KTILE_B / 1024;  // 1 KiB wave loads per K tile
     static constexpr int VINST = VTILE_B / 1024;
-    static constexpr int KPW = (KINST + NW - 1) / NW;  // K loads issued per wave
-    static constexpr int VPW = (VINST + NW - 1) / NW;
-    static constexpr int LDS_B2 = 2 * (KTILE_B + VTILE_B);      // 2 K + 2 V buffers
+    static constexpr int KBUF_INST = KS * KINST;      // loads per K buffer (KS tiles)
+    static constexpr int VBUF_INST = KS * VINST;
+    static constexpr int KPW = (KBUF_INST + NW - 1) / NW;  // K loads issued per wave
+    static constexpr int VPW = (VBUF_INST + NW - 1) / NW;
+    static constexpr int LDS_B2 = 2 * KS * (KTILE_B + VTILE_B);  // 2 K + 2 V buffers
     static_assert(KTILE_B % 1024 == 0 && VTILE_B % 1024 == 0, "tiles are whole wave loads");
+    static_assert(NW % KS == 0, "key groups of equal size");
 };
 
 // With SPLIT the key tiles of each query block are divided into nsplit
@@ -196,7 +203,16 @@ struct Cfg {
 // opart [nsplit][BH][N][D] and the partial logsumexp to lpart [nsplit][BH][N]
 // (-inf for a row that sees no key of the range); attn_combine_kernel merges
 // them.  O and lse are then unused.
-template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL, bool SPLIT, bool VARLEN>
+//
+// With KS = 2 the workgroup's waves form two key groups over the same query
+// rows: wave w (group w / (NW / 2)) computes the even key tiles, wave
+// w + NW / 2 the odd ones, from one LDS buffer that holds both tiles of a
+// pair.  At the end the odd group hands its reference, row sums and output
+// accumulators to the even group through LDS, which merges them by the rule
+// of Lesson 22, section 22 (rescale both to the larger reference and add)
+// and writes O and lse.  A small grid then keeps twice as many waves busy,
+// each with half of the key loop, and needs no workspace.
+template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL, bool SPLIT, bool VARLEN, int KS = 1>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, __bf16* __restrict__ O,
@@ -205,21 +221,23 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const int* __restrict__ cu, int H, int Hkv, int total)
 {
     static_assert(!(SPLIT && VARLEN), "split-KV runs on dense tensors");
-    using C = Cfg<D, QT, NW, BC>;
+    static_assert(KS == 1 || (KS == 2 && !SPLIT), "key groups: two, without split-KV");
+    using C = Cfg<D, QT, NW, BC, KS>;
     static_assert(NW <= 8 && C::KTILE_B >= 2 * 32 * (D + 8) * 2, "output staging fits the tile buffers");
     constexpr int NMT = BC / 32;  // 32-key MFMA tiles per key tile
     // Four separate LDS objects (not slices of one array): the compiler can
     // then prove that the DMA filling one buffer does not alias reads of the
     // other, and does not stall those reads on the DMA's completion.
-    __shared__ __attribute__((aligned(1024))) char kbuf0[C::KTILE_B];
-    __shared__ __attribute__((aligned(1024))) char kbuf1[C::KTILE_B];
-    __shared__ __attribute__((aligned(1024))) char vbuf0[C::VTILE_B];
-    __shared__ __attribute__((aligned(1024))) char vbuf1[C::VTILE_B];
+    __shared__ __attribute__((aligned(1024))) char kbuf0[KS * C::KTILE_B];
+    __shared__ __attribute__((aligned(1024))) char kbuf1[KS * C::KTILE_B];
+    __shared__ __attribute__((aligned(1024))) char vbuf0[KS * C::VTILE_B];
+    __shared__ __attribute__((aligned(1024))) char vbuf1[KS * C::VTILE_B];
     auto kbuf = [&](auto bufc) -> char* { if constexpr (decltype(bufc)::value == 0) return kbuf0; else return kbuf1; };
     auto vbuf = [&](auto bufc) -> char* { if constexpr (decltype(bufc)::value == 0) return vbuf0; else return vbuf1; };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int rw = wave % C::NWR, kg = wave / C::NWR;            // row wave, key group
     const int j = lane & 31, h = lane >> 5;
     // Workgroup id = (t * nsplit + split) * BH + bh.
     int t, bh, split = 0;
@@ -239,7 +257,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     if (VARLEN && q0 >= N) return;  // query block past this sequence (whole workgroup)
     const size_t base = sl.base;
     const uint32_t slice_b = (uint32_t)N * D * 2;
-    const int qw0 = q0 + wave * QT * 32;  // first query row of this wave
+    const int qw0 = q0 + rw * QT * 32;  // first query row of this wave
 
     // Q as the B operand of S^T = K Q^T: lane (j, h), k-step kk holds
     // Q[row][16 kk + 8 h .. +7] of row qw0 + 32 nt + j (zero past N).
@@ -270,22 +288,26 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const float c = scale * kLog2e;
 
     // ---- HBM -> LDS tile loads (loop-invariant per-lane source offsets) ----
-    // Wave load i writes LDS chunk positions 64 i .. 64 i + 63 of a tile; the
-    // lane at position p fetches row p / CPR, column chunk p % CPR (padding
-    // chunks re-fetch the row's last real chunk).  K rows are permuted inside
-    // each 32-row group (swap_bits23); V rows keep key order.
+    // A buffer holds KS consecutive tiles, tile g at byte g * TILE_B.  Wave
+    // load i writes LDS chunk positions 64 i .. 64 i + 63 of the buffer; the
+    // lane at position p of tile g fetches row p / CPR, column chunk p % CPR
+    // (padding chunks re-fetch the row's last real chunk) of that tile.  K
+    // rows are permuted inside each 32-row group (swap_bits23); V rows keep
+    // key order.
     uint32_t ksrc[C::KPW], vsrc[C::VPW];
 #pragma unroll
     for (int u = 0; u < C::KPW; ++u) {
-        const int p = (wave + u * NW) * 64 + lane;
+        const int i = wave + u * NW, g = i / C::KINST;
+        const int p = (i - g * C::KINST) * 64 + lane;
         const int lrow = p / C::KCPR, ch = min(p % C::KCPR, D / 8 - 1);
-        const int row = (lrow & ~31) | swap_bits23(lrow & 31);
+        const int row = g * BC + ((lrow & ~31) | swap_bits23(lrow & 31));
         ksrc[u] = (uint32_t)(row * D + ch * 8) * 2;
     }
 #pragma unroll
     for (int u = 0; u < C::VPW; ++u) {
-        const int p = (wave + u * NW) * 64 + lane;
-        const int row = p / C::VCPR, ch = min(p % C::VCPR, D / 8 - 1);
+        const int i = wave + u * NW, g = i / C::VINST;
+        const int p = (i - g * C::VINST) * 64 + lane;
+        const int row = g * BC + p / C::VCPR, ch = min(p % C::VCPR, D / 8 - 1);
         vsrc[u] = (uint32_t)(row * D + ch * 8) * 2;
     }
     const __bf16* Kb = K + sl.kvbase;
@@ -297,7 +319,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
         for (int u = 0; u < C::KPW; ++u) {
             const int i = wave + u * NW;
-            if (C::KINST % NW == 0 || i < C::KINST)
+            if (C::KBUF_INST % NW == 0 || i < C::KBUF_INST)
                 lds_dma16(krs, (lds_void_t*)(kbuf(bufc) + i * 1024), ksrc[u]);
         }
     };
@@ -308,7 +330,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
         for (int u = 0; u < C::VPW; ++u) {
             const int i = wave + u * NW;
-            if (C::VINST % NW == 0 || i < C::VINST)
+            if (C::VBUF_INST % NW == 0 || i < C::VBUF_INST)
                 lds_dma16(vrs, (lds_void_t*)(vbuf(bufc) + i * 1024), vsrc[u]);
         }
     };
@@ -323,9 +345,10 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // lane group g = lane / 16 the lane 16 g + 4 e + a reads 4 columns
     // (16 (g % 2) + 4 a ..) of key row 8 (g / 2) + e (+ 4 for the second
     // read); lane i of the group then holds column 16 (g % 2) + i for 4 keys.
-    const int kread = (j * C::KP + 8 * h) * 2;
+    // Key group kg reads tile kg of each buffer.
+    const int kread = kg * C::KTILE_B + (j * C::KP + 8 * h) * 2;
     const int g16 = lane >> 4, e4 = (lane >> 2) & 3, a4 = lane & 3;
-    const int vread = ((8 * (g16 >> 1) + e4) * C::VP + 16 * (g16 & 1) + 4 * a4) * 2;
+    const int vread = kg * C::VTILE_B + ((8 * (g16 >> 1) + e4) * C::VP + 16 * (g16 & 1) + 4 * a4) * 2;
 
     // S^T = K Q^T of the K tile in LDS buffer KB, two 32-key MFMA tiles.
     auto qk = [&](auto kbc, f32x16 (&s)[NMT][QT]) {
@@ -395,9 +418,10 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     auto probs = [&](f32x16 (&s)[NMT][QT], bf16x8 (&pf)[BC / 16][QT]) {
 #pragma unroll
         for (int nt = 0; nt < QT; ++nt) {
-            // A key range of a split can lie wholly in a row's future; that
-            // row keeps m = -inf and all its p must come out 0, not NaN.
-            const float mc = (SPLIT && m[nt] == kNegInf) ? 0.f : m[nt] * c;
+            // A key range of a split, or the tiles of the odd key group, can
+            // lie wholly in a row's future; that row keeps m = -inf and all
+            // its p must come out 0, not NaN.
+            const float mc = ((SPLIT || KS > 1) && m[nt] == kNegInf) ? 0.f : m[nt] * c;
             float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) {
@@ -470,17 +494,18 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         probs(s, pf);
         pv(bufc, pf);
     };
+    // A buffer holds tiles kt .. kt + KS - 1; key group kg computes kt + kg.
     issue(B0{}, t_lo);
     __syncthreads();  // waits for the tile loads (vmcnt) before publishing
-    for (int kt = t_lo; kt < t_hi; kt += 2) {
-        // even tile: compute buffer 0 while tile kt + 1 streams into buffer 1
-        if (kt + 1 < t_hi) issue(B1{}, kt + 1);
-        compute(B0{}, kt);
+    for (int kt = t_lo; kt < t_hi; kt += 2 * KS) {
+        // compute buffer 0 while tiles kt + KS .. stream into buffer 1
+        if (kt + KS < t_hi) issue(B1{}, kt + KS);
+        compute(B0{}, kt + kg);
         __syncthreads();
-        if (kt + 1 >= t_hi) break;
-        // odd tile: compute buffer 1 while tile kt + 2 streams into buffer 0
-        if (kt + 2 < t_hi) issue(B0{}, kt + 2);
-        compute(B1{}, kt + 1);
+        if (kt + KS >= t_hi) break;
+        // compute buffer 1 while tiles kt + 2 KS .. stream into buffer 0
+        if (kt + 2 * KS < t_hi) issue(B0{}, kt + 2 * KS);
+        compute(B1{}, kt + KS + kg);
         __syncthreads();
     }
 
@@ -516,15 +541,58 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __amdgpu_buffer_rsrc_t ors = make_rsrc(O + base, slice_b);
     const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lse + sl.lbase, (uint32_t)N * 4);
     __syncthreads();  // every wave is done with the tile buffers
-    char* const ost = out_stage<D>(wave, kbuf0, kbuf1, vbuf0, vbuf1);
+    if constexpr (KS > 1) {
+        // The odd group's (m, l, acc), lane by lane, through the V buffers:
+        // row waves 0-1 use vbuf0, 2-3 vbuf1, element e of lane L of the
+        // buffer's row wave r at float (r E + e) 64 + L.  The even group
+        // includes tile 0, whose key 0 every row sees, so its m is finite;
+        // an odd group that saw no key has m = -inf and weight 0.
+        constexpr int E = QT * (2 + 16 * (D / 32));
+        static_assert(C::NWR <= 4 && 2 * E * 64 * 4 <= KS * C::VTILE_B, "exchange fits the V buffers");
+        float* const xch = reinterpret_cast<float*>(rw < 2 ? vbuf0 : vbuf1) + (rw & 1) * E * 64 + lane;
+        if (kg == 1) {
 #pragma unroll
-    for (int nt = 0; nt < QT; ++nt) {
-        const float l_tot = combine_xor32(l[nt], SumOp());
-        const float inv = 1.0f / l_tot;
-        store_tile_rows<D>(acc[nt], inv, ost, ors, qw0 + nt * 32, lane);
-        if (h == 0)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m[nt] * scale + logf(l_tot)), lrs,
-                                                  (uint32_t)(qw0 + nt * 32 + j) * 4, 0, 0);
+            for (int nt = 0; nt < QT; ++nt) {
+                float* const x = xch + nt * (2 + 16 * (D / 32)) * 64;
+                x[0] = m[nt];
+                x[64] = l[nt];
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) x[(2 + 16 * dt + r) * 64] = acc[nt][dt][r];
+            }
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+            for (int nt = 0; nt < QT; ++nt) {
+                const float* const x = xch + nt * (2 + 16 * (D / 32)) * 64;
+                const float m1 = x[0];
+                const float m_new = fmaxf(m[nt], m1);
+                const float a0 = exp2_hw((m[nt] - m_new) * c);
+                const float a1 = exp2_hw((m1 - m_new) * c);  // 0 for m1 = -inf
+                l[nt] = a0 * l[nt] + a1 * x[64];
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[nt][dt][r] = a0 * acc[nt][dt][r] + a1 * x[(2 + 16 * dt + r) * 64];
+                m[nt] = m_new;
+            }
+        }
+        __syncthreads();  // the exchange area is read before the output staging
+    }
+    if (kg == 0) {
+        char* const ost = out_stage<D>(rw, kbuf0, kbuf1, vbuf0, vbuf1);
+#pragma unroll
+        for (int nt = 0; nt < QT; ++nt) {
+            const float l_tot = combine_xor32(l[nt], SumOp());
+            const float inv = 1.0f / l_tot;
+            store_tile_rows<D>(acc[nt], inv, ost, ors, qw0 + nt * 32, lane);
+            if (h == 0)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m[nt] * scale + logf(l_tot)), lrs,
+                                                      (uint32_t)(qw0 + nt * 32 + j) * 4, 0, 0);
+        }
     }
 }
 
@@ -891,26 +959,32 @@ hipError_t launch_pp(const void* Q, const void* K, const void* V, void* O, float
     return hipGetLastError();
 }
 
-template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL, bool VARLEN>
+template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL, bool VARLEN, int KS = 1>
 hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
                   int N, float scale, const int* cu, int H, int Hkv, int total,
                   hipStream_t stream)
 {
-    using C = Cfg<D, QT, NW, BC>;
+    using C = Cfg<D, QT, NW, BC, KS>;
     const int nqt = (N + C::BR - 1) / C::BR;
     const dim3 grid((unsigned)(nqt * BH)), block(C::T);
-    attn_fwd_bf16_kernel<D, QT, NW, WPE, BC, CAUSAL, false, VARLEN><<<grid, block, 0, stream>>>(
+    attn_fwd_bf16_kernel<D, QT, NW, WPE, BC, CAUSAL, false, VARLEN, KS><<<grid, block, 0, stream>>>(
         static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
         static_cast<__bf16*>(O), lse, N, BH, nqt, scale, nullptr, nullptr, 1, cu, H, Hkv, total);
     return hipGetLastError();
 }
 
 // Workgroups of 8 waves x 32 query rows (two waves per SIMD), 64-key tiles,
-// while that still gives one workgroup per CU (256) or more; smaller problems
-// use workgroups of 4 or 2 waves so that the grid still covers the chip.
-// With 8 waves the phase-staggered kernel serves both masks (without the mask
-// it measures 2-4% faster than the plain kernel, which still serves the
-// smaller grids and the split-KV partial pass).
+// while that still gives one workgroup per CU (256) or more; the
+// phase-staggered kernel serves them for both masks (without the mask it
+// measures 2-4% faster than the plain kernel).  Smaller problems use the
+// plain kernel with 128-row workgroups, then 64-row ones:
+//  * 128 rows: 4 waves without the mask (two such workgroups fit a CU);
+//    under the causal mask 8 waves in two key groups (+7% at d = 128, +20%
+//    at d = 64 on [1, 16, 2048..3000, d]; the same costs 10% unmasked);
+//  * 64 rows: 4 waves in two key groups rather than 2 waves with the whole
+//    key loop (+21-47% on [2, 8, 1024, 64], [1, 8, 2048, 128],
+//    [1, 2, 8192, 128]).
+// The plain kernel also runs the split-KV partial pass.
 template <int D, bool CAUSAL, bool VARLEN = false>
 hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
                     int N, float scale, hipStream_t stream, int H = 1, int Hkv = 1,
@@ -920,9 +994,13 @@ hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float*
     if ((long long)((N + 255) / 256) * BH >= kCUs) {
         return launch_pp<D, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
     }
-    if ((long long)((N + 127) / 128) * BH >= kCUs)
-        return launch<D, 1, 4, 2, 64, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
-    return launch<D, 1, 2, 2, 64, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
+    if ((long long)((N + 127) / 128) * BH >= kCUs) {
+        if constexpr (CAUSAL)
+            return launch<D, 1, 8, 2, 64, CAUSAL, VARLEN, 2>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
+        else
+            return launch<D, 1, 4, 2, 64, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
+    }
+    return launch<D, 1, 4, 2, 64, CAUSAL, VARLEN, 2>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
 }
 
 // Merge of split partials, one row per D / 4 lanes (four fp32 columns per

@@ -210,13 +210,15 @@ def test_attn_deterministic(osm):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("shape", [(2, 8, 2048, 64), (2, 16, 2048, 64), (2, 8, 4096, 128),
-                                   (1, 2, 4096, 128)])
+@pytest.mark.parametrize("shape", [(2, 8, 2048, 64), (1, 16, 2048, 128), (1, 16, 3000, 64),
+                                   (2, 16, 2048, 64), (2, 8, 4096, 128), (1, 2, 4096, 128)])
 def test_attn_workgroup_sizes(osm, shape, causal):
-    # The launch uses workgroups of 2, 4 or 8 waves depending on how many
-    # it takes to cover the chip; these shapes reach the 4-wave size (first),
-    # the 8-wave kernels at d = 64 and d = 128 (second and third) and the
-    # 2-wave size at long N (last) for both masks.  Sampled rows against the
+    # The launch picks the workgroup shape from how many it takes to cover
+    # the chip; these shapes reach the 128-row workgroups (4 waves unmasked,
+    # 8 waves in two key groups under the causal mask) at d = 64 and d = 128
+    # and with a ragged N (first three), the phase-staggered 8-wave kernel at
+    # d = 64 and d = 128 (next two) and the 64-row workgroups of two key
+    # groups at long N (last), for both masks.  Sampled rows against the
     # oracle, every row finite.
     B, H, N, d = shape
     base = inputs.ATTN["attn_bf16_B2H8N1024d64" if d == 64 else "attn_bf16_B4H16N2048d128"]

@@ -1090,11 +1090,12 @@ int attn_splitkv_auto(int BH, int N, int d, bool causal)
     // SIMD busy.  Below that, split the keys so that the partial pass reaches
     // 2048 waves, twice that under the causal mask (its query blocks differ
     // in length, and more, shorter ranges even them out), with at least 512
-    // keys per range.  Rows shorter than 2048 keys are not split: there the
-    // fp32 partials cost as much HBM time as the occupancy gains.
+    // keys per range.  Rows of 2048 keys or fewer are not split: there the
+    // fp32 partials cost as much HBM time as the occupancy gains (and the
+    // single pass already splits the key loop over two wave groups).
     (void)d;
     const long long rows = (long long)BH * N;
-    if (N < 2048 || rows >= 65536) return 1;
+    if (N <= 2048 || rows >= 65536) return 1;
     long long s = (65536 * (causal ? 2 : 1) + rows - 1) / rows;
     const long long cap = N / 512;
     if (s > cap) s = cap;

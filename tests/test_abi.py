@@ -120,9 +120,10 @@ def test_splitkv_plan(abi):
     assert abi.attn_fwd_splitkv_plan(1, 2, 8192, 128, True, 0)[0] == 8
     assert abi.attn_fwd_splitkv_plan(1, 1, 32768, 64, False, 0)[0] == 2
     assert abi.attn_fwd_splitkv_plan(1, 1, 32768, 64, True, 0)[0] == 4
-    assert abi.attn_fwd_splitkv_plan(1, 8, 2048, 128, True, 0)[0] == 4
+    assert abi.attn_fwd_splitkv_plan(1, 4, 4096, 128, False, 0)[0] == 4
     assert abi.attn_fwd_splitkv_plan(1, 1, 65536, 64, True, 0) == (1, 0)
-    # ... and none for rows under 2048 keys or empty problems.
+    # ... and none for rows of 2048 keys or fewer, or empty problems.
+    assert abi.attn_fwd_splitkv_plan(1, 8, 2048, 128, True, 0) == (1, 0)
     assert abi.attn_fwd_splitkv_plan(1, 1, 256, 64, False, 0) == (1, 0)
     assert abi.attn_fwd_splitkv_plan(2, 8, 1024, 64, False, 0) == (1, 0)
     assert abi.attn_fwd_splitkv_plan(0, 4, 4096, 64, False, 0) == (1, 0)

@@ -70,8 +70,9 @@
 //  * Two schedules share these pieces.  attn_fwd_bf16_kernel runs each tile
 //    as S^T, softmax, P V in every wave; the two waves of a SIMD then mostly
 //    use the matrix core and the vector unit at the same time and wait for
-//    each other.  It serves the grids of 4- and 2-wave workgroups and the
-//    split-KV partial pass.  attn_fwd_bf16_pp_kernel (8-wave workgroups, both
+//    each other.  It serves the smaller grids (128- and 64-row workgroups
+//    whose key loop is split over two wave groups) and the split-KV partial
+//    pass.  attn_fwd_bf16_pp_kernel (8-wave workgroups of 256 rows, both
 //    masks) staggers the two waves of each SIMD by half a tile step, so that
 //    one issues only MFMAs while the other runs the softmax.
 //  * The output tile of each wave leaves through LDS as whole rows
@@ -973,17 +974,21 @@ hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* l
     return hipGetLastError();
 }
 
-// Workgroups of 8 waves x 32 query rows (two waves per SIMD), 64-key tiles,
-// while that still gives one workgroup per CU (256) or more; the
-// phase-staggered kernel serves them for both masks (without the mask it
-// measures 2-4% faster than the plain kernel).  Smaller problems use the
-// plain kernel with 128-row workgroups, then 64-row ones:
-//  * 128 rows: 4 waves without the mask (two such workgroups fit a CU);
-//    under the causal mask 8 waves in two key groups (+7% at d = 128, +20%
-//    at d = 64 on [1, 16, 2048..3000, d]; the same costs 10% unmasked);
-//  * 64 rows: 4 waves in two key groups rather than 2 waves with the whole
-//    key loop (+21-47% on [2, 8, 1024, 64], [1, 8, 2048, 128],
-//    [1, 2, 8192, 128]).
+// Launch shape, from the number of 256-row (W256) and 128-row (W128) query
+// blocks against the 256 CUs (measured over [1..2, 6..32, 1024..4096, d]):
+//  * the phase-staggered kernel (8 waves x 32 rows, one workgroup per CU at
+//    a time) when W256 > 256, and without the mask already when W128 > 256:
+//    unmasked, it beats the plain kernel even with 160-192 workgroups (+11%
+//    to +15% on [1, 10..24, 2048..4096, 128]), while under the causal mask
+//    one round of unequal blocks leaves CUs idle ([1, 32, 2048, 64] causal:
+//    396 against 468 TFLOPS with key groups);
+//  * otherwise the plain kernel with 128-row workgroups of 8 waves in two
+//    key groups, as long as that fills the CUs (W128 >= 256 under the causal
+//    mask, W128 > 128 without it: +4-10% over 4 waves with the whole key
+//    loop, +6-20% causal);
+//  * below that 64-row workgroups of 4 waves in two key groups (+21-47%
+//    over 2 waves with the whole key loop on [2, 8, 1024, 64],
+//    [1, 8, 2048, 128] and [1, 2, 8192, 128]).
 // The plain kernel also runs the split-KV partial pass.
 template <int D, bool CAUSAL, bool VARLEN = false>
 hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
@@ -991,15 +996,12 @@ hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float*
                     const int* cu = nullptr, int total = 0)
 {
     constexpr long long kCUs = 256;
-    if ((long long)((N + 255) / 256) * BH >= kCUs) {
+    const long long w256 = (long long)((N + 255) / 256) * BH;
+    const long long w128 = (long long)((N + 127) / 128) * BH;
+    if (w256 > kCUs || (!CAUSAL && w128 > kCUs))
         return launch_pp<D, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
-    }
-    if ((long long)((N + 127) / 128) * BH >= kCUs) {
-        if constexpr (CAUSAL)
-            return launch<D, 1, 8, 2, 64, CAUSAL, VARLEN, 2>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
-        else
-            return launch<D, 1, 4, 2, 64, CAUSAL, VARLEN>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
-    }
+    if (CAUSAL ? w128 >= kCUs : w128 > kCUs / 2)
+        return launch<D, 1, 8, 2, 64, CAUSAL, VARLEN, 2>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
     return launch<D, 1, 4, 2, 64, CAUSAL, VARLEN, 2>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
 }
 

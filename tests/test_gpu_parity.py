@@ -151,7 +151,8 @@ def test_attn_rescale_stress(osm):
 
 def test_attn_rescale_stress_full_grid(osm):
     # Scores built to move the exponent reference in every way, on a grid
-    # large enough for the 8-wave kernels (256 query blocks of 256 rows).
+    # large enough for the phase-staggered kernel under both masks (512
+    # query blocks of 256 rows).
     # Eight kinds of head (score = q_0 k_0 plus small noise): keys rising by
     # 12, 2 or 0.16 (log2 units) per 64-key tile, rising by 13 per tile for
     # queries boosted x16, falling scores, and jumps of ~150 log2 units in
@@ -159,7 +160,7 @@ def test_attn_rescale_stress_full_grid(osm):
     # overflows against the old reference and must be recomputed.  Scaled
     # scores stay below ~150 so that fp32 resolves lse to 1e-3.  Every row of
     # the eight head kinds is compared with the oracle.
-    B, H, N, d = 1, 64, 1024, 128
+    B, H, N, d = 1, 128, 1024, 128
     j = torch.arange(N, dtype=torch.float32)
     kind = [1.5 * j, 0.25 * j, 0.1 * j, 1200.0 * (j >= 300), 1200.0 * (j >= 512), -0.5 * j,
             0.02 * j, 400.0 * (j >= 200) + 800.0 * (j >= 700)]
@@ -173,7 +174,7 @@ def test_attn_rescale_stress_full_grid(osm):
         k[0, h, :, 0] = kind[h % 8]
     q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
     scale = 1.0 / math.sqrt(d)
-    heads = list(range(8)) + [45, 63]
+    heads = list(range(8)) + [45, 127]
     bh = np.repeat(np.array(heads), N)
     qi = np.tile(np.arange(N), len(heads))
     for causal in (False, True):
@@ -214,12 +215,12 @@ def test_attn_deterministic(osm):
                                    (2, 16, 2048, 64), (2, 8, 4096, 128), (1, 2, 4096, 128)])
 def test_attn_workgroup_sizes(osm, shape, causal):
     # The launch picks the workgroup shape from how many it takes to cover
-    # the chip; these shapes reach the 128-row workgroups (4 waves unmasked,
-    # 8 waves in two key groups under the causal mask) at d = 64 and d = 128
-    # and with a ragged N (first three), the phase-staggered 8-wave kernel at
-    # d = 64 and d = 128 (next two) and the 64-row workgroups of two key
-    # groups at long N (last), for both masks.  Sampled rows against the
-    # oracle, every row finite.
+    # the chip.  The 128-row workgroups of two key groups run (1, 16, 2048,
+    # 128) and (2, 8, 2048, 64) under both masks, and the other shapes but
+    # the last under the causal mask; the phase-staggered kernel runs those
+    # without the mask (d = 64 and 128, ragged N = 3000); the 64-row
+    # workgroups of two key groups run the last, at long N, for both masks.
+    # Sampled rows against the oracle, every row finite.
     B, H, N, d = shape
     base = inputs.ATTN["attn_bf16_B2H8N1024d64" if d == 64 else "attn_bf16_B4H16N2048d128"]
     q, k, v = inputs.attn_inputs(base, B=B, H=H, N=N, d=d, seed=base.seed + 7 * N + d)

@@ -838,16 +838,18 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
                 }
             return (ps[0] + ps[1]) + (ps[2] + ps[3]);
         };
-        float lsum = probs(m * c);
+        // Every row of the wave starts at tile 0 with m = -inf: there the
+        // probabilities against m would be inf or NaN, so tile 0 goes
+        // straight to the reference move below.
+        float lsum = i == 0 ? 0.f : probs(m * c);
         // No p exceeds its lane's sum, so while every lane's sum stays within
         // kSumLimit the reference can stay where it is: the tile needs no row
-        // maximum at all.  Otherwise, and on a row's first tile (m = -inf,
-        // where the probabilities above are inf or NaN), the reference moves
-        // to the row maximum, l and the accumulators are rescaled by
+        // maximum at all.  Otherwise, and on tile 0, the reference moves to
+        // the row maximum, l and the accumulators are rescaled by
         // 2^((m_old - m_new) c) (0 for an empty history), and the tile's
-        // probabilities are recomputed.  Tile 0 holds key 0, visible to every
-        // row, so the new reference is finite.
-        if (__builtin_amdgcn_ballot_w64(m == kNegInf || lsum > kSumLimit) != 0) {
+        // probabilities are (re)computed.  Tile 0 holds key 0, visible to
+        // every row, so the new reference is finite.
+        if (i == 0 || __builtin_amdgcn_ballot_w64(lsum > kSumLimit) != 0) {
             float v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[u] = fmaxf(s[0][u], s[0][u + 4]);

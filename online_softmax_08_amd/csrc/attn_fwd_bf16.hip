@@ -423,14 +423,17 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             // lie wholly in a row's future; that row keeps m = -inf and all
             // its p must come out 0, not NaN.
             const float mc = ((SPLIT || KS > 1) && m[nt] == kNegInf) ? 0.f : m[nt] * c;
-            float ps[4] = {0.f, 0.f, 0.f, 0.f};
+            float ps[4];  // four partial sums, seeded by the first four p
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float p = exp2_hw(fmaf(s[mt][nt][r], c, -mc));
                     s[mt][nt][r] = p;
-                    ps[r & 3] += p;
+                    if (mt == 0 && r < 4)
+                        ps[r] = p;
+                    else
+                        ps[r & 3] += p;
                 }
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
@@ -823,7 +826,7 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         // v_exp_f32 each), their bf16 copies (the B operand of P V) and this
         // lane's partial row sum.  s keeps the scores for a recomputation.
         auto probs = [&](float mc) {
-            float ps[4] = {0.f, 0.f, 0.f, 0.f};
+            float ps[4];  // four partial sums, seeded by the first four p
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -832,7 +835,10 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 #pragma unroll
                     for (int r8 = 0; r8 < 8; ++r8) {
                         p8[r8] = exp2_hw(fmaf(s[mt][8 * half + r8], c, -mc));
-                        ps[r8 & 3] += p8[r8];
+                        if (mt == 0 && half == 0 && r8 < 4)
+                            ps[r8] = p8[r8];
+                        else
+                            ps[r8 & 3] += p8[r8];
                     }
                     pf[2 * mt + half] = __builtin_convertvector(p8, bf16x8);
                 }

@@ -51,9 +51,11 @@ int check_attn_shape(int B, int H, int N, int d, float scale, size_t elem)
     if (B == 0 || H == 0 || N == 0) return OSM_OK;
     const long long bh = (long long)B * H;
     // Work-group ids (bh * query blocks of at least 128 rows) and row indices
-    // must fit in 32 bits, a dispatch counts at most 2^32 - 1 work-items (every
-    // launch here has at most two per row, rounded up to 256-row blocks), and
-    // the bytes of one (b, h) slice are a 32-bit buffer offset.
+    // must fit in 32 bits, a dispatch counts at most 2^32 - 1 work-items (the
+    // launch of every grid above 65,536 rows has two per row, rounded up to
+    // 256-row blocks; the smaller grids, with up to four per row in 64- or
+    // 128-row blocks, stay far below), and the bytes of one (b, h) slice are
+    // a 32-bit buffer offset.
     if (bh > INT_MAX || bh * ((N + 127) / 128) > INT_MAX) return OSM_ERR_SIZE;
     if (bh * ((N + 255) / 256) * 512 > UINT32_MAX || (long long)N * d * (long long)elem > UINT32_MAX)
         return OSM_ERR_SIZE;

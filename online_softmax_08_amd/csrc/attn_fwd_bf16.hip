@@ -766,12 +766,10 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 
 
     // Matrix phase of step i (1 <= i <= T): the wave's tile loads (tile kt
-    // of X into ldst), P V of tile i - 1, then S^T of tile i, as one block
-    // whose LDS reads the scheduler keeps several MFMAs ahead of their use
-    // (48 reads feed 32 MFMAs).  A wave past its last tile (i > T) only
-    // loads.  One code path for steps 1 .. T keeps the accumulators in fixed
-    // registers (a separate P V-only path for step T costs more registers
-    // than the 16 products save).
+    // of X into ldst), P V of tile i - 1, then S^T of tile i (skipped at
+    // step T), with the LDS reads of each scheduled several MFMAs ahead of
+    // their use.  A wave past its last tile (i > T) only loads.  One code
+    // path for steps 1 .. T keeps the accumulators in fixed registers.
     auto matrix_phase = [&](auto kbc, auto vbc, auto ldc, const __bf16* X, char* ldst, int kt,
                             int i) {
         constexpr bool LD = decltype(ldc)::value;  // this phase issues the loads
@@ -785,19 +783,28 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
             // leave no time before the barrier that waits for them.
             __builtin_amdgcn_sched_barrier(0);
         }
+        // P V, then S^T unless this is step T, whose scores are never used.
+        // Each block gets its own pipeline: a few LDS reads ahead, then one
+        // MFMA per one or two reads (P V: 2 reads per product, S^T: 1).
+        constexpr int NPV = 4 * (D / 32), NQK = 2 * (D / 16);
         pv(vbc);
-        // Step T's scores are never used.  Without the mask (T = ntiles for
-        // every wave) skipping them pays (+1.5-4% at D = 128, and the split
-        // block needs 210 instead of 230 VGPRs); under the mask the branch
-        // costs 3%, so the causal kernel computes and drops them.
-        if (CAUSAL || i < T) qk(kbc);
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
 #pragma unroll
-        for (int u = 0; u < 20; ++u) {
+        for (int u = 0; u < NPV - 4; ++u) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        if (i < T) {
+            qk(kbc);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int u = 0; u < NQK - 4; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
     };
     // Step 0 has no probabilities yet: its matrix phase is S^T of tile 0.
     auto first_matrix_phase = [&]() {

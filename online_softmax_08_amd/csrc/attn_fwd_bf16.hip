@@ -489,14 +489,37 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // later tiles of the workgroup lie wholly in this wave's future).
     const int wt = CAUSAL ? min(t_hi, (qw0 + QT * 32 - 1) / BC + 1) : t_hi;
 
+    // One tile: S^T, statistics and probabilities, P V.  The two products
+    // get scheduling pipelines that keep their LDS operand reads four
+    // products ahead (neutral to +4% on the grids this kernel serves).
     auto compute = [&](auto bufc, int kt) {
         if (kt >= wt) return;
         f32x16 s[NMT][QT];
         qk(bufc, s);
+        {
+            constexpr int NR = (D / 16) * NMT;  // K reads, QT products each
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS reads
+#pragma unroll
+            for (int u = 0; u < NR - 4; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, QT, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * QT, 0);
+        }
         stats(s, kt * BC);
         bf16x8 pf[BC / 16][QT];
         probs(s, pf);
         pv(bufc, pf);
+        {
+            constexpr int NV = (BC / 16) * (D / 32);  // V operands, 2 reads each
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int u = 0; u < NV - 4; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, QT, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * QT, 0);
+        }
     };
     // A buffer holds tiles kt .. kt + KS - 1; key group kg computes kt + kg.
     issue(B0{}, t_lo);

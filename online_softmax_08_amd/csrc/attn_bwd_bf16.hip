@@ -504,6 +504,18 @@ attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 s[mt] = mfma(rows_a<TK::P>(kt_l, 32 * mt, 16 * kk, j, h), qf[kk], s[mt]);
                 dp[mt] = mfma(rows_a<TK::P>(vt_l, 32 * mt, 16 * kk, j, h), gf[kk], dp[mt]);
             }
+        // Scheduling pipelines for this block and for dQ below keep the LDS
+        // operand reads four products ahead (+2% on the backward).
+        {
+            constexpr int NM = 4 * (D / 16);  // products, one LDS read each
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int u = 0; u < NM - 4; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
         // Register r of half h of tile mt holds key kv0 + 32 mt + 16 (r / 8) + 8 h + r % 8.
         const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
         bf16x8 sb[BC / 16];
@@ -527,6 +539,16 @@ attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
                 acc[dt] = mfma(cols_a<TK::P>(kt_l, 16 * ks, 32 * dt, lane), sb[ks], acc[dt]);
+        {
+            constexpr int NM = (BC / 16) * (D / 32);  // products, two LDS reads each
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int u = 0; u < NM - 4; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
     };
 
     using B0 = std::integral_constant<int, 0>;

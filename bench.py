@@ -14,17 +14,22 @@ before it settles.
 
 Prints one JSON line:
   value             attention TFLOPS, counted FLOPs 4*B*H*N^2*d / 2 (causal)
-                    over the mean attention launch time
+                    over the mean attention launch time (median and fastest
+                    launch beside it)
   roofline          attention kernel against the bf16 matrix-core peak
   softmax           row-softmax GB/s (8 algorithmic bytes per element)
   roofline_softmax  softmax kernel against the HBM peak
   cpu_baseline      the fp64 oracle on the host cores, on a bounded sample
                     of the same workload (and its parity on that sample)
-  supplementary     measured after the timed region: the attention shape
-                    without the mask, a plain device copy of the softmax
-                    input as the practical HBM ceiling, the split-KV
-                    forward beside the single pass on long rows / few heads,
-                    packed variable-length sequences beside padding, and the
+  device            GPU name, architecture, compute units, peak engine clock
+  supplementary     measured after the timed region: every other attention
+                    workload (fp32 [1,1,128,64], bf16 [2,8,1024,64],
+                    [4,16,2048,128], causal [1,32,8192,128]) with mean,
+                    median and fastest launch, the headline shape without
+                    the mask, a plain device copy of the softmax input as the
+                    practical HBM ceiling, the split-KV forward beside the
+                    single pass on long rows / few heads, packed
+                    variable-length sequences beside padding, and the
                     backward pass of the headline workload
 """
 from __future__ import annotations
@@ -43,6 +48,7 @@ if ROOT not in sys.path:
 METRIC = "attn fwd TFLOPS & % bf16 MFMA peak (B·H=32,N=4096,d=128); softmax GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix-core peak
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -58,6 +64,31 @@ ATTN_SOURCES = ["online_softmax_08_amd/csrc/attn_fwd_bf16.hip",
                 "online_softmax_08_amd/csrc/device_common.h"]
 SOFTMAX_SOURCES = ["online_softmax_08_amd/csrc/row_softmax.hip",
                    "online_softmax_08_amd/csrc/device_common.h"]
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def device_info(torch) -> dict:
+    """Name, architecture, compute-unit count and peak engine clock of the GPU
+    the run used, from the HIP device attributes."""
+    import ctypes
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
+            "max_sclk_mhz": None}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate (peak clock in kHz) is entry 5 of
+        # hipDeviceAttribute_t in hip_runtime_api.h.
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, torch.cuda.current_device()) == 0:
+            info["max_sclk_mhz"] = val.value // 1000
+    except OSError:
+        pass
+    return info
 
 
 def measured_traffic(tag: str, sources) -> float | None:
@@ -145,8 +176,9 @@ def main() -> int:
             cdst.copy_(csrc)
         torch.cuda.synchronize()
 
-    attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    sm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    attn_t = [e[0].elapsed_time(e[1]) for e in ev]
+    sm_t = [e[1].elapsed_time(e[2]) for e in ev]
+    attn_ms, sm_ms = sum(attn_t) / K, sum(sm_t) / K
     attn_tflops = wa.flops / (attn_ms * 1e-3) / 1e12
     sm_gbs = ws.bytes / (sm_ms * 1e-3) / 1e9
     # Algorithmic HBM bytes of the attention kernel: Q, K, V read once, O and
@@ -176,8 +208,13 @@ def main() -> int:
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_attn,
                      "kernel": "attn_fwd_bf16_pp_kernel", "kernel_ms": round(attn_ms, 4),
+                     "kernel_ms_median": round(median(attn_t), 4),
+                     "kernel_ms_min": round(min(attn_t), 4),
                      "flops_per_launch": wa.flops, "algorithmic_bytes": attn_bytes},
-        "softmax": {"value": round(sm_gbs, 1), "unit": "GB/s", "kernel_ms": round(sm_ms, 4)},
+        "softmax": {"value": round(sm_gbs, 1), "unit": "GB/s", "kernel_ms": round(sm_ms, 4),
+                    "kernel_ms_median": round(median(sm_t), 4),
+                    "kernel_ms_min": round(min(sm_t), 4)},
+        "device": device_info(torch),
         "roofline_softmax": {"bound": "hbm", "achieved": round(sm_gbs, 1), "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": round(sm_gbs / PEAK_HBM_GBS, 4),
                              "traffic": traffic_sm, "kernel": "softmax_block_vec4",
@@ -204,7 +241,7 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10):
 
     from online_softmax_08_amd import inputs
 
-    def per_launch_ms(fn):
+    def launch_times(fn):
         for _ in range(warm):
             fn()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -215,7 +252,33 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10):
             fn()
             b.record()
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in ev) / reps
+        return [a.elapsed_time(b) for a, b in ev]
+
+    def per_launch_ms(fn):
+        t = launch_times(fn)
+        return sum(t) / len(t)
+
+    # Every attention workload of the parity suite at its own size (the
+    # causal N = 4096 one is the timed headline above), each as its own
+    # sequence of launches: counted FLOPs over the mean, median and fastest
+    # launch, against the matrix-core peak of its arithmetic type.
+    configs = {}
+    for name, w in inputs.ATTN.items():
+        if name == wa.name:
+            continue
+        qc, kc, vc = (t.to(q.device) for t in inputs.attn_inputs(w))
+        Oc = torch.empty_like(qc)
+        lc = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+        t = launch_times(lambda: osm.attention(qc, kc, vc, causal=w.causal, out=Oc, lse=lc))
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+        tf = w.flops / (median(t) * 1e-3) / 1e12
+        configs[name] = {"shape": [w.B, w.H, w.N, w.d], "causal": w.causal, "dtype": w.dtype,
+                         "tflops_median": round(tf, 2),
+                         "tflops_mean": round(w.flops / (sum(t) / len(t) * 1e-3) / 1e12, 2),
+                         "frac_median": round(tf / peak, 4), "peak_tflops": peak,
+                         "ms_median": round(median(t), 4), "ms_min": round(min(t), 4),
+                         "ms_mean": round(sum(t) / len(t), 4)}
+        del qc, kc, vc, Oc, lc
 
     O2 = torch.empty_like(q)
     lse2 = torch.empty((wa.B, wa.H, wa.N), dtype=torch.float32, device=q.device)
@@ -279,6 +342,7 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10):
                      "kernel_ms": round(cp_ms, 4)},
         "attn_splitkv": split,
         "attn_varlen": varlen,
+        "attn_configs": configs,
     }
 
 

@@ -83,9 +83,11 @@ typedef enum {
     OSM_ERR_HEAD_DIM = 3, /* d is not 64 or 128                                */
     OSM_ERR_SCALE = 4,    /* scale is not finite and > 0                       */
     OSM_ERR_ALIAS = 5,    /* an output overlaps an input or the other output   */
-    OSM_ERR_ALIGN = 6,    /* a pointer is not aligned as required              */
-    OSM_ERR_DEVICE = 7,   /* the current device is not a gfx950 GPU            */
-    OSM_ERR_HIP = 8,      /* the HIP runtime reported an error at launch       */
+    OSM_ERR_HIP = 6,      /* the HIP runtime reported an error at launch       */
+    /* Codes added after the first seven for the checks the later entry points
+     * and the device guard make: */
+    OSM_ERR_ALIGN = 7,    /* a pointer is not aligned as required              */
+    OSM_ERR_DEVICE = 8,   /* the current device is not a gfx950 GPU            */
     OSM_ERR_SPLITS = 9,   /* a split count is outside its documented range     */
     OSM_ERR_WORKSPACE = 10, /* workspace_bytes is below what the call requires */
     OSM_ERR_HEADS = 11     /* Hkv is not a divisor of H in 1 .. H               */

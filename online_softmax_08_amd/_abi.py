@@ -65,9 +65,9 @@ OSM_ERR_SIZE = 2
 OSM_ERR_HEAD_DIM = 3
 OSM_ERR_SCALE = 4
 OSM_ERR_ALIAS = 5
-OSM_ERR_ALIGN = 6
-OSM_ERR_DEVICE = 7
-OSM_ERR_HIP = 8
+OSM_ERR_HIP = 6
+OSM_ERR_ALIGN = 7
+OSM_ERR_DEVICE = 8
 OSM_ERR_SPLITS = 9
 OSM_ERR_WORKSPACE = 10
 OSM_ERR_HEADS = 11

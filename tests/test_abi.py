@@ -39,6 +39,29 @@ def test_library_exports_every_declared_symbol(abi):
     assert set(abi.EXPORTS) == set(_declared_functions())
 
 
+def _header_status_codes():
+    # name -> value as include/osm.h declares them
+    import re
+    with open(os.path.join(ROOT, "include", "osm.h")) as f:
+        text = f.read()
+    body = text[text.index("typedef enum {"):text.index("} osm_status;")]
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"(OSM_[A-Z_]+)\s*=\s*(\d+)", body)}
+
+
+def test_status_code_numbering(abi):
+    # The first seven codes keep the numbering of the interface as first
+    # specified (a caller written against it reads the same meaning); the
+    # later checks are appended after them.  The binding mirrors the header.
+    codes = _header_status_codes()
+    assert codes == {"OSM_OK": 0, "OSM_ERR_NULL": 1, "OSM_ERR_SIZE": 2, "OSM_ERR_HEAD_DIM": 3,
+                     "OSM_ERR_SCALE": 4, "OSM_ERR_ALIAS": 5, "OSM_ERR_HIP": 6, "OSM_ERR_ALIGN": 7,
+                     "OSM_ERR_DEVICE": 8, "OSM_ERR_SPLITS": 9, "OSM_ERR_WORKSPACE": 10,
+                     "OSM_ERR_HEADS": 11}
+    for name, value in codes.items():
+        assert getattr(abi, name) == value, name
+    assert "runtime" in abi.osm_status_str(6) and "aligned" in abi.osm_status_str(7)
+
+
 def test_status_strings(abi):
     for st in range(0, 12):
         assert abi.osm_status_str(st) and abi.osm_status_str(st) != "unknown status"

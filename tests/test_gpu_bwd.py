@@ -104,6 +104,27 @@ def test_bwd_headline_shape_sampled_slices(osm):
         _compare([x[sl] for x in got], ref, f"slice ({b}, {hh})")
 
 
+@pytest.mark.parametrize("case", [((1, 16, 2048, 64), False), ((1, 16, 2048, 64), True),
+                                  ((1, 16, 2048, 128), False), ((1, 16, 2048, 128), True),
+                                  ((2, 16, 2048, 64), False), ((2, 16, 2048, 128), False)])
+def test_bwd_workgroup_sizes(osm, case):
+    # The launch picks 8-, 4- or 2-wave workgroups for the dK/dV and dQ
+    # kernels from how many it takes to cover the chip: [1, 16, 2048, d]
+    # runs 4-wave workgroups (under both masks and at both head sizes),
+    # [2, 16, 2048, d] unmasked 8-wave ones.  The whole GPU problem, four
+    # whole (b, h) slices recomputed by the oracle.
+    (B, H, N, d), causal = case
+    q, k, v, g = _case(B, H, N, d, seed=6000 + B * 7 + d)
+    label = f"bwd B{B}H{H}N{N}d{d} causal={causal}"
+    print(label, flush=True)
+    got = _gpu_bwd(osm, q, k, v, g, causal)
+    for bh in (0, 5, B * H - 6, B * H - 1):
+        b, hh = divmod(bh, H)
+        sl = (slice(b, b + 1), slice(hh, hh + 1))
+        ref = oracle.attn_bwd(q[sl], k[sl], v[sl], g[sl], 1.0 / math.sqrt(d), causal)
+        _compare([x[sl] for x in got], ref, f"{label} slice ({b}, {hh})")
+
+
 def test_bwd_deterministic(osm):
     q, k, v, g = _case(1, 2, 1000, 128, seed=91)
     a = _gpu_bwd(osm, q, k, v, g, True)

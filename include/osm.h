@@ -90,7 +90,8 @@ typedef enum {
     OSM_ERR_DEVICE = 8,   /* the current device is not a gfx950 GPU            */
     OSM_ERR_SPLITS = 9,   /* a split count is outside its documented range     */
     OSM_ERR_WORKSPACE = 10, /* workspace_bytes is below what the call requires */
-    OSM_ERR_HEADS = 11     /* Hkv is not a divisor of H in 1 .. H               */
+    OSM_ERR_HEADS = 11,    /* Hkv is not a divisor of H in 1 .. H               */
+    OSM_ERR_SCRATCH = 12   /* the problem exceeds the static scratch's limit    */
 } osm_status;
 
 /*
@@ -246,6 +247,30 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N);
 int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
              const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N, int d,
              float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Query rows B * H * N up to which attn_bwd_noalloc runs (its scratch holds
+ * two fp32 values per row: 32 MiB per GPU). */
+#define OSM_NOALLOC_BWD_MAX_ROWS (1 << 22)
+
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight training loops, harnesses that
+ * forbid hipMalloc.  Same arguments, gradients, rounding, alignment and
+ * overlap rules as attn_bwd, without the workspace: the row statistics live
+ * in a static device array of the library (one per GPU, 32 MiB, held from the
+ * library's first use on that GPU until the process ends).  The call
+ * allocates nothing and calls no allocating routine.
+ *   B * H * N must not exceed OSM_NOALLOC_BWD_MAX_ROWS (else
+ *   OSM_ERR_SCRATCH, before any HIP call).
+ * Every call on one GPU uses that GPU's single array: calls that overlap in
+ * time on one GPU (different streams or host threads without ordering) race
+ * and may return wrong gradients; calls ordered on one stream are safe.
+ * Nothing in the array needs clearing between calls: each call writes every
+ * value it reads.  Returns an osm_status.
+ */
+int attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
+                     int d, float scale, int causal, void* stream);
 
 /*
  * attn_bwd_varlen -- attn_bwd for attn_fwd_varlen: packed sequences.

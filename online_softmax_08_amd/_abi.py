@@ -49,6 +49,9 @@ _lib.attn_bwd_workspace_bytes.restype = _sz
 _lib.attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                           _i, _vp, _sz, _vp]
 _lib.attn_bwd.restype = _i
+_lib.attn_bwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                  _f, _i, _vp]
+_lib.attn_bwd_noalloc.restype = _i
 _lib.attn_bwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
                                  _i, _i, _i, _f, _i, _vp, _sz, _vp]
 _lib.attn_bwd_varlen.restype = _i
@@ -56,8 +59,8 @@ _lib.osm_status_str.argtypes = [_i]
 _lib.osm_status_str.restype = ctypes.c_char_p
 
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_gqa", "attn_fwd_varlen", "attn_fwd_splitkv_plan", "attn_fwd_splitkv",
-           "attn_combine", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_varlen", "row_softmax",
-           "osm_status_str")
+           "attn_combine", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_varlen",
+           "row_softmax", "osm_status_str")
 
 OSM_OK = 0
 OSM_ERR_NULL = 1
@@ -71,6 +74,9 @@ OSM_ERR_DEVICE = 8
 OSM_ERR_SPLITS = 9
 OSM_ERR_WORKSPACE = 10
 OSM_ERR_HEADS = 11
+OSM_ERR_SCRATCH = 12
+# attn_bwd_noalloc's limit on B * H * N (include/osm.h OSM_NOALLOC_BWD_MAX_ROWS)
+NOALLOC_BWD_MAX_ROWS = 1 << 22
 
 
 class OsmError(RuntimeError):
@@ -145,6 +151,15 @@ def attn_bwd(Q: int, K: int, V: int, O: int, dO: int, lse: int, dQ: int, dK: int
     """Backward pass of attn_fwd / attn_fwd_gqa (dQ, dK, dV); see include/osm.h."""
     _call("attn_bwd", Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale, int(bool(causal)),
           workspace, workspace_bytes, stream)
+
+
+def attn_bwd_noalloc(Q: int, K: int, V: int, O: int, dO: int, lse: int, dQ: int, dK: int,
+                     dV: int, B: int, H: int, Hkv: int, N: int, d: int, scale: float, causal: bool,
+                     stream: int = 0) -> None:
+    """attn_bwd with the row statistics in the library's static device scratch
+    (no workspace, no allocation); see include/osm.h."""
+    _call("attn_bwd_noalloc", Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale,
+          int(bool(causal)), stream)
 
 
 def attn_fwd_varlen(Q: int, K: int, V: int, O: int, lse: int, cu_seqlens: int, B: int, H: int,

@@ -42,6 +42,31 @@ int check_device()
 
 int finish(hipError_t e) { return e == hipSuccess ? OSM_OK : OSM_ERR_HIP; }
 
+// Device scratch of attn_bwd_noalloc: the two fp32 row statistics of the
+// backward (D and L log2 e, OSM_NOALLOC_BWD_MAX_ROWS rows each), one copy per
+// GPU, held from the library's first use on that GPU until the process ends.
+// On the host, `scratch` names a host-side stand-in, not device memory: host
+// code only ever uses the per-device address hipGetSymbolAddress returns.
+static __device__ __align__(256) float scratch[2 * (size_t)OSM_NOALLOC_BWD_MAX_ROWS];
+
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of this GPU's scratch array, looked up once per device with
+// that device current (the caller has run check_device, so the current
+// device index is valid).  Concurrent first calls look up the same address.
+int scratch_address(float** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return OSM_ERR_HIP;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return OSM_ERR_HIP;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = static_cast<float*>(p);
+    return OSM_OK;
+}
+
 // Shape and scale checks shared by the attention entry points.
 int check_attn_shape(int B, int H, int N, int d, float scale, size_t elem)
 {
@@ -262,21 +287,30 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N)
     return (size_t)2 * B * H * N * sizeof(float);
 }
 
-int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-             const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N, int d,
-             float scale, int causal, void* workspace, size_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Validation of attn_bwd's tensors and, with use_ws, of its workspace
+// (attn_bwd_noalloc has none).  *work is set to false for an empty problem
+// (valid, nothing to launch).
+int validate_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                 const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
+                 int d, float scale, bool use_ws, const void* workspace, size_t workspace_bytes,
+                 bool* work)
 {
+    *work = false;
     int st = check_attn_shape(B, H, N, d, scale, 2);
     if (st != OSM_OK || B == 0 || H == 0 || N == 0) return st;
     if ((st = check_heads(H, Hkv)) != OSM_OK) return st;
-    if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || !workspace)
+    if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || (use_ws && !workspace))
         return OSM_ERR_NULL;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
         !aligned(dO, 16) || !aligned(lse, 4) || !aligned(dQ, 16) || !aligned(dK, 16) ||
-        !aligned(dV, 16) || !aligned(workspace, 16))
+        !aligned(dV, 16) || (workspace && !aligned(workspace, 16)))
         return OSM_ERR_ALIGN;
     const long long bh = (long long)B * H;
-    const size_t need = attn_bwd_workspace_bytes(B, H, N);
+    const size_t need = use_ws ? attn_bwd_workspace_bytes(B, H, N) : 0;
     if (workspace_bytes < need) return OSM_ERR_WORKSPACE;
     const size_t tb = (size_t)bh * N * d * 2, lb = (size_t)bh * N * sizeof(float);
     const size_t kvb = (size_t)B * Hkv * N * d * 2;
@@ -293,9 +327,47 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
     }
     for (int b = 0; b < 6; ++b)
         if (overlaps(workspace, need, ins[b], in_bytes[b])) return OSM_ERR_ALIAS;
+    *work = true;
+    return OSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N, int d,
+             float scale, int causal, void* workspace, size_t workspace_bytes, void* stream)
+{
+    bool work = false;
+    int st = validate_bwd(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale, true, workspace,
+                          workspace_bytes, &work);
+    if (st != OSM_OK || !work) return st;
     if ((st = check_device()) != OSM_OK) return st;
+    const long long bh = (long long)B * H;
     float* Dl = static_cast<float*>(workspace);
     float* Lc = Dl + (size_t)bh * N;
+    return finish(osm::launch_attn_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale,
+                                            causal != 0, Dl, Lc, static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
+                     int d, float scale, int causal, void* stream)
+{
+    bool work = false;
+    int st = validate_bwd(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale, false, nullptr,
+                          0, &work);
+    if (st != OSM_OK || !work) return st;
+    const long long rows = (long long)B * H * N;
+    if (rows > OSM_NOALLOC_BWD_MAX_ROWS) return OSM_ERR_SCRATCH;
+    if ((st = check_device()) != OSM_OK) return st;
+    float* Dl = nullptr;
+    if ((st = scratch_address(&Dl)) != OSM_OK) return st;
+    // Same kernels as attn_bwd, with the row statistics in the static scratch
+    // (D in rows 0 .. rows - 1, L log2 e after them).  The delta kernel writes
+    // every value the later kernels read, so nothing needs clearing.
+    float* Lc = Dl + rows;
     return finish(osm::launch_attn_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale,
                                             causal != 0, Dl, Lc, static_cast<hipStream_t>(stream)));
 }
@@ -359,6 +431,7 @@ const char* osm_status_str(int status)
     case OSM_ERR_SPLITS: return "the number of key splits is out of range";
     case OSM_ERR_WORKSPACE: return "the workspace is smaller than the call requires";
     case OSM_ERR_HEADS: return "key/value heads must divide the query heads (1 <= Hkv <= H)";
+    case OSM_ERR_SCRATCH: return "the problem needs more than the library's static scratch";
     default: return "unknown status";
     }
 }

@@ -28,6 +28,7 @@ def test_header_declares_the_entry_points():
                                             "attn_fwd_splitkv_plan",
                                             "attn_fwd_splitkv", "attn_combine",
                                             "attn_bwd_workspace_bytes", "attn_bwd",
+                                            "attn_bwd_noalloc",
                                             "attn_bwd_varlen", "row_softmax",
                                             "osm_status_str"])
 
@@ -56,14 +57,14 @@ def test_status_code_numbering(abi):
     assert codes == {"OSM_OK": 0, "OSM_ERR_NULL": 1, "OSM_ERR_SIZE": 2, "OSM_ERR_HEAD_DIM": 3,
                      "OSM_ERR_SCALE": 4, "OSM_ERR_ALIAS": 5, "OSM_ERR_HIP": 6, "OSM_ERR_ALIGN": 7,
                      "OSM_ERR_DEVICE": 8, "OSM_ERR_SPLITS": 9, "OSM_ERR_WORKSPACE": 10,
-                     "OSM_ERR_HEADS": 11}
+                     "OSM_ERR_HEADS": 11, "OSM_ERR_SCRATCH": 12}
     for name, value in codes.items():
         assert getattr(abi, name) == value, name
     assert "runtime" in abi.osm_status_str(6) and "aligned" in abi.osm_status_str(7)
 
 
 def test_status_strings(abi):
-    for st in range(0, 12):
+    for st in range(0, 13):
         assert abi.osm_status_str(st) and abi.osm_status_str(st) != "unknown status"
     assert abi.osm_status_str(99) == "unknown status"
 
@@ -242,6 +243,36 @@ def test_bwd_workspace_and_validation(abi):
     assert status(H=2, Hkv=0) == abi.OSM_ERR_HEADS
     assert status(H=2, Hkv=4) == abi.OSM_ERR_HEADS
     abi.attn_bwd(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 2, 2, 16, 64, 0.125, 1, 0, 0)  # empty: no-op
+
+
+def test_bwd_noalloc_validation(abi):
+    # The allocation-free backward validates like attn_bwd (no workspace
+    # arguments) and rejects problems beyond its static scratch with
+    # OSM_ERR_SCRATCH, all before any HIP call.
+    far = {n: (i + 1) << 36 for i, n in enumerate(("Q", "K", "V", "O", "dO", "lse", "dQ", "dK",
+                                                     "dV"))}
+
+    def status(**kw):
+        a = dict(far, B=1, H=1, Hkv=1, N=16, d=64, scale=0.125, causal=0)
+        a.update(kw)
+        with pytest.raises(abi.OsmError) as e:
+            abi.attn_bwd_noalloc(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["lse"], a["dQ"],
+                                 a["dK"], a["dV"], a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+                                 a["scale"], a["causal"])
+        return e.value.status
+    assert status(d=96) == abi.OSM_ERR_HEAD_DIM
+    assert status(scale=-1.0) == abi.OSM_ERR_SCALE
+    assert status(N=-3) == abi.OSM_ERR_SIZE
+    assert status(lse=0) == abi.OSM_ERR_NULL
+    assert status(dV=far["dV"] + 8) == abi.OSM_ERR_ALIGN
+    assert status(dQ=far["O"]) == abi.OSM_ERR_ALIAS
+    assert status(H=2, Hkv=3) == abi.OSM_ERR_HEADS
+    # one row past the limit, and the largest shape inside it (which then
+    # reaches the device check: no gfx950 device here)
+    rows = abi.NOALLOC_BWD_MAX_ROWS
+    assert status(B=1, H=64, Hkv=64, N=rows // 64 + 1) == abi.OSM_ERR_SCRATCH
+    assert status(B=1, H=64, Hkv=64, N=rows // 64) in (abi.OSM_ERR_HIP, abi.OSM_ERR_DEVICE)
+    abi.attn_bwd_noalloc(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 2, 2, 16, 64, 0.125, 1)  # empty: no-op
 
 
 def test_varlen_validation(abi):

@@ -22,7 +22,7 @@ Prints one JSON line:
   cpu_baseline      the fp64 oracle on the host cores, on a bounded sample
                     of the same workload (and its parity on that sample)
   device            GPU name, architecture, compute units, peak engine clock
-  supplementary     measured after the timed region: every other attention
+  supplementary     measured before the warm-up (see main): every other attention
                     workload (fp32 [1,1,128,64], bf16 [2,8,1024,64],
                     [4,16,2048,128], causal [1,32,8192,128]) with mean,
                     median and fastest launch, the headline shape without
@@ -111,6 +111,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing leg (profiling runs)")
+    ap.add_argument("--supplementary", choices=("before", "after", "none"), default="before",
+                    help="when to run the supplementary measurements: before the warm-up and "
+                         "timed steps (default), after them, or not at all (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy per step (outside the timed "
                          "region) to calibrate HBM byte counters")
@@ -147,6 +150,16 @@ def main() -> int:
         osm.attention(q, k, v, causal=wa.causal, out=O, lse=lse)
         osm.softmax(x, out=y)
 
+    # The supplementary figures are measured first: besides being figures
+    # of their own, their second or so of GPU work takes the clocks out of
+    # the idle state the GPU sits in while the inputs are drawn, so that the
+    # timed steps see the sustained state even after a short warm-up (from
+    # idle, the first ~10 ms of alternating steps run up to 10% slower).
+    # The backward figure takes O and lse from one forward call.
+    supp = None
+    if args.supplementary == "before":
+        step()
+        supp = supplementary(osm, wa, ws, q, k, v, x, O, lse)
     for _ in range(args.warmup):
         step()
         if args.copy_probe:
@@ -221,17 +234,19 @@ def main() -> int:
                              "algorithmic_bytes": ws.bytes},
         "cpu_baseline": None,
     }
-    # The supplementary figures run while the GPU is still warm; the CPU
-    # baseline (seconds of host work, GPU idle) comes last.
-    out["supplementary"] = supplementary(osm, wa, ws, q, k, v, x, O, lse)
+    # The CPU baseline (seconds of host work, GPU idle) comes last.
+    if args.supplementary == "after":
+        supp = supplementary(osm, wa, ws, q, k, v, x, O, lse)
+    out["supplementary"] = supp
+    out["supplementary_order"] = args.supplementary
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wa, ws, q_cpu, k_cpu, v_cpu, x_cpu, O, lse, y)
     print(json.dumps(out), flush=True)
     return 0
 
 
-def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10):
-    """Figures measured after the timed region, not part of a step: the same
+def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10, warm_ms=15.0):
+    """Figures measured outside the timed region, not part of a step: the same
     attention shape without the causal mask, a plain device copy of the
     softmax input (the practical ceiling for a read-once / write-once
     kernel on this GPU), the split-KV forward on long rows, and the backward
@@ -242,8 +257,16 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10):
     from online_softmax_08_amd import inputs
 
     def launch_times(fn):
+        # at least `warm` launches and warm_ms of back-to-back launches, so
+        # that each figure is taken at the clocks that workload settles at
         for _ in range(warm):
             fn()
+        torch.cuda.synchronize()
+        t_end = time.perf_counter() + warm_ms * 1e-3
+        while time.perf_counter() < t_end:
+            for _ in range(warm):
+                fn()
+            torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]
         torch.cuda.synchronize()

@@ -3,14 +3,17 @@ against the fp64 oracle's chain-rule gradients, on seeded inputs.
 
 The GPU backward takes the forward's own bf16 O and fp32 lse as inputs, as a
 training step would; the oracle recomputes everything from Q, K, V and dO in
-fp64.  Bar, per gradient tensor: max-abs error <= 2e-2 * max(1, max |ref|),
-i.e. the forward's bf16 bar for gradients up to 1 and 2% of the tensor's
-largest magnitude beyond.  The error is not a fixed multiple of one bf16
-rounding: D_i = sum_t dO_it O_it is formed from the rounded O (relative error
-up to 2^-9 per term), and that error reaches dK_j through
-scale * sum_i P_ij dD_i Q_i, which the x8 query rows of the causal stress
-workload amplify (there it is 0.10 of the 0.13 max error on dK, |dK| <= 14);
-the bf16 rounding of P and dS inside the products adds the rest.
+fp64.  Two bars, both enforced:
+  * per gradient tensor, max-abs error <= 2e-2 * max(1, max |ref|);
+  * per element, |err| <= 6 sigma + u |grad| + 1e-5, with sigma the error
+    scale of that element under the bf16 error model of the backward
+    (_grad_bounds): the rounding of P before dV, D_i = sum_t dO_it O_it
+    formed from the forward's rounded O, the rounding of dS before dK and
+    dQ, each rounding at most u = 2^-8 relative, independent and of mean
+    zero.  The largest measured ratio of error to this bar is 0.47; a
+    regression that corrupts some elements (a missed tile, a wrong mask or
+    statistic) exceeds it there even when the tensor's largest error does
+    not move.
 """
 from __future__ import annotations
 
@@ -52,14 +55,71 @@ def _gpu_bwd(osm, q, k, v, g, causal):
     return [t.to(torch.float64).cpu().numpy() for t in (dq, dk, dv)]
 
 
-def _compare(got, ref, label):
+U = 2.0 ** -8       # unit roundoff of bf16 (round to nearest even)
+ELEM_FACTOR = 6.0   # per-element bar: ELEM_FACTOR * sigma + u |grad| + ELEM_FLOOR
+ELEM_FLOOR = 1e-5
+
+
+def _grad_bounds(q, k, v, g, scale, causal):
+    """Per-element error scale of the bf16 backward, from the error model of
+    its rounding steps.  Each rounding of a value x to bf16 errs by at most
+    u |x| (u = 2^-8), and the roundings are independent and of mean zero, so
+    the error of a sum of such terms has a standard deviation of at most
+    u sqrt(sum x^2).  The steps:
+      * P rounded before dV = P^T dO: u sqrt(sum_i (P_ij dO_it)^2);
+      * D_i = sum_t dO_it O_it from the forward's bf16 O, whose error is at
+        most 2u sum_j P_ij |V_jt| (the forward's P rounded, then O rounded):
+        dD_i = 2u sqrt(sum_t (dO_it sum_j P_ij |V_jt|)^2), reaching dS_ij as
+        P_ij dD_i;
+      * dS rounded before dK = scale dS^T Q and dQ = scale dS K: u |dS_ij|;
+      * each gradient rounded to bf16 (u |grad|, kept separately).
+    Returns (sigma, rounding) pairs for dQ, dK, dV.  The magnitudes are
+    evaluated in float64 from the same inputs; they set tolerances only,
+    the reference values come from the oracle."""
+    Q, Kt, Vt, G = (np.asarray(t.to(torch.float64).numpy()) for t in (q, k, v, g))
+    B, H, N, d = Q.shape
+    sq, sk, sv = np.zeros_like(Q), np.zeros_like(Q), np.zeros_like(Q)
+    rq, rk, rv = np.zeros_like(Q), np.zeros_like(Q), np.zeros_like(Q)
+    mask = np.triu(np.ones((N, N), dtype=bool), 1) if causal else None
+    for b in range(B):
+        for h in range(H):
+            qs, ks, vs, gs = Q[b, h], Kt[b, h], Vt[b, h], G[b, h]
+            S = scale * (qs @ ks.T)
+            if causal:
+                S[mask] = -np.inf
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            O = P @ vs
+            D = np.sum(gs * O, axis=1)
+            dS = P * (gs @ vs.T - D[:, None])
+            dD = 2 * U * np.sqrt(np.sum((gs * (P @ np.abs(vs))) ** 2, axis=1))
+            E2 = (P * dD[:, None]) ** 2 + (U * dS) ** 2   # variance scale of dS
+            sv[b, h] = U * np.sqrt((P ** 2).T @ gs ** 2)
+            sk[b, h] = scale * np.sqrt(E2.T @ qs ** 2)
+            sq[b, h] = scale * np.sqrt(E2 @ ks ** 2)
+            rv[b, h] = U * np.abs(P.T @ gs)
+            rk[b, h] = U * np.abs(scale * (dS.T @ qs))
+            rq[b, h] = U * np.abs(scale * (dS @ ks))
+    return (sq, rq), (sk, rk), (sv, rv)
+
+
+def _compare(got, ref, label, bounds=None):
+    """Max-abs error within the per-tensor bar and, with bounds, every
+    element within ELEM_FACTOR times its error scale plus its own rounding
+    (and a small floor)."""
     ok = True
-    for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+    for x, (name, a, b) in enumerate(zip(("dQ", "dK", "dV"), got, ref)):
         assert np.all(np.isfinite(a)), f"{label}: {name} not finite"
         e = float(np.max(np.abs(a - b))) if a.size else 0.0
         scale = max(1.0, float(np.max(np.abs(b))) if b.size else 0.0)
-        print(f"{label}: {name} max|err|={e:.3e} max|ref|={scale:.3f} bar={TOL * scale:.3e}", flush=True)
+        msg = f"{label}: {name} max|err|={e:.3e} max|ref|={scale:.3f} bar={TOL * scale:.3e}"
         ok &= e <= TOL * scale
+        if bounds is not None and a.size:
+            sig, rnd = bounds[x]
+            r = np.abs(a - b) / (ELEM_FACTOR * sig + rnd + ELEM_FLOOR)
+            msg += f" max err/elem-bar={float(np.max(r)):.3f}"
+            ok &= bool(np.all(r <= 1.0))
+        print(msg, flush=True)
     assert ok, label
 
 
@@ -74,7 +134,7 @@ def test_bwd_full(osm, shape, causal):
     print(label, flush=True)
     got = _gpu_bwd(osm, q, k, v, g, causal)
     ref = oracle.attn_bwd(q, k, v, g, 1.0 / math.sqrt(d), causal)
-    _compare(got, ref, label)
+    _compare(got, ref, label, _grad_bounds(q, k, v, g, 1.0 / math.sqrt(d), causal))
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -87,7 +147,7 @@ def test_bwd_small_workload(osm, causal):
     print(label, flush=True)
     got = _gpu_bwd(osm, q, k, v, g, causal)
     ref = oracle.attn_bwd(q, k, v, g, w.scale, causal)
-    _compare(got, ref, label)
+    _compare(got, ref, label, _grad_bounds(q, k, v, g, w.scale, causal))
 
 
 def test_bwd_headline_shape_sampled_slices(osm):
@@ -101,7 +161,8 @@ def test_bwd_headline_shape_sampled_slices(osm):
     for b, hh in ((0, 0), (w.B - 1, w.H - 1)):
         sl = (slice(b, b + 1), slice(hh, hh + 1))
         ref = oracle.attn_bwd(q[sl], k[sl], v[sl], g[sl], w.scale, w.causal)
-        _compare([x[sl] for x in got], ref, f"slice ({b}, {hh})")
+        _compare([x[sl] for x in got], ref, f"slice ({b}, {hh})",
+                 _grad_bounds(q[sl], k[sl], v[sl], g[sl], w.scale, w.causal))
 
 
 @pytest.mark.parametrize("case", [((1, 16, 2048, 64), False), ((1, 16, 2048, 64), True),
@@ -122,7 +183,8 @@ def test_bwd_workgroup_sizes(osm, case):
         b, hh = divmod(bh, H)
         sl = (slice(b, b + 1), slice(hh, hh + 1))
         ref = oracle.attn_bwd(q[sl], k[sl], v[sl], g[sl], 1.0 / math.sqrt(d), causal)
-        _compare([x[sl] for x in got], ref, f"{label} slice ({b}, {hh})")
+        _compare([x[sl] for x in got], ref, f"{label} slice ({b}, {hh})",
+                 _grad_bounds(q[sl], k[sl], v[sl], g[sl], 1.0 / math.sqrt(d), causal))
 
 
 def test_bwd_deterministic(osm):

@@ -249,9 +249,10 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10, warm_ms=15.
     """Figures measured outside the timed region, not part of a step: the same
     attention shape without the causal mask, a plain device copy of the
     softmax input (the practical ceiling for a read-once / write-once
-    kernel on this GPU), the split-KV forward on long rows, and the backward
-    pass of the headline workload (its FLOPs counted as 2.5 times the
-    forward's, the five products of the gradient; the kernels compute seven)."""
+    kernel on this GPU), the split-KV forward on long rows, the backward pass
+    of the headline workload (its FLOPs counted as 2.5 times the forward's,
+    the five products of the gradient; the kernels compute seven), and the
+    split backward on the long-row input."""
     import torch
 
     from online_softmax_08_amd import inputs
@@ -353,6 +354,24 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10, warm_ms=15.
     bwd_ms = per_launch_ms(lambda: osm.attention_backward(q, k, v, O, lse, go, causal=wa.causal,
                                                           workspace=wsb))
     bwd_flops = 2.5 * 4.0 * wa.B * wa.H * wa.N * wa.N * wa.d / (2 if wa.causal else 1)
+    # Backward on few heads (the split-KV input above): the split backward at
+    # the library's range count beside the unsplit call.
+    gs = inputs.grad_output(qs.shape, 6).to(q.device)
+    bsplit = {"workload": f"bf16 B={B} H={H} N={N} d={d} backward"}
+    for causal in (False, True):
+        Os, ls = osm.attention(qs, ks, vs, causal=causal)
+        ns, ws_bytes = osm.attn_bwd_split_plan(B, H, H, N, d, causal, 0)
+        wsp = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        ws1 = torch.empty(osm.attn_bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device=q.device)
+        flops = 2.5 * 4.0 * B * H * N * N * d / (2 if causal else 1)
+        t_split = per_launch_ms(lambda: osm.attention_backward_split(
+            qs, ks, vs, Os, ls, gs, causal=causal, nsplit=ns, workspace=wsp))
+        t_one = per_launch_ms(lambda: osm.attention_backward(qs, ks, vs, Os, ls, gs, causal=causal,
+                                                             workspace=ws1))
+        bsplit["causal" if causal else "noncausal"] = {
+            "nsplit": ns, "split_tflops": round(flops / (t_split * 1e-3) / 1e12, 1),
+            "unsplit_tflops": round(flops / (t_one * 1e-3) / 1e12, 1),
+            "split_ms": round(t_split, 4), "unsplit_ms": round(t_one, 4)}
     return {
         "attn_backward": {"workload": f"{wa.name} backward (dQ, dK, dV)",
                           "value": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 1), "unit": "TFLOPS",
@@ -364,6 +383,7 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10, warm_ms=15.
                      "value": round(ws.bytes / (cp_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                      "kernel_ms": round(cp_ms, 4)},
         "attn_splitkv": split,
+        "attn_backward_split": bsplit,
         "attn_varlen": varlen,
         "attn_configs": configs,
     }

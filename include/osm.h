@@ -248,6 +248,56 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
              const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N, int d,
              float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * attn_bwd_split_plan -- resolve a split count for attn_bwd_split and size its
+ * workspace.
+ *   B, H, Hkv, N, d, causal : as for attn_bwd (d must be 64 or 128)
+ *   nsplit             : 1 .. 64 ranges, or 0 to let the library choose (it
+ *                        splits only when 256-row blocks alone would leave
+ *                        compute units idle)
+ *   *nsplit_out        : the count attn_bwd_split will use for nsplit
+ *   *workspace_bytes   : device bytes attn_bwd_split needs for it: for a
+ *                        count of 1 attn_bwd_workspace_bytes(B, H, N) (the
+ *                        call is then exactly attn_bwd), otherwise
+ *                        round_up(2 B H N 4, 256) + nsplit (2 B Hkv + B H) N d 4
+ * Host only; touches no device.  Returns OSM_ERR_NULL for NULL out pointers,
+ * OSM_ERR_SIZE, OSM_ERR_HEAD_DIM, OSM_ERR_HEADS or OSM_ERR_SPLITS for bad
+ * sizes.
+ */
+int attn_bwd_split_plan(int B, int H, int Hkv, int N, int d, int causal, int nsplit,
+                        int* nsplit_out, size_t* workspace_bytes);
+
+/*
+ * attn_bwd_split -- attn_bwd for problems with few (batch, head) slices, the
+ * backward counterpart of attn_fwd_splitkv (Lesson 22, sections 30-31, and
+ * "Fast, memory-efficient and exact attention", section 3.3: the gradient
+ * is a sum over key blocks for dQ and over query blocks for dK and dV, so
+ * either sum can be cut into parts computed in parallel and added).  The
+ * dK/dV workgroup of each 256-key block divides its query tiles (64 rows;
+ * with Hkv < H those of all query heads of the group, head by head) into
+ * nsplit near-equal contiguous ranges; the dQ workgroup of each 256-query
+ * block divides its visible key tiles (64 keys) likewise.  Each range writes
+ * its partial sums in fp32 to the workspace, and a last kernel adds the
+ * nsplit partials of every element in range order and rounds to bf16.
+ *   Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale, causal, stream :
+ *             as for attn_bwd
+ *   nsplit  : 0 (library's choice) or 1 .. 64; a count of 1 runs attn_bwd
+ *   workspace : device memory of at least workspace_bytes as returned by
+ *             attn_bwd_split_plan for the same arguments, 16-byte aligned,
+ *             caller-owned, not overlapping any other argument; its contents
+ *             on entry do not matter and on return are unspecified.  Calls
+ *             that share a workspace must be ordered on one stream.
+ * The gradients satisfy attn_bwd's tolerance against the exact result and
+ * are deterministic for a given nsplit; they are not bitwise equal to
+ * attn_bwd's (the products are summed in another order).  Returns an
+ * osm_status (OSM_ERR_WORKSPACE if workspace_bytes is too small, OSM_ERR_SIZE
+ * if N * d * 4 does not fit in 32 bits).
+ */
+int attn_bwd_split(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
+                   int d, float scale, int causal, int nsplit, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 /* Query rows B * H * N up to which attn_bwd_noalloc runs (its scratch holds
  * two fp32 values per row: 32 MiB per GPU). */
 #define OSM_NOALLOC_BWD_MAX_ROWS (1 << 22)

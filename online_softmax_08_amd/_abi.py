@@ -52,6 +52,12 @@ _lib.attn_bwd.restype = _i
 _lib.attn_bwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                   _f, _i, _vp]
 _lib.attn_bwd_noalloc.restype = _i
+_lib.attn_bwd_split_plan.argtypes = [_i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(_i),
+                                     ctypes.POINTER(_sz)]
+_lib.attn_bwd_split_plan.restype = _i
+_lib.attn_bwd_split.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                _f, _i, _i, _vp, _sz, _vp]
+_lib.attn_bwd_split.restype = _i
 _lib.attn_bwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
                                  _i, _i, _i, _f, _i, _vp, _sz, _vp]
 _lib.attn_bwd_varlen.restype = _i
@@ -60,7 +66,7 @@ _lib.osm_status_str.restype = ctypes.c_char_p
 
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_gqa", "attn_fwd_varlen", "attn_fwd_splitkv_plan", "attn_fwd_splitkv",
            "attn_combine", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_varlen",
-           "row_softmax", "osm_status_str")
+           "attn_bwd_split_plan", "attn_bwd_split", "row_softmax", "osm_status_str")
 
 OSM_OK = 0
 OSM_ERR_NULL = 1
@@ -160,6 +166,24 @@ def attn_bwd_noalloc(Q: int, K: int, V: int, O: int, dO: int, lse: int, dQ: int,
     (no workspace, no allocation); see include/osm.h."""
     _call("attn_bwd_noalloc", Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale,
           int(bool(causal)), stream)
+
+
+def attn_bwd_split_plan(B: int, H: int, Hkv: int, N: int, d: int, causal: bool,
+                        nsplit: int = 0) -> tuple[int, int]:
+    """(resolved split count, workspace bytes) for attn_bwd_split; see include/osm.h."""
+    n_out, ws = _i(0), _sz(0)
+    _call("attn_bwd_split_plan", B, H, Hkv, N, d, int(bool(causal)), nsplit, ctypes.byref(n_out),
+          ctypes.byref(ws))
+    return n_out.value, ws.value
+
+
+def attn_bwd_split(Q: int, K: int, V: int, O: int, dO: int, lse: int, dQ: int, dK: int, dV: int,
+                   B: int, H: int, Hkv: int, N: int, d: int, scale: float, causal: bool,
+                   nsplit: int, workspace: int, workspace_bytes: int, stream: int = 0) -> None:
+    """attn_bwd with the query (dK, dV) and key (dQ) loops split into nsplit
+    ranges and the fp32 partials summed; see include/osm.h."""
+    _call("attn_bwd_split", Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale,
+          int(bool(causal)), nsplit, workspace, workspace_bytes, stream)
 
 
 def attn_fwd_varlen(Q: int, K: int, V: int, O: int, lse: int, cu_seqlens: int, B: int, H: int,

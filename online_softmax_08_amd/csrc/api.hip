@@ -296,8 +296,8 @@ namespace {
 // (valid, nothing to launch).
 int validate_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                  const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
-                 int d, float scale, bool use_ws, const void* workspace, size_t workspace_bytes,
-                 bool* work)
+                 int d, float scale, bool use_ws, size_t need, const void* workspace,
+                 size_t workspace_bytes, bool* work)
 {
     *work = false;
     int st = check_attn_shape(B, H, N, d, scale, 2);
@@ -310,7 +310,7 @@ int validate_bwd(const void* Q, const void* K, const void* V, const void* O, con
         !aligned(dV, 16) || (workspace && !aligned(workspace, 16)))
         return OSM_ERR_ALIGN;
     const long long bh = (long long)B * H;
-    const size_t need = use_ws ? attn_bwd_workspace_bytes(B, H, N) : 0;
+    if (!use_ws) need = 0;
     if (workspace_bytes < need) return OSM_ERR_WORKSPACE;
     const size_t tb = (size_t)bh * N * d * 2, lb = (size_t)bh * N * sizeof(float);
     const size_t kvb = (size_t)B * Hkv * N * d * 2;
@@ -340,8 +340,8 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
              float scale, int causal, void* workspace, size_t workspace_bytes, void* stream)
 {
     bool work = false;
-    int st = validate_bwd(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale, true, workspace,
-                          workspace_bytes, &work);
+    int st = validate_bwd(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale, true,
+                          attn_bwd_workspace_bytes(B, H, N), workspace, workspace_bytes, &work);
     if (st != OSM_OK || !work) return st;
     if ((st = check_device()) != OSM_OK) return st;
     const long long bh = (long long)B * H;
@@ -356,8 +356,8 @@ int attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
                      int d, float scale, int causal, void* stream)
 {
     bool work = false;
-    int st = validate_bwd(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale, false, nullptr,
-                          0, &work);
+    int st = validate_bwd(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale, false, 0,
+                          nullptr, 0, &work);
     if (st != OSM_OK || !work) return st;
     const long long rows = (long long)B * H * N;
     if (rows > OSM_NOALLOC_BWD_MAX_ROWS) return OSM_ERR_SCRATCH;
@@ -370,6 +370,84 @@ int attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
     float* Lc = Dl + rows;
     return finish(osm::launch_attn_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale,
                                             causal != 0, Dl, Lc, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of the split backward: the row statistics (2 B H N fp32, padded
+// to 256 bytes), then the fp32 partials of dK and dV ([2][nsplit][B Hkv][N][d])
+// and of dQ ([nsplit][B H][N][d]).
+size_t bwd_stats_bytes(long long bh, int N)
+{
+    return ((size_t)2 * bh * N * sizeof(float) + 255) & ~(size_t)255;
+}
+
+size_t bwd_split_workspace(int nsplit, long long bh, long long bhkv, int N, int d)
+{
+    return bwd_stats_bytes(bh, N) + (size_t)nsplit * (2 * bhkv + bh) * N * d * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_bwd_split_plan(int B, int H, int Hkv, int N, int d, int causal, int nsplit,
+                        int* nsplit_out, size_t* workspace_bytes)
+{
+    if (!nsplit_out || !workspace_bytes) return OSM_ERR_NULL;
+    if (B < 0 || H < 0 || N < 0) return OSM_ERR_SIZE;
+    if (d != 64 && d != 128) return OSM_ERR_HEAD_DIM;
+    if (nsplit < 0 || nsplit > osm::kMaxSplits) return OSM_ERR_SPLITS;
+    const long long bh = (long long)B * H;
+    if (bh > INT_MAX) return OSM_ERR_SIZE;
+    if (bh > 0 && N > 0) {
+        const int st = check_heads(H, Hkv);
+        if (st != OSM_OK) return st;
+    }
+    if (nsplit == 0) nsplit = (bh == 0 || N == 0) ? 1 : osm::attn_bwd_split_auto((int)bh, N, d, causal != 0);
+    *nsplit_out = nsplit;
+    *workspace_bytes = (bh == 0 || N == 0) ? 0
+                       : nsplit == 1       ? attn_bwd_workspace_bytes(B, H, N)
+                                           : bwd_split_workspace(nsplit, bh, (long long)B * Hkv, N, d);
+    return OSM_OK;
+}
+
+int attn_bwd_split(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
+                   int d, float scale, int causal, int nsplit, void* workspace,
+                   size_t workspace_bytes, void* stream)
+{
+    if (nsplit < 0 || nsplit > osm::kMaxSplits) return OSM_ERR_SPLITS;
+    const long long bh = (long long)B * H;
+    if (B > 0 && H > 0 && N > 0 && bh <= INT_MAX && nsplit == 0)
+        nsplit = osm::attn_bwd_split_auto((int)bh, N, d, causal != 0);
+    if (nsplit <= 1)
+        return attn_bwd(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale, causal, workspace,
+                        workspace_bytes, stream);
+    // Sizes are checked by validate_bwd first; the workspace size formula
+    // needs them non-negative.
+    int st = check_attn_shape(B, H, N, d, scale, 2);
+    if (st != OSM_OK || B == 0 || H == 0 || N == 0) return st;
+    if ((st = check_heads(H, Hkv)) != OSM_OK) return st;
+    const size_t need = bwd_split_workspace(nsplit, bh, (long long)B * Hkv, N, d);
+    bool work = false;
+    st = validate_bwd(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale, true, need,
+                      workspace, workspace_bytes, &work);
+    if (st != OSM_OK || !work) return st;
+    // The split kernels launch ceil(N / 256) * nsplit * B * H workgroups of
+    // 512 work-items, and a dispatch counts at most 2^32 - 1 work-items;
+    // offsets into one fp32 partial slice are 32-bit.
+    if (bh * ((N + 255) / 256) * nsplit * 512 > UINT32_MAX || (long long)N * d * 4 > UINT32_MAX)
+        return OSM_ERR_SIZE;
+    if ((st = check_device()) != OSM_OK) return st;
+    float* Dl = static_cast<float*>(workspace);
+    float* Lc = Dl + (size_t)bh * N;
+    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_stats_bytes(bh, N));
+    return finish(osm::launch_attn_bwd_bf16_split(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d,
+                                                  scale, causal != 0, nsplit, Dl, Lc, part,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 int attn_bwd_varlen(const void* Q, const void* K, const void* V, const void* O, const void* dO,

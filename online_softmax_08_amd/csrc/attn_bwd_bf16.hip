@@ -167,6 +167,25 @@ __device__ __forceinline__ bf16x8 half_bf16(const f32x16& v, int G)
     return __builtin_convertvector(p8, bf16x8);
 }
 
+// fp32 rows of a wave's 32-row accumulator tile (lane (j, h) holds row
+// row0 + j, columns 32 dt + 8 g + 4 h .. + 3 in registers 4 g .. 4 g + 3 of
+// acc[dt]), stored straight from the registers: 16 bytes per lane and
+// instruction.  Rows past the buffer's range are dropped.
+template <int D>
+__device__ __forceinline__ void store_rows_f32(const f32x16 (&acc)[D / 32],
+                                               __amdgpu_buffer_rsrc_t rs, int row0, int lane)
+{
+    const int j = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 o4 = {acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), rs,
+                                                   (uint32_t)((row0 + j) * D + dt * 32 + 8 * g + 4 * h) * 4, 0, 0);
+        }
+}
+
 // ---------------------------------------------------------------- delta ----
 // D[r] = sum_t dO[r][t] O[r][t] (bf16 products, fp32 sums) and
 // Lc[r] = lse[r] log2(e), for rows r of [rows][D]; D / 8 lanes per row.
@@ -195,13 +214,14 @@ attn_bwd_delta_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ d
 }
 
 // ------------------------------------------------------------ dK and dV ----
-template <int D, int NW, bool CAUSAL, bool VARLEN>
+template <int D, int NW, bool CAUSAL, bool VARLEN, bool SPLIT = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                      const float* __restrict__ Lc, const float* __restrict__ Dl,
                      __bf16* __restrict__ dK, __bf16* __restrict__ dV, int Nmax, int BHkv, int H,
-                     int Hkv, float scale, const int* __restrict__ cu, int total)
+                     int Hkv, float scale, const int* __restrict__ cu, int total,
+                     float* __restrict__ part, int nsplit)
 {
     constexpr int BK = NW * 32, BQ = 64;
     using TQ = Tile<D, BQ>;
@@ -225,7 +245,12 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // most queries, so the longest workgroups start first.  The workgroup's
     // key/value head kvbh serves the query heads b H + hkv G .. + G - 1
     // (G = H / Hkv), whose contributions it sums.
-    const int t = blockIdx.x / BHkv, kvbh = blockIdx.x - t * BHkv;
+    // With SPLIT (dense only) the query tiles of a key block are divided
+    // into nsplit contiguous ranges, one workgroup per (key block, range);
+    // each writes its partial dK^T and dV^T sums in fp32 to part.
+    const int tt = blockIdx.x / BHkv, kvbh = blockIdx.x - tt * BHkv;
+    const int t = SPLIT ? tt / nsplit : tt;
+    const int sp = SPLIT ? tt - t * nsplit : 0;
     const int k0 = t * BK, kw0 = k0 + wave * 32;
     const int G = H / Hkv, hkv = kvbh % Hkv;
     const Seq<VARLEN> sq(kvbh / Hkv, Nmax, cu, total);
@@ -379,21 +404,27 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
     const int nit = G * nq;
-    if (nq > 0) {
-        issue(B0{}, 0);
-        stat_store(B0{}, stat_load(0));
+    int it0 = 0, it1 = nit;  // this workgroup's steps
+    if constexpr (SPLIT) {
+        const int per = (nit + nsplit - 1) / nsplit;
+        it0 = min(nit, sp * per);
+        it1 = min(nit, it0 + per);
+    }
+    if (it1 > it0) {
+        issue(B0{}, it0);
+        stat_store(B0{}, stat_load(it0));
         __syncthreads();
-        for (int it = 0; it < nit; it += 2) {
+        for (int it = it0; it < it1; it += 2) {
             float st = 0.f;
-            if (it + 1 < nit) {
+            if (it + 1 < it1) {
                 issue(B1{}, it + 1);
                 st = stat_load(it + 1);
             }
             compute(B0{}, it);
             stat_store(B1{}, st);
             __syncthreads();
-            if (it + 1 >= nit) break;
-            if (it + 2 < nit) {
+            if (it + 1 >= it1) break;
+            if (it + 2 < it1) {
                 issue(B0{}, it + 2);
                 st = stat_load(it + 2);
             }
@@ -401,6 +432,16 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             stat_store(B0{}, st);
             __syncthreads();
         }
+    }
+    if constexpr (SPLIT) {
+        // Partials [2][nsplit][BHkv][N][D]: dK^T (scale not applied), then
+        // dV^T; an empty range writes zeros.
+        const size_t slice = (size_t)N * D;
+        float* const pk = part + ((size_t)sp * BHkv + kvbh) * slice;
+        float* const pv = pk + (size_t)nsplit * BHkv * slice;
+        store_rows_f32<D>(dkt, make_rsrc(pk, (uint32_t)slice * 4), kw0, lane);
+        store_rows_f32<D>(dvt, make_rsrc(pv, (uint32_t)slice * 4), kw0, lane);
+        return;
     }
     // Both gradients leave through the wave's 32-row slice of the V block
     // (BK x (D + 8) elements, 32 rows per wave), which no wave reads any more.
@@ -410,14 +451,58 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     store_tile_rows<D>(dvt, 1.0f, ost, make_rsrc(dV + base, slice_b), key - j, lane);
 }
 
+// ------------------------------------------------------ split reduction ----
+// out[e] = bf16(mul * sum_{s < S} part[s * stride + e]) for the n8 * 8
+// elements of one gradient; the sum runs in s order, so the result does not
+// depend on the launch shape.  Three gradients per launch (dK, dV, dQ), eight
+// elements per thread per trip, grid-stride.
+struct SumSeg {
+    const float* part;
+    __bf16* out;
+    long long n8, stride;
+    float mul;
+};
+
+__global__ void __launch_bounds__(256)
+attn_bwd_sum_kernel(SumSeg a, SumSeg b, SumSeg c, int S)
+{
+    const long long total = a.n8 + b.n8 + c.n8;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (long long)gridDim.x * 256) {
+        const float* p;
+        __bf16* o;
+        long long stride;
+        float mul;
+        if (i < a.n8) {
+            p = a.part + 8 * i; o = a.out + 8 * i; stride = a.stride; mul = a.mul;
+        } else if (i < a.n8 + b.n8) {
+            const long long k = i - a.n8;
+            p = b.part + 8 * k; o = b.out + 8 * k; stride = b.stride; mul = b.mul;
+        } else {
+            const long long k = i - a.n8 - b.n8;
+            p = c.part + 8 * k; o = c.out + 8 * k; stride = c.stride; mul = c.mul;
+        }
+        f32x4 x0 = *reinterpret_cast<const f32x4*>(p), x1 = *reinterpret_cast<const f32x4*>(p + 4);
+        for (int sp = 1; sp < S; ++sp) {
+            p += stride;
+            x0 += *reinterpret_cast<const f32x4*>(p);
+            x1 += *reinterpret_cast<const f32x4*>(p + 4);
+        }
+        const f32x8 y = {x0[0] * mul, x0[1] * mul, x0[2] * mul, x0[3] * mul,
+                         x1[0] * mul, x1[1] * mul, x1[2] * mul, x1[3] * mul};
+        *reinterpret_cast<bf16x8*>(o) = __builtin_convertvector(y, bf16x8);
+    }
+}
+
 // ------------------------------------------------------------------- dQ ----
-template <int D, int NW, bool CAUSAL, bool VARLEN>
+template <int D, int NW, bool CAUSAL, bool VARLEN, bool SPLIT = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                    const float* __restrict__ Lc, const float* __restrict__ Dl,
                    __bf16* __restrict__ dQ, int Nmax, int BH, int nqb, int H, int Hkv,
-                   float scale, const int* __restrict__ cu, int total)
+                   float scale, const int* __restrict__ cu, int total,
+                   float* __restrict__ part, int nsplit)
 {
     constexpr int BR = NW * 32, BC = 64;
     using TK = Tile<D, BC>;
@@ -433,7 +518,12 @@ attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 31, h = lane >> 5;
-    const int t = blockIdx.x / BH, bh = blockIdx.x - t * BH;
+    // With SPLIT (dense only) the key tiles of a query block are divided into
+    // nsplit contiguous ranges, one workgroup per (query block, range); each
+    // writes its partial dQ^T sum in fp32 to part.
+    const int tt = blockIdx.x / BH, bh = blockIdx.x - tt * BH;
+    const int t = SPLIT ? tt / nsplit : tt;
+    const int sp = SPLIT ? tt - t * nsplit : 0;
     const int qb = CAUSAL ? nqb - 1 - t : t;  // longest first under the mask
     const int q0 = qb * BR, qw0 = q0 + wave * 32, q = qw0 + j;
     const int hq = bh % H;
@@ -553,16 +643,32 @@ attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    issue(B0{}, 0);
-    __syncthreads();
-    for (int kt = 0; kt < ntiles; kt += 2) {
-        if (kt + 1 < ntiles) issue(B1{}, kt + 1);
-        compute(B0{}, kt);
+    int kt0 = 0, kt1 = ntiles;  // this workgroup's key tiles
+    if constexpr (SPLIT) {
+        const int per = (ntiles + nsplit - 1) / nsplit;
+        kt0 = min(ntiles, sp * per);
+        kt1 = min(ntiles, kt0 + per);
+    }
+    if (kt1 > kt0) {
+        issue(B0{}, kt0);
         __syncthreads();
-        if (kt + 1 >= ntiles) break;
-        if (kt + 2 < ntiles) issue(B0{}, kt + 2);
-        compute(B1{}, kt + 1);
-        __syncthreads();
+        for (int kt = kt0; kt < kt1; kt += 2) {
+            if (kt + 1 < kt1) issue(B1{}, kt + 1);
+            compute(B0{}, kt);
+            __syncthreads();
+            if (kt + 1 >= kt1) break;
+            if (kt + 2 < kt1) issue(B0{}, kt + 2);
+            compute(B1{}, kt + 1);
+            __syncthreads();
+        }
+    }
+    if constexpr (SPLIT) {
+        // Partials [nsplit][BH][N][D] of dQ^T (scale not applied); an empty
+        // range writes zeros.
+        const size_t slice = (size_t)N * D;
+        store_rows_f32<D>(acc, make_rsrc(part + ((size_t)sp * BH + bh) * slice, (uint32_t)slice * 4),
+                          qw0, lane);
+        return;
     }
     // dQ leaves through LDS: the wave's half of one of the four K/V tile
     // buffers (waves 2b, 2b + 1 share buffer b; each holds 2 x 32 rows of
@@ -589,7 +695,7 @@ hipError_t launch_dkdv(const __bf16* q, const __bf16* k, const __bf16* v, const 
         const int nkb = (N + NW * 32 - 1) / (NW * 32);
         attn_bwd_dkdv_kernel<D, NW, CAUSAL, VARLEN><<<dim3((unsigned)(nkb * BHkv)), dim3(NW * 64), 0, stream>>>(
             q, k, v, g, Lc, Dl, static_cast<__bf16*>(dK), static_cast<__bf16*>(dV), N, BHkv, H, Hkv,
-            scale, cu, total);
+            scale, cu, total, nullptr, 1);
         return hipGetLastError();
     };
     if ((long long)((N + 255) / 256) * BHkv >= kCUs) return go(std::integral_constant<int, 8>{});
@@ -607,7 +713,8 @@ hipError_t launch_dq(const __bf16* q, const __bf16* k, const __bf16* v, const __
         constexpr int NW = decltype(nwc)::value;
         const int nqb = (N + NW * 32 - 1) / (NW * 32);
         attn_bwd_dq_kernel<D, NW, CAUSAL, VARLEN><<<dim3((unsigned)(nqb * BH)), dim3(NW * 64), 0, stream>>>(
-            q, k, v, g, Lc, Dl, static_cast<__bf16*>(dQ), N, BH, nqb, H, Hkv, scale, cu, total);
+            q, k, v, g, Lc, Dl, static_cast<__bf16*>(dQ), N, BH, nqb, H, Hkv, scale, cu, total,
+            nullptr, 1);
         return hipGetLastError();
     };
     if ((long long)((N + 255) / 256) * BH >= kCUs) return go(std::integral_constant<int, 8>{});
@@ -643,7 +750,82 @@ hipError_t launch_bwd(const void* Q, const void* K, const void* V, const void* O
     return launch_dq<D, CAUSAL, VARLEN>(q, k, v, g, Lc, Dl, dQ, B, H, Hkv, N, scale, cu, total, stream);
 }
 
+// Split backward (dense): the dK/dV workgroups divide their query tiles, the
+// dQ workgroups their key tiles, into nsplit ranges; fp32 partials in part
+// ([2][nsplit][B Hkv][N][D] for dK and dV, then [nsplit][B H][N][D] for dQ),
+// summed by attn_bwd_sum_kernel.  8-wave workgroups throughout.
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_split(const void* Q, const void* K, const void* V, const void* O,
+                            const void* dO, const float* lse, void* dQ, void* dK, void* dV, int B,
+                            int H, int Hkv, int N, float scale, int nsplit, float* Dl, float* Lc,
+                            float* part, hipStream_t stream)
+{
+    const int BH = B * H, BHkv = B * Hkv;
+    const __bf16* q = static_cast<const __bf16*>(Q);
+    const __bf16* k = static_cast<const __bf16*>(K);
+    const __bf16* v = static_cast<const __bf16*>(V);
+    const __bf16* g = static_cast<const __bf16*>(dO);
+    const long long rows = (long long)BH * N;
+    {
+        constexpr int RPB = 256 / (D / 8);
+        const long long need = (rows + RPB - 1) / RPB;
+        attn_bwd_delta_kernel<D><<<dim3((unsigned)(need < 65536 ? need : 65536)), dim3(256), 0, stream>>>(
+            static_cast<const __bf16*>(O), g, lse, Dl, Lc, rows);
+        if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    const int nb = (N + 255) / 256;
+    float* const pkv = part;
+    float* const pq = part + (size_t)2 * nsplit * BHkv * N * D;
+    attn_bwd_dkdv_kernel<D, 8, CAUSAL, false, true><<<dim3((unsigned)(nb * nsplit * BHkv)), dim3(512), 0, stream>>>(
+        q, k, v, g, Lc, Dl, nullptr, nullptr, N, BHkv, H, Hkv, scale, nullptr, 0, pkv, nsplit);
+    if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    attn_bwd_dq_kernel<D, 8, CAUSAL, false, true><<<dim3((unsigned)(nb * nsplit * BH)), dim3(512), 0, stream>>>(
+        q, k, v, g, Lc, Dl, nullptr, N, BH, nb, H, Hkv, scale, nullptr, 0, pq, nsplit);
+    if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const long long kv8 = (long long)BHkv * N * D / 8, q8 = rows * D / 8;
+    const long long kvs = (long long)BHkv * N * D, qs = rows * D;
+    const SumSeg sk{pkv, static_cast<__bf16*>(dK), kv8, kvs, scale};
+    const SumSeg sv{pkv + (size_t)nsplit * kvs, static_cast<__bf16*>(dV), kv8, kvs, 1.0f};
+    const SumSeg sq{pq, static_cast<__bf16*>(dQ), q8, qs, scale};
+    const long long blocks = (2 * kv8 + q8 + 255) / 256;
+    attn_bwd_sum_kernel<<<dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream>>>(sk, sv, sq, nsplit);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+int attn_bwd_split_auto(int BH, int N, int d, bool causal)
+{
+    // Measured over [1..2, 1..16, 2048..32768, d] (both masks): no split
+    // while 8-wave workgroups of 256 rows cover the 256 compute units, nor
+    // for rows of 2048 or fewer once the unsplit launch's 4-wave workgroups
+    // do; otherwise enough ranges for about one 8-wave workgroup per CU,
+    // twice that under the mask (its ranges are unequal), while each range
+    // keeps at least 512 rows of the loop it divides (256 at d = 64, whose
+    // partials cost half the bytes), and at most 16.
+    const long long w = (long long)((N + 255) / 256) * BH;
+    if (w >= kCUs || N <= 256) return 1;
+    if (N <= 2048 && (long long)((N + 127) / 128) * BH >= kCUs) return 1;
+    long long n = (kCUs + w - 1) / w;
+    if (causal) n *= 2;
+    long long cap = N / (d == 64 ? 256 : 512);
+    if (cap > 16) cap = 16;
+    if (n > cap) n = cap;
+    return n < 2 ? 1 : (int)n;
+}
+
+hipError_t launch_attn_bwd_bf16_split(const void* Q, const void* K, const void* V, const void* O,
+                                      const void* dO, const float* lse, void* dQ, void* dK,
+                                      void* dV, int B, int H, int Hkv, int N, int d, float scale,
+                                      bool causal, int nsplit, float* Dl, float* Lc, float* part,
+                                      hipStream_t stream)
+{
+    if (d == 64)
+        return causal ? launch_bwd_split<64, true>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, nsplit, Dl, Lc, part, stream)
+                      : launch_bwd_split<64, false>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, nsplit, Dl, Lc, part, stream);
+    return causal ? launch_bwd_split<128, true>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, nsplit, Dl, Lc, part, stream)
+                  : launch_bwd_split<128, false>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, scale, nsplit, Dl, Lc, part, stream);
+}
 
 hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* lse, void* dQ, void* dK, void* dV,

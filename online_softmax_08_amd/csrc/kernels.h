@@ -44,6 +44,15 @@ hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, con
                                 const void* dO, const float* lse, void* dQ, void* dK, void* dV,
                                 int B, int H, int Hkv, int N, int d, float scale, bool causal,
                                 float* Dl, float* Lc, hipStream_t stream);
+// Split backward (dense): part is fp32 workspace of
+// (2 nsplit B Hkv + nsplit B H) N d values; 1 <= nsplit <= kMaxSplits.
+hipError_t launch_attn_bwd_bf16_split(const void* Q, const void* K, const void* V, const void* O,
+                                      const void* dO, const float* lse, void* dQ, void* dK,
+                                      void* dV, int B, int H, int Hkv, int N, int d, float scale,
+                                      bool causal, int nsplit, float* Dl, float* Lc, float* part,
+                                      hipStream_t stream);
+// The number of ranges the split backward picks when asked to choose.
+int attn_bwd_split_auto(int BH, int N, int d, bool causal);
 // Backward over packed sequences: Q, O, dO, dQ [H][total][d], K, V, dK, dV
 // [Hkv][total][d], lse, Dl, Lc [H][total].
 hipError_t launch_attn_bwd_bf16_varlen(const void* Q, const void* K, const void* V, const void* O,

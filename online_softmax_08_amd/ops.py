@@ -178,6 +178,43 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
     return dq, dk, dv
 
 
+def attention_backward_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             out: torch.Tensor, lse: torch.Tensor, grad_out: torch.Tensor,
+                             causal: bool = False, scale: float | None = None, nsplit: int = 0,
+                             workspace: torch.Tensor | None = None):
+    """attention_backward() with the dK/dV query loop and the dQ key loop split
+    into nsplit parallel ranges whose fp32 partials are summed (nsplit 0: the
+    library's choice; it splits only small grids).
+
+    ``workspace`` (optional) is a device uint8 tensor of at least the planned
+    size (attn_bwd_split_plan); otherwise one is allocated.  Returns
+    (dq, dk, dv).
+    """
+    _check_attn(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("the backward pass takes bfloat16 q, k, v")
+    for name, tsr in (("out", out), ("grad_out", grad_out)):
+        if tsr.shape != q.shape or tsr.dtype != q.dtype or not tsr.is_contiguous() or tsr.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    ns, ws_bytes = _abi.attn_bwd_split_plan(B, H, k.shape[1], N, d, causal, nsplit)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    with torch.cuda.device(q.device):
+        _abi.attn_bwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            grad_out.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                            dv.data_ptr(), B, H, k.shape[1], N, d, scale, causal, ns,
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                            _stream_handle(q.device))
+    return dq, dk, dv
+
+
 def attention_varlen_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                               out: torch.Tensor, lse: torch.Tensor, grad_out: torch.Tensor,
                               cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = False,

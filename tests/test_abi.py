@@ -29,6 +29,7 @@ def test_header_declares_the_entry_points():
                                             "attn_fwd_splitkv", "attn_combine",
                                             "attn_bwd_workspace_bytes", "attn_bwd",
                                             "attn_bwd_noalloc",
+                                            "attn_bwd_split_plan", "attn_bwd_split",
                                             "attn_bwd_varlen", "row_softmax",
                                             "osm_status_str"])
 
@@ -342,3 +343,72 @@ def test_bwd_varlen_validation(abi):
     assert status(dK=ptr["cu"]) == abi.OSM_ERR_ALIAS
     assert status(ws=ptr["dQ"] + 16) == abi.OSM_ERR_ALIAS
     abi.attn_bwd_varlen(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 2, 2, 2, 0, 64, 64, 0.125, 1, 0, 0)
+
+
+def _bwd_split_ws(B, H, Hkv, N, d, nsplit):
+    stats = (2 * B * H * N * 4 + 255) // 256 * 256
+    return stats + nsplit * (2 * B * Hkv + B * H) * N * d * 4
+
+
+def test_bwd_split_plan(abi):
+    # Explicit counts are kept; the workspace holds the row statistics and
+    # the fp32 partials of dK, dV (per key/value head) and dQ; a count of 1
+    # is attn_bwd with its own workspace.
+    assert abi.attn_bwd_split_plan(1, 2, 2, 1000, 64, False, 1) == (1, 2 * 2 * 1000 * 4)
+    assert abi.attn_bwd_split_plan(1, 2, 2, 1000, 64, True, 3) == (3, _bwd_split_ws(1, 2, 2, 1000, 64, 3))
+    assert abi.attn_bwd_split_plan(1, 4, 2, 600, 128, False, 64) == (64, _bwd_split_ws(1, 4, 2, 600, 128, 64))
+    assert abi.attn_bwd_split_plan(0, 4, 4, 4096, 64, False, 0) == (1, 0)
+    # Automatic choice: none once 256-row blocks fill the 256 CUs, nor for
+    # rows of 2048 when 128-row blocks do ...
+    auto = lambda B, H, N, d, c: abi.attn_bwd_split_plan(B, H, H, N, d, c, 0)[0]
+    assert auto(2, 16, 4096, 128, True) == 1
+    assert auto(1, 16, 2048, 128, False) == 1 and auto(2, 8, 2048, 128, True) == 1
+    assert auto(1, 1, 256, 64, False) == 1
+    # ... below that, about one 8-wave workgroup per CU (twice that under the
+    # mask), at least 512 rows per range (256 at d = 64), at most 16.
+    assert auto(1, 2, 4096, 128, False) == 8 and auto(1, 2, 4096, 128, True) == 8
+    assert auto(1, 2, 8192, 128, False) == 4 and auto(1, 2, 8192, 128, True) == 8
+    assert auto(1, 1, 16384, 64, False) == 4 and auto(1, 1, 16384, 64, True) == 8
+    assert auto(1, 8, 2048, 128, False) == 4 and auto(1, 8, 2048, 128, True) == 4
+    assert auto(1, 1, 32768, 128, False) == 2 and auto(1, 1, 32768, 128, True) == 4
+    assert auto(1, 4, 2048, 64, False) == 8 and auto(1, 4, 2048, 64, True) == 8
+    assert auto(1, 1, 1000, 128, True) == 1
+    ns, ws = abi.attn_bwd_split_plan(1, 2, 2, 4096, 128, True, 0)
+    assert ws == _bwd_split_ws(1, 2, 2, 4096, 128, ns)
+    for bad, st in (((1, 1, 1, 64, 96, False, 2), abi.OSM_ERR_HEAD_DIM),
+                    ((1, 1, 1, 64, 64, False, 65), abi.OSM_ERR_SPLITS),
+                    ((1, 1, 1, 64, 64, False, -1), abi.OSM_ERR_SPLITS),
+                    ((1, 4, 3, 64, 64, False, 2), abi.OSM_ERR_HEADS),
+                    ((-1, 1, 1, 64, 64, False, 2), abi.OSM_ERR_SIZE)):
+        with pytest.raises(abi.OsmError) as e:
+            abi.attn_bwd_split_plan(*bad)
+        assert e.value.status == st
+
+
+def test_bwd_split_validation(abi):
+    # attn_bwd_split checks its workspace against the planned size (and the
+    # tensors as attn_bwd does) before any HIP call.
+    far = {n: (i + 1) << 36 for i, n in enumerate(("Q", "K", "V", "O", "dO", "lse", "dQ", "dK",
+                                                     "dV", "ws"))}
+    need = _bwd_split_ws(1, 2, 2, 1000, 64, 3)
+
+    def status(nsplit=3, ws_bytes=need, **kw):
+        a = dict(far, B=1, H=2, Hkv=2, N=1000, d=64, scale=0.125, causal=1)
+        a.update(kw)
+        with pytest.raises(abi.OsmError) as e:
+            abi.attn_bwd_split(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["lse"], a["dQ"],
+                               a["dK"], a["dV"], a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+                               a["scale"], a["causal"], nsplit, a["ws"], ws_bytes)
+        return e.value.status
+    assert status(nsplit=65) == abi.OSM_ERR_SPLITS
+    assert status(ws_bytes=need - 1) == abi.OSM_ERR_WORKSPACE
+    assert status(ws=0) == abi.OSM_ERR_NULL
+    assert status(ws=far["ws"] + 8) == abi.OSM_ERR_ALIGN
+    assert status(ws=far["O"] - 64) == abi.OSM_ERR_ALIAS
+    assert status(H=2, Hkv=3) == abi.OSM_ERR_HEADS
+    assert status(d=96) == abi.OSM_ERR_HEAD_DIM
+    # a valid call reaches the device check (no gfx950 device here); so does
+    # a count of 1, which is attn_bwd with its smaller workspace
+    assert status() in (abi.OSM_ERR_HIP, abi.OSM_ERR_DEVICE)
+    assert status(nsplit=1, ws_bytes=2 * 2 * 1000 * 4) in (abi.OSM_ERR_HIP, abi.OSM_ERR_DEVICE)
+    abi.attn_bwd_split(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 2, 2, 16, 64, 0.125, 1, 3, 0, 0)  # empty: no-op

@@ -192,3 +192,75 @@ def test_bwd_deterministic(osm):
     a = _gpu_bwd(osm, q, k, v, g, True)
     b = _gpu_bwd(osm, q, k, v, g, True)
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+# ----------------------------------------------------------- split backward --
+def _gpu_bwd_split(osm, q, k, v, g, causal, nsplit):
+    dev = torch.device("cuda:0")
+    q, k, v, g = (t.to(dev) for t in (q, k, v, g))
+    O, lse = osm.attention(q, k, v, causal=causal)
+    dq, dk, dv = osm.attention_backward_split(q, k, v, O, lse, g, causal=causal, nsplit=nsplit)
+    torch.cuda.synchronize()
+    return [t.to(torch.float64).cpu().numpy() for t in (dq, dk, dv)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape,nsplit", [((1, 2, 1000, 64), 3), ((1, 1, 777, 128), 4),
+                                          ((2, 1, 512, 128), 2), ((1, 2, 1500, 128), 16),
+                                          ((1, 1, 300, 64), 64)])
+def test_bwd_split_full(osm, shape, nsplit, causal):
+    # attn_bwd_split: the dK/dV query loop and the dQ key loop cut into
+    # nsplit ranges, the fp32 partials summed.  Ragged N (a partial last
+    # tile in every loop), uneven ranges, and more ranges than tiles (the
+    # empty ranges contribute zeros).  Whole tensors against the oracle.
+    B, H, N, d = shape
+    q, k, v, g = _case(B, H, N, d, seed=7000 + N + d + nsplit)
+    label = f"bwd split={nsplit} B{B}H{H}N{N}d{d} causal={causal}"
+    print(label, flush=True)
+    got = _gpu_bwd_split(osm, q, k, v, g, causal, nsplit)
+    ref = oracle.attn_bwd(q, k, v, g, 1.0 / math.sqrt(d), causal)
+    _compare(got, ref, label, _grad_bounds(q, k, v, g, 1.0 / math.sqrt(d), causal))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_split_gqa(osm, causal):
+    # Four query heads on two key/value heads: a dK/dV workgroup's ranges run
+    # over the query tiles of both heads of its group, head by head.
+    B, H, Hkv, N, d = 1, 4, 2, 600, 128
+    q, k, v, g = _case(B, H, N, d, seed=7100)
+    k, v = k[:, :Hkv].contiguous(), v[:, :Hkv].contiguous()
+    label = f"bwd split=3 GQA B{B}H{H}/{Hkv}N{N}d{d} causal={causal}"
+    print(label, flush=True)
+    got = _gpu_bwd_split(osm, q, k, v, g, causal, 3)
+    G = H // Hkv
+    kr, vr = k.repeat_interleave(G, dim=1), v.repeat_interleave(G, dim=1)
+    rq, rk, rv = oracle.attn_bwd(q, kr, vr, g, 1.0 / math.sqrt(d), causal)
+    rk = rk.reshape(B, Hkv, G, N, d).sum(axis=2)
+    rv = rv.reshape(B, Hkv, G, N, d).sum(axis=2)
+    _compare(got, (rq, rk, rv), label)
+
+
+def test_bwd_split_small_grid_full(osm):
+    # A small grid at full length: [1, 2, 4096, 128] causal, the library's
+    # own split count, every element against the oracle; and the same call
+    # twice gives the same bits (partials summed in range order).
+    osm_abi = osm
+    B, H, N, d = 1, 2, 4096, 128
+    ns, _ = osm_abi.attn_bwd_split_plan(B, H, H, N, d, True, 0)
+    assert ns > 1
+    q, k, v, g = _case(B, H, N, d, seed=7200)
+    label = f"bwd split={ns} B{B}H{H}N{N}d{d} causal=True"
+    print(label, flush=True)
+    got = _gpu_bwd_split(osm, q, k, v, g, True, 0)
+    ref = oracle.attn_bwd(q, k, v, g, 1.0 / math.sqrt(d), True)
+    _compare(got, ref, label, _grad_bounds(q, k, v, g, 1.0 / math.sqrt(d), True))
+    again = _gpu_bwd_split(osm, q, k, v, g, True, 0)
+    assert all(np.array_equal(x, y) for x, y in zip(got, again))
+
+
+def test_bwd_split_one_is_attn_bwd(osm):
+    # A count of 1 is attn_bwd itself: bitwise the same gradients.
+    q, k, v, g = _case(1, 2, 1000, 64, seed=7300)
+    a = _gpu_bwd_split(osm, q, k, v, g, True, 1)
+    b = _gpu_bwd(osm, q, k, v, g, True)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))

@@ -642,12 +642,19 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
                         float* __restrict__ lse, int Nmax, int BH, int nqt, float scale,
                         const int* __restrict__ cu, int H, int Hkv, int total)
 {
-    constexpr int NW = 8, BC = 64;
-    using C = Cfg<D, 1, NW, BC>;
-    __shared__ __attribute__((aligned(1024))) char kbuf0[C::KTILE_B];
-    __shared__ __attribute__((aligned(1024))) char kbuf1[C::KTILE_B];
-    __shared__ __attribute__((aligned(1024))) char vbuf0[C::VTILE_B];
-    __shared__ __attribute__((aligned(1024))) char vbuf1[C::VTILE_B];
+    // Keys per step: 128 at D = 64 (its 64-key steps are half as long as at
+    // D = 128, so the per-step costs weigh twice as much), 64 at D = 128
+    // (128-key steps there need more than 256 registers).
+    constexpr int NW = 8, BC = D == 64 ? 128 : 64;
+    using C = Cfg<D, 1, NW, 64>;
+    // Unpadded tiles; at least the padded 64-key size, which the output
+    // staging (store_tile_rows) needs.
+    constexpr int KT_B = BC * D * 2 > C::KTILE_B ? BC * D * 2 : C::KTILE_B;
+    constexpr int VT_B = BC * D * 2 > C::VTILE_B ? BC * D * 2 : C::VTILE_B;
+    __shared__ __attribute__((aligned(1024))) char kbuf0[KT_B];
+    __shared__ __attribute__((aligned(1024))) char kbuf1[KT_B];
+    __shared__ __attribute__((aligned(1024))) char vbuf0[VT_B];
+    __shared__ __attribute__((aligned(1024))) char vbuf1[VT_B];
     auto kbuf = [&](auto bufc) -> char* { if constexpr (decltype(bufc)::value == 0) return kbuf0; else return kbuf1; };
     auto vbuf = [&](auto bufc) -> char* { if constexpr (decltype(bufc)::value == 0) return vbuf0; else return vbuf1; };
 
@@ -731,7 +738,7 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     // gets an empty range: its loads read nothing and fill dst with zeros,
     // which no later step reads, so the loads need no branch.
     static_assert(LPW >= 1 && LPW <= 4, "one to four loads per wave");
-    auto load_part = [&](const __bf16* X, char* dst, int kt) {
+    auto load_part = [&](const __bf16* X, char* dst, int kt) __attribute__((always_inline)) {
         const int kv0 = kt * BC;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(
             X + sl.kvbase + (size_t)kv0 * D, kt < ntiles ? (uint32_t)(N - kv0) * D * 2 : 0u);
@@ -755,28 +762,28 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     const int vrow = 8 * (g16 >> 1) + e4;
     const int vbase = vrow * D * 2 + (16 * (g16 & 1) + 4 * a4) * 2 + (((vrow / RPQ) & (NB - 1)) << 6);
 
-    f32x16 s[2];    // scores of the current tile, 32 keys each
-    bf16x8 pf[4];   // its probabilities, bf16, 16 keys each
+    f32x16 s[BC / 32];   // scores of the current tile, 32 keys each
+    bf16x8 pf[BC / 16];  // its probabilities, bf16, 16 keys each
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) pf[ks] = bf16x8{};
+    for (int ks = 0; ks < BC / 16; ++ks) pf[ks] = bf16x8{};
 
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    auto qk = [&](auto kbc) {
-        s[0] = f32x16{};
-        s[1] = f32x16{};
+    auto qk = [&](auto kbc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < BC / 32; ++mt) s[mt] = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
+            for (int mt = 0; mt < BC / 32; ++mt) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(
                     kbuf(kbc) + mt * 64 * D + (kbase ^ (kk << 5)));
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mt], 0, 0, 0);
             }
     };
-    auto pv = [&](auto vbc) {
+    auto pv = [&](auto vbc) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < BC / 16; ++ks)
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
                 const char* vp = vbuf(vbc) + 16 * ks * D * 2 + (vbase ^ (dt << 6));
@@ -794,7 +801,7 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     // their use.  A wave past its last tile (i > T) only loads.  One code
     // path for steps 1 .. T keeps the accumulators in fixed registers.
     auto matrix_phase = [&](auto kbc, auto vbc, auto ldc, const __bf16* X, char* ldst, int kt,
-                            int i) {
+                            int i) __attribute__((always_inline)) {
         constexpr bool LD = decltype(ldc)::value;  // this phase issues the loads
         if (CAUSAL && i > T) {  // without the mask every wave computes every step
             if constexpr (LD) load_part(X, ldst, kt);
@@ -809,7 +816,7 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         // P V, then S^T unless this is step T, whose scores are never used.
         // Each block gets its own pipeline: a few LDS reads ahead, then one
         // MFMA per one or two reads (P V: 2 reads per product, S^T: 1).
-        constexpr int NPV = 4 * (D / 32), NQK = 2 * (D / 16);
+        constexpr int NPV = (BC / 16) * (D / 32), NQK = (BC / 32) * (D / 16);
         pv(vbc);
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
 #pragma unroll
@@ -830,11 +837,11 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         }
     };
     // Step 0 has no probabilities yet: its matrix phase is S^T of tile 0.
-    auto first_matrix_phase = [&]() {
+    auto first_matrix_phase = [&]() __attribute__((always_inline)) {
         qk(B0{});
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int u = 0; u < 12; ++u) {
+        for (int u = 0; u < (BC / 32) * (D / 16) - 4; ++u) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
@@ -842,7 +849,7 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     };
     // Vector phase of step i: mask (last tile only), probabilities and row
     // sums, and the rare move of the exponent reference.
-    auto vector_phase = [&](int i) {
+    auto vector_phase = [&](int i) __attribute__((always_inline)) {
         if (i < 0 || i >= T) return;
         if (i == T - 1 && mask_last) {
             // Key kvm + o of register r (o below) is hidden when o >= thr.
@@ -851,18 +858,21 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
             int thr = (CAUSAL ? min(N, qrow + 1) : N) - kvm - 8 * h;
             asm volatile("" : "+v"(thr));
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < BC / 32; ++mt) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (mt * 32 + 16 * (r >> 3) + (r & 7) >= thr) s[mt][r] = kNegInf;
+                // one 32-key group at a time: bounds the live compare masks
+                if constexpr (BC > 64) __builtin_amdgcn_sched_barrier(0);
+            }
         }
         // Probabilities against the current reference m (one FMA and one
         // v_exp_f32 each), their bf16 copies (the B operand of P V) and this
         // lane's partial row sum.  s keeps the scores for a recomputation.
-        auto probs = [&](float mc) {
+        auto probs = [&](float mc) __attribute__((always_inline)) {
             float ps[4];  // four partial sums, seeded by the first four p
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < BC / 32; ++mt)
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     f32x8 p8;
@@ -896,7 +906,9 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 #pragma unroll
             for (int r = 8; r < 16; ++r) v[r & 3] = fmaxf(v[r & 3], s[0][r]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) v[r & 3] = fmaxf(v[r & 3], s[1][r]);
+            for (int mt = 1; mt < BC / 32; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) v[r & 3] = fmaxf(v[r & 3], s[mt][r]);
             const float mx = combine_xor32(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), MaxOp());
             const float m_new = fmaxf(m, mx);
             const float alpha = (m_new == kNegInf) ? 1.f : exp2_hw((m - m_new) * c);
@@ -931,7 +943,7 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     // causal D = 128.
     using VEarly = std::integral_constant<bool, D == 64>;
     using VInMatrix = std::integral_constant<bool, D != 64>;
-    auto steps = [&](auto latec) {
+    auto steps = [&](auto latec) __attribute__((always_inline)) {
         constexpr bool LATE = decltype(latec)::value;
         // step 0
         if constexpr (!LATE) {

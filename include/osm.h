@@ -178,9 +178,10 @@ int attn_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int nsplit,
  * merge.  Q, K, V, O, lse, B, H, Hkv, N, d, scale, causal, stream as for
  * attn_fwd_gqa (Hkv = H for plain multi-head attention).
  *   nsplit          : 0 (library's choice) or 1 .. 64.  Each 256-row query
- *                     block divides its visible key tiles (64 keys each)
- *                     into nsplit near-equal contiguous ranges; ranges past
- *                     the last visible tile are empty.
+ *                     block divides its visible key tiles (64 keys each at
+ *                     d = 128, 128 at d = 64) into nsplit near-equal
+ *                     contiguous ranges; ranges past the last visible tile
+ *                     are empty.
  *   workspace       : device memory of at least workspace_bytes as returned
  *                     by attn_fwd_splitkv_plan for the same arguments,
  *                     16-byte aligned, not overlapping any other argument;

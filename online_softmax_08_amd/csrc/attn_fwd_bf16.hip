@@ -71,10 +71,11 @@
 //    as S^T, softmax, P V in every wave; the two waves of a SIMD then mostly
 //    use the matrix core and the vector unit at the same time and wait for
 //    each other.  It serves the smaller grids (128- and 64-row workgroups
-//    whose key loop is split over two wave groups) and the split-KV partial
-//    pass.  attn_fwd_bf16_pp_kernel (8-wave workgroups of 256 rows, both
-//    masks) staggers the two waves of each SIMD by half a tile step, so that
-//    one issues only MFMAs while the other runs the softmax.
+//    whose key loop is split over two wave groups).
+//    attn_fwd_bf16_pp_kernel (8-wave workgroups of 256 rows, both masks, and
+//    the split-KV partial pass) staggers the two waves of each SIMD by half
+//    a tile step, so that one issues only MFMAs while the other runs the
+//    softmax.
 //  * The output tile of each wave leaves through LDS as whole rows
 //    (store_tile_rows): the accumulators hold O^T, whose direct stores would
 //    write 16-byte pieces of 32 rows per instruction.
@@ -198,13 +199,6 @@ struct Cfg {
     static_assert(NW % KS == 0, "key groups of equal size");
 };
 
-// With SPLIT the key tiles of each query block are divided into nsplit
-// contiguous ranges, one workgroup per (query block, range), and each
-// workgroup writes the normalised partial output of its range in fp32 to
-// opart [nsplit][BH][N][D] and the partial logsumexp to lpart [nsplit][BH][N]
-// (-inf for a row that sees no key of the range); attn_combine_kernel merges
-// them.  O and lse are then unused.
-//
 // With KS = 2 the workgroup's waves form two key groups over the same query
 // rows: wave w (group w / (NW / 2)) computes the even key tiles, wave
 // w + NW / 2 the odd ones, from one LDS buffer that holds both tiles of a
@@ -213,16 +207,14 @@ struct Cfg {
 // of Lesson 22, section 22 (rescale both to the larger reference and add)
 // and writes O and lse.  A small grid then keeps twice as many waves busy,
 // each with half of the key loop, and needs no workspace.
-template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL, bool SPLIT, bool VARLEN, int KS = 1>
+template <int D, int QT, int NW, int WPE, int BC, bool CAUSAL, bool VARLEN, int KS = 1>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, __bf16* __restrict__ O,
                      float* __restrict__ lse, int Nmax, int BH, int nqt, float scale,
-                     float* __restrict__ opart, float* __restrict__ lpart, int nsplit,
                      const int* __restrict__ cu, int H, int Hkv, int total)
 {
-    static_assert(!(SPLIT && VARLEN), "split-KV runs on dense tensors");
-    static_assert(KS == 1 || (KS == 2 && !SPLIT), "key groups: two, without split-KV");
+    static_assert(KS == 1 || KS == 2, "one or two key groups");
     using C = Cfg<D, QT, NW, BC, KS>;
     static_assert(NW <= 8 && C::KTILE_B >= 2 * 32 * (D + 8) * 2, "output staging fits the tile buffers");
     constexpr int NMT = BC / 32;  // 32-key MFMA tiles per key tile
@@ -240,17 +232,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int rw = wave % C::NWR, kg = wave / C::NWR;            // row wave, key group
     const int j = lane & 31, h = lane >> 5;
-    // Workgroup id = (t * nsplit + split) * BH + bh.
-    int t, bh, split = 0;
-    if constexpr (SPLIT) {
-        bh = blockIdx.x % BH;
-        const int rest = blockIdx.x / BH;
-        t = rest / nsplit;
-        split = rest - t * nsplit;
-    } else {
-        t = blockIdx.x / BH;
-        bh = blockIdx.x - t * BH;
-    }
+    const int t = blockIdx.x / BH, bh = blockIdx.x - t * BH;
     const int qt = CAUSAL ? nqt - 1 - t : t;
     const int q0 = qt * C::BR;
     const Slice sl = slice_of<D, VARLEN>(bh, Nmax, H, Hkv, cu, total);
@@ -419,10 +401,10 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     auto probs = [&](f32x16 (&s)[NMT][QT], bf16x8 (&pf)[BC / 16][QT]) {
 #pragma unroll
         for (int nt = 0; nt < QT; ++nt) {
-            // A key range of a split, or the tiles of the odd key group, can
-            // lie wholly in a row's future; that row keeps m = -inf and all
-            // its p must come out 0, not NaN.
-            const float mc = ((SPLIT || KS > 1) && m[nt] == kNegInf) ? 0.f : m[nt] * c;
+            // The tiles of the odd key group can lie wholly in a row's
+            // future; that row keeps m = -inf and all its p must come out 0,
+            // not NaN.
+            const float mc = (KS > 1 && m[nt] == kNegInf) ? 0.f : m[nt] * c;
             float ps[4];  // four partial sums, seeded by the first four p
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) {
@@ -468,23 +450,8 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     using B1 = std::integral_constant<int, 1>;
     const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
     const int ntiles = (kv_end + BC - 1) / BC;
-    // Key tiles of this workgroup: t_lo .. t_hi - 1 (all of them, or split
-    // number `split` of nsplit near-equal ranges).
-    int t_lo = 0, t_hi = ntiles;
-    if constexpr (SPLIT) {
-        const int per = (ntiles + nsplit - 1) / nsplit;
-        t_lo = min(ntiles, split * per);
-        t_hi = min(ntiles, t_lo + per);
-        if (t_lo >= t_hi) {
-            // Empty range: only the -inf partial logsumexp of every row.
-            const __amdgpu_buffer_rsrc_t lrs =
-                make_rsrc(lpart + ((size_t)split * BH + bh) * N, (uint32_t)N * 4);
-            for (int r = tid; r < C::BR; r += C::T)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(kNegInf), lrs,
-                                                      (uint32_t)(q0 + r) * 4, 0, 0);
-            return;
-        }
-    }
+    // Key tiles of this workgroup: t_lo .. t_hi - 1.
+    const int t_lo = 0, t_hi = ntiles;
     // Tiles this wave computes: t_lo .. wt - 1 (under the causal mask the
     // later tiles of the workgroup lie wholly in this wave's future).
     const int wt = CAUSAL ? min(t_hi, (qw0 + QT * 32 - 1) / BC + 1) : t_hi;
@@ -534,34 +501,6 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         if (kt + 2 * KS < t_hi) issue(B0{}, kt + 2 * KS);
         compute(B1{}, kt + KS + kg);
         __syncthreads();
-    }
-
-    if constexpr (SPLIT) {
-        // ---- partial epilogue: fp32 acc / l and m scale + ln l of this key
-        // range; a row that saw no key of it gets O = 0 and -inf ----
-        const size_t pslice = (size_t)split * BH + bh;
-        const __amdgpu_buffer_rsrc_t ors = make_rsrc(opart + pslice * N * D, (uint32_t)N * D * 4);
-        const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lpart + pslice * N, (uint32_t)N * 4);
-#pragma unroll
-        for (int nt = 0; nt < QT; ++nt) {
-            const int q = qw0 + nt * 32 + j;
-            const float l_tot = combine_xor32(l[nt], SumOp());
-            const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 o4 = {acc[nt][dt][4 * g] * inv, acc[nt][dt][4 * g + 1] * inv,
-                                      acc[nt][dt][4 * g + 2] * inv, acc[nt][dt][4 * g + 3] * inv};
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), ors,
-                                                           (uint32_t)(q * D + dt * 32 + 8 * g + 4 * h) * 4, 0, 0);
-                }
-            if (h == 0) {
-                const float ls = l_tot > 0.f ? m[nt] * scale + logf(l_tot) : kNegInf;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ls), lrs, (uint32_t)q * 4, 0, 0);
-            }
-        }
-        return;
     }
 
     // ---- epilogue: O = acc / l in bf16 (rows past N dropped), lse = m scale + ln l ----
@@ -635,13 +574,58 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 // (waves 4-7); the loads of K(i + 1) start in phase 2i, those of V(i) in
 // phase 2i + 1 (phase 2i at D = 64), and both are waited for before the
 // barrier that ends phase 2i + 1.
-template <int D, bool CAUSAL, bool VARLEN>
+//
+// Merge of the S split partials of one row, four fp32 columns (4 c4 ..
+// 4 c4 + 3) per lane, by the merge rule of Lesson 22, section 22: keep the
+// largest partial logsumexp M seen so far, scale what was accumulated by
+// e^(M_old - M_new) when it grows, and add each partial output with weight
+// e^(lse_s - M).  At the end O = sum_s e^(lse_s - M) O_s / sum_s e^(lse_s - M)
+// and lse = M + ln sum_s e^(lse_s - M).  Partials with lse_s = -inf are empty
+// and skipped without reading their O_s; a row with no non-empty partial
+// gets O = 0 and lse = -inf.  Partial s of row `row` sits at s rows + row.
+template <int D>
+__device__ __forceinline__ void merge_row(const float* __restrict__ opart,
+                                          const float* __restrict__ lpart, __bf16* __restrict__ O,
+                                          float* __restrict__ lse, int S, long long rows,
+                                          long long row, int c4)
+{
+    float M = kNegInf, l = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) {
+        const size_t pr = (size_t)s * rows + row;
+        const float ls = lpart[pr];
+        if (ls == kNegInf) continue;
+        const f32x4 o = *reinterpret_cast<const f32x4*>(opart + pr * D + 4 * c4);
+        if (ls > M) {
+            const float a = exp2_hw((M - ls) * kLog2e);  // M = -inf gives 0
+            acc *= a;
+            l *= a;
+            M = ls;
+        }
+        const float w = exp2_hw((ls - M) * kLog2e);
+        acc += w * o;
+        l += w;
+    }
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const bf16x4 ob = __builtin_convertvector(acc * inv, bf16x4);
+    *reinterpret_cast<bf16x4*>(O + (size_t)row * D + 4 * c4) = ob;
+    if (c4 == 0) lse[row] = l > 0.f ? M + logf(l) : kNegInf;
+}
+
+// With SPLIT (dense only) the workgroup computes one of nsplit contiguous
+// ranges of its query block's key tiles and writes the normalised partial
+// output in fp32 and the partial logsumexp (-inf for a row that sees no key
+// of the range) to opart [nsplit][BH][N][D] and lpart [nsplit][BH][N];
+// attn_combine_kernel merges them.
+template <int D, bool CAUSAL, bool VARLEN, bool SPLIT = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                         const __bf16* __restrict__ V, __bf16* __restrict__ O,
                         float* __restrict__ lse, int Nmax, int BH, int nqt, float scale,
-                        const int* __restrict__ cu, int H, int Hkv, int total)
+                        const int* __restrict__ cu, int H, int Hkv, int total,
+                        float* __restrict__ opart, float* __restrict__ lpart, int nsplit)
 {
+    static_assert(!(SPLIT && VARLEN), "split-KV runs on dense tensors");
     // Keys per step: 128 at D = 64 (its 64-key steps are half as long as at
     // D = 128, so the per-step costs weigh twice as much), 64 at D = 128
     // (128-key steps there need more than 256 registers).
@@ -662,7 +646,10 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool late = wave >= NW / 2;  // runs each phase one step after its SIMD partner
     const int j = lane & 31, h = lane >> 5;
-    const int t = blockIdx.x / BH, bh = blockIdx.x - t * BH;
+    // Workgroup id = t * BH + bh, or with SPLIT (t * nsplit + split) * BH + bh.
+    const int tt = blockIdx.x / BH, bh = blockIdx.x - tt * BH;
+    const int t = SPLIT ? tt / nsplit : tt;
+    const int split = SPLIT ? tt - t * nsplit : 0;
     const int qt = CAUSAL ? nqt - 1 - t : t;
     const int q0 = qt * C::BR;
     const Slice sl = slice_of<D, VARLEN>(bh, Nmax, H, Hkv, cu, total);
@@ -687,10 +674,23 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     const float c = scale * kLog2e;
 
     const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
-    const int ntiles = (kv_end + BC - 1) / BC;
-    // This wave computes tiles 0 .. T - 1; only tile T - 1 can need a mask.
-    const int T = CAUSAL ? min(ntiles, qw0 / BC + 1) : ntiles;
-    const int kvm = (T - 1) * BC;
+    const int nvis = (kv_end + BC - 1) / BC;  // key tiles the block sees
+    // The workgroup's tiles are kt0 .. kt0 + ntiles - 1 (all nvis without
+    // SPLIT); the steps below count tiles from kt0.
+    int kt0 = 0, ntiles = nvis;
+    if constexpr (SPLIT) {
+        const int per = (nvis + nsplit - 1) / nsplit;
+        kt0 = min(nvis, split * per);
+        ntiles = min(nvis, kt0 + per) - kt0;
+    }
+    // This wave computes tiles 0 .. T - 1 (of the workgroup's); only tile
+    // T - 1 can need a mask.  Under SPLIT the first of a wave's tiles holds a
+    // key every row of the wave sees (its first key precedes the wave's rows),
+    // so its reference becomes finite there.
+    const int T = !CAUSAL ? ntiles
+                : SPLIT  ? max(0, min(ntiles, qw0 / BC + 1 - kt0))
+                         : min(ntiles, qw0 / BC + 1);
+    const int kvm = (kt0 + T - 1) * BC;
     const bool mask_last = (kvm + BC > N) || (CAUSAL && kvm + BC - 1 > qw0);
 
     // Tile loads.  The four waves that are about to run their matrix phase
@@ -739,7 +739,7 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     // which no later step reads, so the loads need no branch.
     static_assert(LPW >= 1 && LPW <= 4, "one to four loads per wave");
     auto load_part = [&](const __bf16* X, char* dst, int kt) __attribute__((always_inline)) {
-        const int kv0 = kt * BC;
+        const int kv0 = (kt0 + kt) * BC;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(
             X + sl.kvbase + (size_t)kv0 * D, kt < ntiles ? (uint32_t)(N - kv0) * D * 2 : 0u);
         lds_void_t* const d = (lds_void_t*)(dst + g * LPW * 1024);
@@ -946,13 +946,14 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     auto steps = [&](auto latec) __attribute__((always_inline)) {
         constexpr bool LATE = decltype(latec)::value;
         // step 0
+        // (under SPLIT a wave may have no tile of the range: T = 0)
         if constexpr (!LATE) {
             if (1 < ntiles) load_part(K, kbuf1, 1);
-            first_matrix_phase();
+            if (!SPLIT || T > 0) first_matrix_phase();
             vector_phase(0);
         } else {
             load_part(V, vbuf0, 0);
-            first_matrix_phase();
+            if (!SPLIT || T > 0) first_matrix_phase();
         }
         __syncthreads();  // K(1) and V(0) have landed
         for (int i = 1; i <= ntiles; i += 2) {
@@ -988,9 +989,33 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     else
         steps(std::false_type{});
 
+    const float l_tot = combine_xor32(l, SumOp());
+    if constexpr (SPLIT) {
+        // Partial of this key range: O_s = acc / l in fp32 straight from the
+        // registers (lane (j, h): row qw0 + j, columns 32 dt + 8 g + 4 h ..
+        // + 3), lse_s = m scale + ln l, or O_s = 0 and -inf for a row that saw
+        // no key of the range.
+        const size_t pslice = (size_t)split * BH + bh;
+        const __amdgpu_buffer_rsrc_t prs = make_rsrc(opart + pslice * N * D, (uint32_t)N * D * 4);
+        const __amdgpu_buffer_rsrc_t plrs = make_rsrc(lpart + pslice * N, (uint32_t)N * 4);
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 o4 = {acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv,
+                                  acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), prs,
+                                                       (uint32_t)(qrow * D + dt * 32 + 8 * g + 4 * h) * 4, 0, 0);
+            }
+        if (h == 0) {
+            const float ls = l_tot > 0.f ? m * scale + logf(l_tot) : kNegInf;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ls), plrs, (uint32_t)qrow * 4, 0, 0);
+        }
+        return;
+    }
     const __amdgpu_buffer_rsrc_t ors = make_rsrc(O + base, slice_b);
     const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lse + sl.lbase, (uint32_t)N * 4);
-    const float l_tot = combine_xor32(l, SumOp());
     __syncthreads();  // every wave is done with the tile buffers
     store_tile_rows<D>(acc, 1.0f / l_tot, out_stage<D>(wave, kbuf0, kbuf1, vbuf0, vbuf1), ors, qw0, lane);
     if (h == 0)
@@ -1010,7 +1035,7 @@ hipError_t launch_pp(const void* Q, const void* K, const void* V, void* O, float
     const dim3 grid((unsigned)(nqt * BH)), block(512);
     attn_fwd_bf16_pp_kernel<D, CAUSAL, VARLEN><<<grid, block, 0, stream>>>(
         static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
-        static_cast<__bf16*>(O), lse, N, BH, nqt, scale, cu, H, Hkv, total);
+        static_cast<__bf16*>(O), lse, N, BH, nqt, scale, cu, H, Hkv, total, nullptr, nullptr, 1);
     return hipGetLastError();
 }
 
@@ -1022,9 +1047,9 @@ hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* l
     using C = Cfg<D, QT, NW, BC, KS>;
     const int nqt = (N + C::BR - 1) / C::BR;
     const dim3 grid((unsigned)(nqt * BH)), block(C::T);
-    attn_fwd_bf16_kernel<D, QT, NW, WPE, BC, CAUSAL, false, VARLEN, KS><<<grid, block, 0, stream>>>(
+    attn_fwd_bf16_kernel<D, QT, NW, WPE, BC, CAUSAL, VARLEN, KS><<<grid, block, 0, stream>>>(
         static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
-        static_cast<__bf16*>(O), lse, N, BH, nqt, scale, nullptr, nullptr, 1, cu, H, Hkv, total);
+        static_cast<__bf16*>(O), lse, N, BH, nqt, scale, cu, H, Hkv, total);
     return hipGetLastError();
 }
 
@@ -1043,7 +1068,6 @@ hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* l
 //  * below that 64-row workgroups of 4 waves in two key groups (+21-47%
 //    over 2 waves with the whole key loop on [2, 8, 1024, 64],
 //    [1, 8, 2048, 128] and [1, 2, 8192, 128]).
-// The plain kernel also runs the split-KV partial pass.
 template <int D, bool CAUSAL, bool VARLEN = false>
 hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
                     int N, float scale, hipStream_t stream, int H = 1, int Hkv = 1,
@@ -1059,15 +1083,8 @@ hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float*
     return launch<D, 1, 4, 2, 64, CAUSAL, VARLEN, 2>(Q, K, V, O, lse, BH, N, scale, cu, H, Hkv, total, stream);
 }
 
-// Merge of split partials, one row per D / 4 lanes (four fp32 columns per
-// lane).  The partials are folded in one pass with the merge rule of Lesson
-// 22, section 22: keep the largest partial logsumexp M seen so far, scale
-// what was accumulated by e^(M_old - M_new) when it grows, and add each
-// partial output with weight e^(lse_s - M).  At the end
-// O = sum_s e^(lse_s - M) O_s / sum_s e^(lse_s - M) and
-// lse = M + ln sum_s e^(lse_s - M).  Partials with lse_s = -inf are empty and
-// skipped without reading their O_s; a row with no non-empty partial gets
-// O = 0 and lse = -inf.  Rows are walked grid-stride.
+// Merge of split partials (attn_combine): merge_row for every row, D / 4
+// lanes per row, rows walked grid-stride.
 template <int D>
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(const float* __restrict__ opart, const float* __restrict__ lpart,
@@ -1077,29 +1094,8 @@ attn_combine_kernel(const float* __restrict__ opart, const float* __restrict__ l
     constexpr int RPB = 256 / LPR;     // rows per workgroup and pass
     const int c4 = threadIdx.x % LPR;  // column group of this lane
     for (long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR; row < rows;
-         row += (long long)gridDim.x * RPB) {
-        float M = kNegInf, l = 0.f;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < S; ++s) {
-            const size_t pr = (size_t)s * rows + row;
-            const float ls = lpart[pr];
-            if (ls == kNegInf) continue;
-            const f32x4 o = *reinterpret_cast<const f32x4*>(opart + pr * D + 4 * c4);
-            if (ls > M) {
-                const float a = exp2_hw((M - ls) * kLog2e);  // M = -inf gives 0
-                acc *= a;
-                l *= a;
-                M = ls;
-            }
-            const float w = exp2_hw((ls - M) * kLog2e);
-            acc += w * o;
-            l += w;
-        }
-        const float inv = l > 0.f ? 1.0f / l : 0.f;
-        const bf16x4 ob = __builtin_convertvector(acc * inv, bf16x4);
-        *reinterpret_cast<bf16x4*>(O + (size_t)row * D + 4 * c4) = ob;
-        if (c4 == 0) lse[row] = l > 0.f ? M + logf(l) : kNegInf;
-    }
+         row += (long long)gridDim.x * RPB)
+        merge_row<D>(opart, lpart, O, lse, S, rows, row, c4);
 }
 
 // Split-KV forward: 8-wave workgroups (256 query rows) over nsplit key ranges
@@ -1109,13 +1105,19 @@ hipError_t launch_split(const void* Q, const void* K, const void* V, void* O, fl
                         int N, float scale, int nsplit, float* opart, float* lpart, int H, int Hkv,
                         hipStream_t stream)
 {
-    using C = Cfg<D, 1, 8, 64>;
-    const int nqt = (N + C::BR - 1) / C::BR;
-    attn_fwd_bf16_kernel<D, 1, 8, 2, 64, CAUSAL, true, false>
-        <<<dim3((unsigned)(nqt * nsplit * BH)), dim3(C::T), 0, stream>>>(
+    // Partial pass: the phase-staggered kernel over (256-row query block,
+    // key range) workgroups, longest blocks first under the mask; then the
+    // merge over all rows.  (Merging each block in the last of its
+    // workgroups to finish, behind a per-block counter, was measured 1.7-6x
+    // slower: one workgroup's serial loads cannot move a block's nsplit fp32
+    // partials, ~1 MiB at d = 128, in the time the whole-chip merge takes.)
+    constexpr int BR = 256;
+    const int nqt = (N + BR - 1) / BR;
+    attn_fwd_bf16_pp_kernel<D, CAUSAL, false, true>
+        <<<dim3((unsigned)(nqt * nsplit * BH)), dim3(512), 0, stream>>>(
             static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K),
-            static_cast<const __bf16*>(V), nullptr, nullptr, N, BH, nqt, scale, opart, lpart,
-            nsplit, nullptr, H, Hkv, 0);
+            static_cast<const __bf16*>(V), nullptr, nullptr, N, BH, nqt, scale, nullptr, H, Hkv, 0,
+            opart, lpart, nsplit);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_attn_combine(opart, lpart, O, lse, nsplit, (long long)BH * N, D, stream);

@@ -132,16 +132,18 @@ def test_valid_call_without_a_gpu_fails_loudly(abi):
 def test_splitkv_plan(abi):
     # Explicit counts are kept; the workspace holds nsplit fp32 partial
     # outputs and logsumexps per row, none when the count is 1.
+    def ws(ns, bh, N, d):  # fp32 partial outputs and logsumexps
+        return ns * bh * N * (d + 1) * 4
     assert abi.attn_fwd_splitkv_plan(2, 8, 1024, 64, False, 1) == (1, 0)
-    assert abi.attn_fwd_splitkv_plan(2, 8, 1024, 64, False, 3) == (3, 3 * 16 * 1024 * 65 * 4)
-    assert abi.attn_fwd_splitkv_plan(1, 2, 777, 128, True, 64) == (64, 64 * 2 * 777 * 129 * 4)
+    assert abi.attn_fwd_splitkv_plan(2, 8, 1024, 64, False, 3) == (3, ws(3, 16, 1024, 64))
+    assert abi.attn_fwd_splitkv_plan(1, 2, 777, 128, True, 64) == (64, ws(64, 2, 777, 128))
     # Automatic choice: no split once 256-row blocks fill the 256 CUs ...
     assert abi.attn_fwd_splitkv_plan(2, 16, 4096, 128, True, 0) == (1, 0)
     assert abi.attn_fwd_splitkv_plan(1, 32, 8192, 128, True, 0) == (1, 0)
     # ... below that, a split that brings the partial pass to 2048 waves of
     # 32 rows (twice that under the causal mask), at least 512 keys per range ...
-    ns, ws = abi.attn_fwd_splitkv_plan(1, 2, 8192, 128, False, 0)
-    assert ns == 4 and ws == 4 * 2 * 8192 * 129 * 4
+    ns, wsb = abi.attn_fwd_splitkv_plan(1, 2, 8192, 128, False, 0)
+    assert ns == 4 and wsb == ws(4, 2, 8192, 128)
     assert abi.attn_fwd_splitkv_plan(1, 2, 8192, 128, True, 0)[0] == 8
     assert abi.attn_fwd_splitkv_plan(1, 1, 32768, 64, False, 0)[0] == 2
     assert abi.attn_fwd_splitkv_plan(1, 1, 32768, 64, True, 0)[0] == 4

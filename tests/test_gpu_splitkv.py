@@ -125,6 +125,33 @@ def test_splitkv_deterministic_and_one_split_is_attn_fwd(osm):
     assert torch.equal(O3, O4) and torch.equal(l3, l4)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_splitkv_workspace_contents_do_not_matter(osm, causal):
+    # A workspace full of arbitrary bytes, then the same workspace again
+    # (now holding the previous call's partials), and a call with another
+    # split count in between: every call matches the oracle, and equal
+    # counts give equal bits.
+    B, H, N, d = 1, 2, 2000, 128
+    q, k, v = _inputs(B, H, N, d, seed=3000 + int(causal))
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    ws_bytes = max(osm.attn_fwd_splitkv_plan(B, H, N, d, causal, n)[1] for n in (5, 3))
+    ws = torch.full((ws_bytes,), 0xA5, dtype=torch.uint8, device=dev)
+    Oref, lref = oracle.attn_fwd(q, k, v, 1.0 / math.sqrt(d), causal)
+    outs = []
+    for n in (5, 5, 3, 5):
+        O, lse = osm.attention_splitkv(qd, kd, vd, causal=causal, nsplit=n, workspace=ws)
+        torch.cuda.synchronize()
+        On, ln = O.to(torch.float64).cpu().numpy(), lse.to(torch.float64).cpu().numpy()
+        eo, el = _maxabs(On, Oref), _maxabs(ln, lref)
+        print(f"splitkv reuse nsplit={n} causal={causal}: max|dO|={eo:.3e} max|dlse|={el:.3e}",
+              flush=True)
+        assert eo <= TOL_O and el <= TOL_LSE
+        outs.append((O, lse))
+    for i in (1, 3):
+        assert torch.equal(outs[0][0], outs[i][0]) and torch.equal(outs[0][1], outs[i][1])
+
+
 def _oracle_partials(q, k, v, shards, scale):
     # Partials over disjoint key sets of a non-causal problem, from the oracle
     # (each shard holds as many keys as there are queries), rounded to fp32.

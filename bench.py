@@ -49,6 +49,7 @@ METRIC = "attn fwd TFLOPS & % bf16 MFMA peak (B·H=32,N=4096,d=128); softmax GB/
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix-core peak
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix-core peak
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -251,8 +252,9 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10, warm_ms=15.
     softmax input (the practical ceiling for a read-once / write-once
     kernel on this GPU), the split-KV forward on long rows, the backward pass
     of the headline workload (its FLOPs counted as 2.5 times the forward's,
-    the five products of the gradient; the kernels compute seven), and the
-    split backward on the long-row input."""
+    the five products of the gradient; the kernels compute seven), the
+    split backward on the long-row input, and the fp8 forward on the headline
+    shape."""
     import torch
 
     from online_softmax_08_amd import inputs
@@ -372,7 +374,23 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10, warm_ms=15.
             "nsplit": ns, "split_tflops": round(flops / (t_split * 1e-3) / 1e12, 1),
             "unsplit_tflops": round(flops / (t_one * 1e-3) / 1e12, 1),
             "split_ms": round(t_split, 4), "unsplit_ms": round(t_one, 4)}
+    # The fp8 forward on the headline workload's shape and recipe (every
+    # 64th query row x8), each tensor stored as E4M3 with its own scale,
+    # with and without the mask; FLOPs as for bf16, against the fp8 peak.
+    (q8, k8, v8), sc8 = inputs.attn_inputs_fp8(wa)
+    q8, k8, v8 = q8.to(q.device), k8.to(q.device), v8.to(q.device)
+    fp8 = {"workload": f"fp8 (E4M3, per-tensor scales) B={wa.B} H={wa.H} N={wa.N} d={wa.d}, "
+                       f"every {wa.boost_every}th query row x{wa.boost:g}",
+           "peak_tflops": PEAK_FP8_TFLOPS}
+    for causal in (False, True):
+        t = launch_times(lambda: osm.attention_fp8(q8, k8, v8, *sc8, causal=causal))
+        flops = 4.0 * wa.B * wa.H * wa.N * wa.N * wa.d / (2 if causal else 1)
+        tf = flops / (median(t) * 1e-3) / 1e12
+        fp8["causal" if causal else "noncausal"] = {
+            "tflops_median": round(tf, 1), "frac_median": round(tf / PEAK_FP8_TFLOPS, 4),
+            "ms_median": round(median(t), 4), "ms_min": round(min(t), 4)}
     return {
+        "attn_fp8": fp8,
         "attn_backward": {"workload": f"{wa.name} backward (dQ, dK, dV)",
                           "value": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 1), "unit": "TFLOPS",
                           "flops_per_call": bwd_flops, "call_ms": round(bwd_ms, 4)},

@@ -23,6 +23,13 @@
  *    head h / (H / Hkv).  Every key/value-head argument below has this
  *    meaning; Hkv = H is attn_fwd.
  *
+ *  attn_fwd_fp8
+ *    The same attention with Q, K and V stored as 8-bit floats (OCP FP8
+ *    E4M3) and one scale per tensor, both products on the fp8 matrix cores:
+ *    the FP8 variant of "Moving less: four generations of FlashAttention",
+ *    section 4.6.  Its own tolerance, from the rounding of the
+ *    probabilities to fp8, is stated with the function below.
+ *
  *  attn_fwd_varlen
  *    The same attention over a batch of sequences of different lengths
  *    packed end to end with no padding: the padding mask of Lesson 22,
@@ -128,6 +135,36 @@ int attn_fwd_f32(const float* Q, const float* K, const float* V, float* O, float
  */
 int attn_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* lse,
                  int B, int H, int Hkv, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * attn_fwd_fp8 -- attention forward on fp8 inputs.
+ *   Q : uint8 [B][H][N][d], K, V : uint8 [B][Hkv][N][d], each byte an OCP
+ *       FP8 E4M3 code (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ *       subnormals below exponent 1; S.1111.111 is NaN, no infinities; the
+ *       largest finite magnitude is 448).  Element x of Q stands for
+ *       decode(x) * q_scale, of K for decode(x) * k_scale, of V for
+ *       decode(x) * v_scale.  NaN codes give undefined results.
+ *   q_scale, k_scale, v_scale : finite and > 0 (else OSM_ERR_SCALE), as is
+ *       scale * q_scale * k_scale
+ *   O   : bf16 [B][H][N][d], lse : fp32 [B][H][N]: the attention of attn_fwd
+ *       (with the same scale and mask) on the decoded, scaled inputs.
+ *   Hkv, B, H, N, d, scale, causal, stream : as for attn_fwd_gqa.
+ * The matrix cores form the fp8 products exactly and sum each 64-term block
+ * at reduced precision (measured on gfx950: up to ~2e-5 of the block's sum
+ * of |products| on Gaussian data, 1e-4 on arbitrary codes), so a score
+ * errs by up to ~1e-4 * scale * sum_d |q_d k_d| and lse by as much.  The
+ * probabilities enter the P V product rounded to fp8 (E4M3, relative error
+ * up to 2^-4; each is kept at or below 28 times its row's running maximum,
+ * and values below 2^-13 of it may round to zero), and the row sums use them
+ * unrounded, so each element of O carries an error of about
+ * 2^-4 sqrt(sum_j (P_ij V_jt)^2 / 3) (a sum of independent roundings)
+ * besides the score error's share and its bf16 rounding.
+ * Q, K, V, O need 16-byte alignment, lse 4; O and lse may not overlap the
+ * inputs or each other.  Returns an osm_status.
+ */
+int attn_fwd_fp8(const void* Q, const void* K, const void* V, float q_scale, float k_scale,
+                 float v_scale, void* O, float* lse, int B, int H, int Hkv, int N, int d,
+                 float scale, int causal, void* stream);
 
 /*
  * attn_fwd_varlen -- attn_fwd over packed variable-length sequences.

@@ -36,6 +36,8 @@ _lib.attn_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _
 _lib.attn_fwd_varlen.restype = _i
 _lib.attn_fwd_gqa.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]
 _lib.attn_fwd_gqa.restype = _i
+_lib.attn_fwd_fp8.argtypes = [_vp, _vp, _vp, _f, _f, _f, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]
+_lib.attn_fwd_fp8.restype = _i
 _lib.attn_fwd_splitkv_plan.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(_i),
                                        ctypes.POINTER(_sz)]
 _lib.attn_fwd_splitkv_plan.restype = _i
@@ -64,7 +66,7 @@ _lib.attn_bwd_varlen.restype = _i
 _lib.osm_status_str.argtypes = [_i]
 _lib.osm_status_str.restype = ctypes.c_char_p
 
-EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_gqa", "attn_fwd_varlen", "attn_fwd_splitkv_plan", "attn_fwd_splitkv",
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_gqa", "attn_fwd_fp8", "attn_fwd_varlen", "attn_fwd_splitkv_plan", "attn_fwd_splitkv",
            "attn_combine", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_varlen",
            "attn_bwd_split_plan", "attn_bwd_split", "row_softmax", "osm_status_str")
 
@@ -184,6 +186,14 @@ def attn_bwd_split(Q: int, K: int, V: int, O: int, dO: int, lse: int, dQ: int, d
     ranges and the fp32 partials summed; see include/osm.h."""
     _call("attn_bwd_split", Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale,
           int(bool(causal)), nsplit, workspace, workspace_bytes, stream)
+
+
+def attn_fwd_fp8(Q: int, K: int, V: int, q_scale: float, k_scale: float, v_scale: float, O: int,
+                 lse: int, B: int, H: int, Hkv: int, N: int, d: int, scale: float, causal: bool,
+                 stream: int = 0) -> None:
+    """Attention forward on OCP FP8 E4M3 inputs with per-tensor scales; see include/osm.h."""
+    _call("attn_fwd_fp8", Q, K, V, q_scale, k_scale, v_scale, O, lse, B, H, Hkv, N, d, scale,
+          int(bool(causal)), stream)
 
 
 def attn_fwd_varlen(Q: int, K: int, V: int, O: int, lse: int, cu_seqlens: int, B: int, H: int,

@@ -150,6 +150,37 @@ int attn_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* ls
                                             static_cast<hipStream_t>(stream)));
 }
 
+int attn_fwd_fp8(const void* Q, const void* K, const void* V, float q_scale, float k_scale,
+                 float v_scale, void* O, float* lse, int B, int H, int Hkv, int N, int d,
+                 float scale, int causal, void* stream)
+{
+    // Sizes as for the bf16 call (the bf16 output's slice bytes bound the
+    // 32-bit offsets); one byte per input element.
+    int st = check_attn_shape(B, H, N, d, scale, 2);
+    if (st != OSM_OK || B == 0 || H == 0 || N == 0) return st;
+    if (!(std::isfinite(q_scale) && q_scale > 0.f && std::isfinite(k_scale) && k_scale > 0.f &&
+          std::isfinite(v_scale) && v_scale > 0.f))
+        return OSM_ERR_SCALE;
+    if (!(std::isfinite(scale * q_scale * k_scale) && scale * q_scale * k_scale > 0.f))
+        return OSM_ERR_SCALE;
+    if ((st = check_heads(H, Hkv)) != OSM_OK) return st;
+    if (!Q || !K || !V || !O || !lse) return OSM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(lse, 4))
+        return OSM_ERR_ALIGN;
+    const long long bh = (long long)B * H;
+    const size_t qbytes = (size_t)bh * N * d, kvbytes = (size_t)B * Hkv * N * d;
+    const size_t obytes = (size_t)bh * N * d * 2, lbytes = (size_t)bh * N * sizeof(float);
+    if (overlaps(O, obytes, Q, qbytes) || overlaps(O, obytes, K, kvbytes) ||
+        overlaps(O, obytes, V, kvbytes) || overlaps(lse, lbytes, Q, qbytes) ||
+        overlaps(lse, lbytes, K, kvbytes) || overlaps(lse, lbytes, V, kvbytes) ||
+        overlaps(lse, lbytes, O, obytes))
+        return OSM_ERR_ALIAS;
+    if ((st = check_device()) != OSM_OK) return st;
+    return finish(osm::launch_attn_fwd_fp8(Q, K, V, O, lse, B, H, Hkv, N, d,
+                                           scale * q_scale * k_scale, v_scale, causal != 0,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int attn_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* lse, int B,
                  int H, int N, int d, float scale, int causal, void* stream)
 {

@@ -60,6 +60,12 @@ hipError_t launch_attn_bwd_bf16_varlen(const void* Q, const void* K, const void*
                                        void* dV, const int* cu, int B, int H, int Hkv, int total,
                                        int max_seqlen, int d, float scale, bool causal, float* Dl,
                                        float* Lc, hipStream_t stream);
+// fp8 forward: Q [B*H][N][d], K, V [B*Hkv][N][d] as OCP FP8 E4M3 bytes, O
+// bf16 and lse fp32 as for the bf16 call; qk_scale = scale * q_scale *
+// k_scale multiplies the raw fp8 dot products, v_scale the output.
+hipError_t launch_attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* lse,
+                               int B, int H, int Hkv, int N, int d, float qk_scale, float v_scale,
+                               bool causal, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const float* Q, const float* K, const float* V, float* O,
                                float* lse, int BH, int N, int d, float scale, bool causal,
                                hipStream_t stream);

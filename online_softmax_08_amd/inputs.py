@@ -124,6 +124,39 @@ def attn_inputs(w: AttnWorkload, *, B: int | None = None, H: int | None = None,
     return q, k, v
 
 
+def fp8_quantize(t: torch.Tensor):
+    """Per-tensor FP8 (E4M3) storage of ``t``: the scale that maps the
+    largest magnitude to 448 (1 for an all-zero tensor) and the codes of
+    t / scale (round to nearest even), as uint8.  Returns (codes, scale)."""
+    amax = float(t.abs().max()) if t.numel() else 0.0
+    scale = amax / 448.0 if amax > 0 else 1.0
+    codes = (t.to(torch.float32) / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.contiguous(), scale
+
+
+def attn_inputs_fp8(w: AttnWorkload, *, B: int | None = None, H: int | None = None,
+                    N: int | None = None, d: int | None = None, seed: int | None = None,
+                    Hkv: int | None = None):
+    """FP8 inputs for workload ``w``: the fp32 draws of attn_inputs (same
+    seed, boosted rows included), each tensor stored as E4M3 codes with its own
+    scale (fp8_quantize); K and V keep their first Hkv heads.  Returns
+    ((q8, k8, v8), (q_scale, k_scale, v_scale)) as CPU tensors and floats."""
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    N = w.N if N is None else N
+    d = w.d if d is None else d
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    shape = (B, H, N, d)
+    q, k, v = (torch.randn(shape, generator=g, dtype=torch.float32) for _ in range(3))
+    if w.boost_every > 0 and N > 0:
+        q[:, :, ::w.boost_every, :] *= w.boost
+    if Hkv is not None:
+        k, v = k[:, :Hkv].contiguous(), v[:, :Hkv].contiguous()
+    (q8, qs), (k8, ks), (v8, vs) = fp8_quantize(q), fp8_quantize(k), fp8_quantize(v)
+    return (q8, k8, v8), (qs, ks, vs)
+
+
 def grad_output(shape, seed: int, dtype: str = "bf16") -> torch.Tensor:
     """The upstream gradient dO for a backward test: N(0, 1) of ``shape`` from
     its own generator (seed), so Q, K, V stay those of the forward recipe."""

@@ -63,6 +63,35 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     return out, lse
 
 
+def attention_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_scale: float,
+                  k_scale: float, v_scale: float, causal: bool = False,
+                  scale: float | None = None):
+    """attention() on fp8 inputs: q [B, H, N, d], k, v [B, Hkv, N, d] holding OCP
+    FP8 E4M3 codes (torch.uint8 or torch.float8_e4m3fn, contiguous, on one GPU),
+    each element standing for its decoded value times the tensor's scale.
+    Returns (O bf16 [B, H, N, d], lse fp32 [B, H, N]); scale defaults to
+    1/sqrt(d).
+    """
+    ts = (q, k, v)
+    if not all(t.is_cuda for t in ts):
+        raise ValueError("q, k, v must be GPU tensors")
+    if not all(t.dtype in (torch.uint8, torch.float8_e4m3fn) for t in ts):
+        raise ValueError("q, k, v must hold FP8 E4M3 codes (uint8 or float8_e4m3fn)")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or not all(t.is_contiguous() for t in ts):
+        raise ValueError("q must be [B, H, N, d] and k, v one [B, Hkv, N, d] shape, contiguous")
+    B, H, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d or k.shape[1] < 1 or H % k.shape[1]:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hkv dividing q's H")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        _abi.attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), float(q_scale), float(k_scale),
+                          float(v_scale), out.data_ptr(), lse.data_ptr(), B, H, k.shape[1], N, d,
+                          scale, causal, _stream_handle(q.device))
+    return out, lse
+
+
 def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = False,
                      scale: float | None = None):

@@ -70,9 +70,11 @@ class Oracle:
         lib.oracle_attn_merge.argtypes = [_dp, _dp, _dp, _dp, _L, _L, _L]
         lib.oracle_attn_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _L, _L, _L, _L,
                                         ctypes.c_double, ctypes.c_int]
+        lib.oracle_fp8_e4m3_decode.argtypes = [ctypes.POINTER(ctypes.c_ubyte), ctypes.c_double,
+                                               _dp, _L]
         for name in ("oracle_row_softmax", "oracle_attn_fwd", "oracle_attn_rows",
                      "oracle_online_row_trace", "oracle_attn_online", "oracle_attn_merge",
-                     "oracle_attn_bwd"):
+                     "oracle_attn_bwd", "oracle_fp8_e4m3_decode"):
             getattr(lib, name).restype = ctypes.c_int
         self._lib = lib
 
@@ -172,6 +174,29 @@ class Oracle:
                                            S, rows, d), "attn_merge")
         return O, lse
 
+    def fp8_decode(self, codes, s: float = 1.0) -> np.ndarray:
+        """float64 values of FP8 E4M3 codes (uint8 or torch float8_e4m3fn
+        storage, any shape) times s (the FP8 variant of "Moving less",
+        section 4.6; encoding in ``oracle.c``)."""
+        try:
+            import torch
+            if isinstance(codes, torch.Tensor):
+                codes = codes.detach().to("cpu").contiguous().view(torch.uint8).numpy()
+        except ImportError:  # pragma: no cover
+            pass
+        x = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+        y = np.empty(x.shape, dtype=np.float64)
+        _check(self._lib.oracle_fp8_e4m3_decode(x.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte)),
+                                                float(s), _ptr(y), _L(x.size)), "fp8_decode")
+        return y
+
+    def attn_fwd_fp8(self, Q8, K8, V8, q_scale: float, k_scale: float, v_scale: float,
+                     scale: float, causal: bool):
+        """attn_fwd on the decoded, scaled FP8 inputs (Q8, K8, V8: E4M3 codes of
+        one shape [B, H, N, d]).  Returns (O, lse)."""
+        return self.attn_fwd(self.fp8_decode(Q8, q_scale), self.fp8_decode(K8, k_scale),
+                             self.fp8_decode(V8, v_scale), scale, causal)
+
     def attn_bwd(self, Q, K, V, dO, scale: float, causal: bool):
         """Gradients of sum(dO * O) with respect to Q, K, V for the attention
         forward, by the chain rule with the probabilities recomputed from Q
@@ -229,6 +254,14 @@ def attn_online(Q, K, V, scale, causal, br, bc):
 
 def attn_merge(O_part, lse_part):
     return default().attn_merge(O_part, lse_part)
+
+
+def fp8_decode(codes, s=1.0):
+    return default().fp8_decode(codes, s)
+
+
+def attn_fwd_fp8(Q8, K8, V8, q_scale, k_scale, v_scale, scale, causal):
+    return default().attn_fwd_fp8(Q8, K8, V8, q_scale, k_scale, v_scale, scale, causal)
 
 
 def attn_bwd(Q, K, V, dO, scale, causal):

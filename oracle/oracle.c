@@ -472,3 +472,30 @@ int oracle_attn_bwd(const double *Q, const double *K, const double *V,
     free(dS);
     return failed ? -2 : 0;
 }
+
+/* ------------------------------------------------------------------------ *
+ * FP8 inputs ([GEN] section 4.6, the FP8 variant: Q, K and V stored as 8-bit
+ * floats with a scale per tensor).  The pages name the format but not its
+ * encoding; the encoding here is the 8-bit E4M3 one: sign bit, 4 exponent
+ * bits with bias 7, 3 mantissa bits; exponent field 0 holds the subnormals
+ * m * 2^-9; exponent field 15 with mantissa 7 is NaN and there are no
+ * infinities, so the largest magnitude is 1.75 * 2^8 = 448.
+ *   y_i = value(x_i) * s
+ * The attention on the decoded values is oracle_attn_fwd itself.
+ * ------------------------------------------------------------------------ */
+int oracle_fp8_e4m3_decode(const unsigned char *x, double s, double *y, long n)
+{
+    if (!x || !y || n < 0) return -1;
+    for (long i = 0; i < n; ++i) {
+        const int sign = x[i] >> 7, e = (x[i] >> 3) & 15, m = x[i] & 7;
+        double v;
+        if (e == 15 && m == 7)
+            v = NAN;
+        else if (e == 0)
+            v = ldexp((double)m, -9);                 /* subnormal: m / 8 * 2^(1 - 7) */
+        else
+            v = ldexp(1.0 + (double)m / 8.0, e - 7);  /* normal: 1.m * 2^(e - 7) */
+        y[i] = (sign ? -v : v) * s;
+    }
+    return 0;
+}

@@ -516,4 +516,31 @@ def pin_bwd_invariants(orc):
     assert np.array_equal(dV, dO), "one key: dV = dO"
 
 
+# --------------------------------------------------------------- FP8 inputs --
+def pin_fp8_decode_values(orc):
+    # The E4M3 encoding written out: zero and negative zero, the smallest and
+    # largest subnormals (2^-9, 7 * 2^-9), the smallest normal 2^-6, 1, 1.5, 2,
+    # the largest finite 448 and its negative, the two NaN codes; and the
+    # scale multiplies.
+    codes = np.array([0x00, 0x80, 0x01, 0x07, 0x08, 0x38, 0x3C, 0x40, 0x7E, 0xFE, 0x7F, 0xFF],
+                     dtype=np.uint8)
+    want = [0.0, -0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.5, 2.0, 448.0, -448.0]
+    got = orc.fp8_decode(codes)
+    assert list(got[:10]) == want, got
+    assert np.signbit(got[1]) and np.isnan(got[10]) and np.isnan(got[11])
+    np.testing.assert_array_equal(orc.fp8_decode(codes[:10], 0.25), np.array(want) * 0.25)
+
+
+def pin_fp8_decode_library(orc):
+    # Every one of the 256 codes against torch's float8_e4m3fn conversion, an
+    # independent implementation of the same encoding.
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = orc.fp8_decode(codes)
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], lib[~nan])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -24,6 +24,7 @@ def abi():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_gqa",
+                                            "attn_fwd_fp8",
                                             "attn_fwd_varlen",
                                             "attn_fwd_splitkv_plan",
                                             "attn_fwd_splitkv", "attn_combine",
@@ -414,3 +415,33 @@ def test_bwd_split_validation(abi):
     assert status() in (abi.OSM_ERR_HIP, abi.OSM_ERR_DEVICE)
     assert status(nsplit=1, ws_bytes=2 * 2 * 1000 * 4) in (abi.OSM_ERR_HIP, abi.OSM_ERR_DEVICE)
     abi.attn_bwd_split(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 2, 2, 16, 64, 0.125, 1, 3, 0, 0)  # empty: no-op
+
+
+def test_fp8_validation(abi):
+    # attn_fwd_fp8 checks sizes, scales, pointers, alignment and overlaps
+    # (one byte per input element, two per output element) before any HIP
+    # call.
+    far = {n: (i + 1) << 36 for i, n in enumerate(("Q", "K", "V", "O", "lse"))}
+
+    def status(**kw):
+        a = dict(far, qs=0.01, ks=0.02, vs=0.03, B=1, H=4, Hkv=2, N=100, d=128, scale=0.125,
+                 causal=1)
+        a.update(kw)
+        with pytest.raises(abi.OsmError) as e:
+            abi.attn_fwd_fp8(a["Q"], a["K"], a["V"], a["qs"], a["ks"], a["vs"], a["O"], a["lse"],
+                             a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"])
+        return e.value.status
+    assert status(d=96) == abi.OSM_ERR_HEAD_DIM
+    assert status(N=-1) == abi.OSM_ERR_SIZE
+    assert status(scale=0.0) == abi.OSM_ERR_SCALE
+    assert status(qs=0.0) == abi.OSM_ERR_SCALE
+    assert status(vs=float("nan")) == abi.OSM_ERR_SCALE
+    assert status(ks=float("inf")) == abi.OSM_ERR_SCALE
+    assert status(qs=1e-30, ks=1e-30) == abi.OSM_ERR_SCALE   # scale * q_scale * k_scale underflows
+    assert status(Hkv=3) == abi.OSM_ERR_HEADS
+    assert status(V=0) == abi.OSM_ERR_NULL
+    assert status(K=far["K"] + 8) == abi.OSM_ERR_ALIGN
+    assert status(O=far["Q"] + 16 * 1024) == abi.OSM_ERR_ALIAS   # O inside Q's 51200 bytes
+    assert status(lse=far["O"] + 1024) == abi.OSM_ERR_ALIAS
+    assert status() in (abi.OSM_ERR_HIP, abi.OSM_ERR_DEVICE)
+    abi.attn_fwd_fp8(0, 0, 0, 1.0, 1.0, 1.0, 0, 0, 0, 4, 4, 128, 64, 0.125, 0)  # empty: no-op

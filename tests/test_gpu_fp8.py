@@ -1,0 +1,145 @@
+"""GPU parity of the fp8 attention forward (attn_fwd_fp8 through the C ABI)
+against the fp64 oracle on the decoded, scaled fp8 inputs.
+
+The reference is exact attention on the values the fp8 codes stand for
+(oracle.attn_fwd_fp8: the oracle's own E4M3 decoding, then oracle.attn_fwd).
+The kernel adds three roundings, each modelled from its definition or a
+measurement:
+  * the scores: the matrix cores form the fp8 products exactly but sum each
+    64-term block at reduced precision.  On this GPU the error of a 128-term
+    dot product measured at most 1.75e-5 of its sum of |products| on Gaussian
+    data stored as E4M3, 1e-4 on codes drawn at random from the whole range;
+    the bar takes EPS_S = 2^-13 of that sum:
+        dS_ij = EPS_S * scale * sum_d |Q_id K_jd|;
+    lse_i then moves by at most max_j dS_ij, O_it by at most
+    sum_j P_ij dS_ij |V_jt - O_it| <= sum_j P_ij dS_ij (|V_jt| + |O_it|);
+  * each probability rounded to fp8 before the P V product: E4M3 keeps 3
+    mantissa bits, so a normal value x rounds to nearest with an error up to
+    u8 x (u8 = 2^-4), of standard deviation u8 x / sqrt(3) for uniformly
+    placed x.  The kernel forms p' = 16 P / P_max or larger (its reference
+    trails the row maximum), so a probability below 2^-10 P_max may be
+    subnormal in fp8 and err by up to 2^-10 in p' units, at most 2^-14 P_max
+    in P.  Independent, zero-mean roundings give element (i, t) of O the
+    standard deviation
+        sigma_it = sqrt( sum_j (u8 P_ij V_jt)^2 / 3
+                         + sum_{j: P_ij < 2^-10 P_i,max} (2^-14 P_i,max V_jt)^2 / 3 );
+  * O rounded to bf16: 2^-8 |O_it|.
+The bars: |err O_it| <= 6 sigma_it + sum_j P_ij dS_ij (|V_jt| + |O_it|)
++ 2^-8 |O_it| + 1e-4, and |err lse_i| <= max_j dS_ij + 1e-4.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from online_softmax_08_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+U8 = 2.0 ** -4      # unit roundoff of E4M3 (3 mantissa bits)
+EPS_S = 2.0 ** -13  # score error per sum of |products| (fp8 matrix-core sums)
+ELEM_FACTOR = 6.0
+
+
+@pytest.fixture(scope="module")
+def osm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import online_softmax_08_amd
+    return online_softmax_08_amd
+
+
+def _gpu(osm, q8, k8, v8, sc, causal, scale):
+    dev = torch.device("cuda:0")
+    O, lse = osm.attention_fp8(q8.to(dev), k8.to(dev), v8.to(dev), *sc, causal=causal,
+                               scale=scale)
+    torch.cuda.synchronize()
+    return O.to(torch.float64).cpu().numpy(), lse.to(torch.float64).cpu().numpy()
+
+
+def _bars(Qd, Kd, Vd, scale, causal):
+    """Per-element bars of O and per-row bars of lse for one (b, h) slice (the
+    module docstring), from its decoded inputs in fp64."""
+    S = scale * (Qd @ Kd.T)
+    dS = EPS_S * scale * (np.abs(Qd) @ np.abs(Kd).T)
+    N = S.shape[0]
+    if causal:
+        hidden = np.triu(np.ones((N, N), dtype=bool), 1)
+        S[hidden] = -np.inf
+        dS[hidden] = 0.0
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    O = P @ Vd
+    pmax = P.max(axis=1, keepdims=True)
+    sub = ((P < 2.0 ** -10 * pmax) * (2.0 ** -14 * pmax)) ** 2
+    sigma = np.sqrt(((U8 * P) ** 2 @ Vd ** 2 + sub @ Vd ** 2) / 3.0)
+    PdS = P * dS
+    score_term = PdS @ np.abs(Vd) + PdS.sum(axis=1, keepdims=True) * np.abs(O)
+    o_bar = ELEM_FACTOR * sigma + score_term + 2.0 ** -8 * np.abs(O) + 1e-4
+    lse_bar = dS.max(axis=1) + 1e-4
+    return o_bar, lse_bar
+
+
+def _check(osm, q8, k8, v8, sc, causal, label, slices=None):
+    B, H, N, d = q8.shape
+    Hkv = k8.shape[1]
+    G = H // Hkv
+    scale = 1.0 / math.sqrt(d)
+    O, lse = _gpu(osm, q8, k8, v8, sc, causal, scale)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse)), label
+    worst, worst_lse = 0.0, 0.0
+    for (b, hh) in (slices or [(b, hh) for b in range(B) for hh in range(H)]):
+        qs, ks, vs = q8[b:b + 1, hh:hh + 1], k8[b:b + 1, hh // G:hh // G + 1], v8[b:b + 1, hh // G:hh // G + 1]
+        Oref, lref = oracle.attn_fwd_fp8(qs, ks, vs, *sc, scale, causal)
+        Qd, Kd, Vd = (oracle.fp8_decode(t, s)[0, 0] for t, s in zip((qs, ks, vs), sc))
+        o_bar, lse_bar = _bars(Qd, Kd, Vd, scale, causal)
+        r = np.abs(O[b, hh] - Oref[0, 0]) / o_bar
+        rl = np.abs(lse[b, hh] - lref[0, 0]) / lse_bar
+        worst = max(worst, float(r.max()) if r.size else 0.0)
+        worst_lse = max(worst_lse, float(rl.max()) if rl.size else 0.0)
+    print(f"{label}: max err/elem-bar O {worst:.3f} lse {worst_lse:.3f}", flush=True)
+    assert worst <= 1.0 and worst_lse <= 1.0, label
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 2, 1000, 64), (2, 1, 777, 128), (1, 1, 65, 128),
+                                   (1, 3, 1, 64), (1, 2, 256, 128), (1, 1, 300, 64)])
+def test_fp8_full(osm, shape, causal):
+    # Ragged N (partial last tiles, the causal diagonal in the last tile),
+    # both head sizes, one-row and one-block problems; every element.
+    B, H, N, d = shape
+    w = inputs.ATTN["attn_bf16_B2H8N1024d64" if d == 64 else "attn_bf16_B4H16N2048d128"]
+    (q8, k8, v8), sc = inputs.attn_inputs_fp8(w, B=B, H=H, N=N, d=d, seed=8000 + N + d)
+    _check(osm, q8, k8, v8, sc, causal, f"fp8 B{B}H{H}N{N}d{d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_grouped_heads(osm, causal):
+    # Four query heads on two key/value heads.
+    w = inputs.ATTN["attn_bf16_B4H16N2048d128"]
+    (q8, k8, v8), sc = inputs.attn_inputs_fp8(w, B=2, H=4, N=600, d=128, seed=8100, Hkv=2)
+    _check(osm, q8, k8, v8, sc, causal, f"fp8 GQA B2H4/2N600d128 causal={causal}")
+
+
+@pytest.mark.parametrize("shape", [(2, 16, 4096, 128), (2, 16, 4000, 128), (2, 16, 4000, 64)])
+def test_fp8_large_sampled_slices(osm, shape):
+    # The headline workload's shape and recipe (every 64th query row x8,
+    # causal), stored as fp8, and ragged N at both head sizes: the whole GPU
+    # problem, with four whole (b, h) slices recomputed by the oracle.
+    B, H, N, d = shape
+    w = inputs.ATTN[inputs.HEADLINE_ATTN]
+    (q8, k8, v8), sc = inputs.attn_inputs_fp8(w, B=B, H=H, N=N, d=d)
+    _check(osm, q8, k8, v8, sc, True, f"fp8 B{B}H{H}N{N}d{d} causal x8 rows",
+           slices=[(0, 0), (0, 7), (1, 9), (1, 15)])
+
+
+def test_fp8_deterministic(osm):
+    w = inputs.ATTN["attn_bf16_B4H16N2048d128"]
+    (q8, k8, v8), sc = inputs.attn_inputs_fp8(w, B=1, H=2, N=700, d=128, seed=8200)
+    a = _gpu(osm, q8, k8, v8, sc, True, 0.1)
+    b = _gpu(osm, q8, k8, v8, sc, True, 0.1)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -58,6 +58,13 @@ MUTANTS = [
     ("bwd_dv_transposed_p", "av += P[i * N + r] * dOs[i * d + t];", "av += P[r * N + i] * dOs[i * d + t];"),
     ("bwd_dp_from_keys", "for (long t = 0; t < d; ++t) dp += dOs[i * d + t] * Vs[j * d + t];",
      "for (long t = 0; t < d; ++t) dp += dOs[i * d + t] * Ks[j * d + t];"),
+    ("fp8_exponent_bias_8", "v = ldexp(1.0 + (double)m / 8.0, e - 7);",
+     "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    ("fp8_mantissa_over_16", "v = ldexp(1.0 + (double)m / 8.0, e - 7);",
+     "v = ldexp(1.0 + (double)m / 16.0, e - 7);"),
+    ("fp8_subnormal_scale", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    ("fp8_no_nan", "if (e == 15 && m == 7)", "if (e == 16)"),
+    ("fp8_scale_dropped", "y[i] = (sign ? -v : v) * s;", "y[i] = (sign ? -v : v);"),
 ]
 
 

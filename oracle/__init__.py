@@ -46,6 +46,21 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(_dp)
 
 
+def _u8(a) -> np.ndarray:
+    """Contiguous uint8 view of codes or scale bytes (numpy or torch storage)."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().to("cpu").contiguous().view(torch.uint8).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(a, dtype=np.uint8))
+
+
+def _bptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte))
+
+
 def _check(rc: int, what: str) -> None:
     if rc != 0:
         raise RuntimeError(f"oracle {what} failed with code {rc}")
@@ -72,9 +87,19 @@ class Oracle:
                                         ctypes.c_double, ctypes.c_int]
         lib.oracle_fp8_e4m3_decode.argtypes = [ctypes.POINTER(ctypes.c_ubyte), ctypes.c_double,
                                                _dp, _L]
+        _bp = ctypes.POINTER(ctypes.c_ubyte)
+        lib.oracle_fp8_e4m3_encode.argtypes = [_dp, ctypes.c_double, _bp, _L]
+        lib.oracle_hadamard_rotate.argtypes = [_dp, _dp, _dp, _L, _L]
+        lib.oracle_mx_quantize_rows.argtypes = [_dp, _bp, _bp, _L, _L]
+        lib.oracle_mx_quantize_cols.argtypes = [_dp, _bp, _bp, _L, _L, _L]
+        lib.oracle_mx_decode_rows.argtypes = [_bp, _bp, _dp, _L, _L]
+        lib.oracle_mx_decode_cols.argtypes = [_bp, _bp, _dp, _L, _L, _L]
         for name in ("oracle_row_softmax", "oracle_attn_fwd", "oracle_attn_rows",
                      "oracle_online_row_trace", "oracle_attn_online", "oracle_attn_merge",
-                     "oracle_attn_bwd", "oracle_fp8_e4m3_decode"):
+                     "oracle_attn_bwd", "oracle_fp8_e4m3_decode", "oracle_fp8_e4m3_encode",
+                     "oracle_hadamard_rotate", "oracle_mx_quantize_rows",
+                     "oracle_mx_quantize_cols", "oracle_mx_decode_rows",
+                     "oracle_mx_decode_cols"):
             getattr(lib, name).restype = ctypes.c_int
         self._lib = lib
 
@@ -197,6 +222,81 @@ class Oracle:
         return self.attn_fwd(self.fp8_decode(Q8, q_scale), self.fp8_decode(K8, k_scale),
                              self.fp8_decode(V8, v_scale), scale, causal)
 
+    def fp8_encode(self, x, s: float = 1.0) -> np.ndarray:
+        """E4M3 codes (uint8, shape of x) of x / s, rounded to the nearest
+        code with ties to the even code (encoding in ``oracle.c``)."""
+        x = _f64(x)
+        out = np.empty(x.shape, dtype=np.uint8)
+        _check(self._lib.oracle_fp8_e4m3_encode(_ptr(x), float(s), _bptr(out), _L(x.size)),
+               "fp8_encode")
+        return out
+
+    def hadamard_rotate(self, X, signs) -> np.ndarray:
+        """X [..., d] times diag(signs) H / sqrt(d), H the Sylvester Hadamard
+        matrix (incoherent processing, "Moving less", section 4.6)."""
+        X = _f64(X)
+        signs = _f64(signs)
+        d = X.shape[-1]
+        if signs.shape != (d,):
+            raise ValueError("signs must hold d values")
+        Y = np.empty_like(X)
+        _check(self._lib.oracle_hadamard_rotate(_ptr(X), _ptr(signs), _ptr(Y),
+                                                _L(X.size // max(d, 1)), _L(d)), "hadamard_rotate")
+        return Y
+
+    def mx_quantize_rows(self, Y):
+        """Block quantization along the last axis ("Moving less", section 4.6):
+        blocks of 32 elements of a row, one power-of-two scale each.  Returns
+        (codes uint8 [..., d], scale bytes uint8 [..., d / 32])."""
+        Y = _f64(Y)
+        d = Y.shape[-1]
+        codes = np.empty(Y.shape, dtype=np.uint8)
+        scales = np.empty(Y.shape[:-1] + (d // 32,), dtype=np.uint8)
+        _check(self._lib.oracle_mx_quantize_rows(_ptr(Y), _bptr(codes), _bptr(scales),
+                                                 _L(Y.size // max(d, 1)), _L(d)), "mx_quantize_rows")
+        return codes, scales
+
+    def mx_quantize_cols(self, Y):
+        """Block quantization along the rows of each column of every [n, d]
+        slice of Y [..., n, d]: blocks of 32 rows (the last one ragged).
+        Returns (codes uint8 [..., n, d], scale bytes uint8 [..., ceil(n/32), d])."""
+        Y = _f64(Y)
+        n, d = Y.shape[-2], Y.shape[-1]
+        slices = int(np.prod(Y.shape[:-2])) if Y.ndim > 2 else 1
+        codes = np.empty(Y.shape, dtype=np.uint8)
+        scales = np.empty(Y.shape[:-2] + ((n + 31) // 32, d), dtype=np.uint8)
+        _check(self._lib.oracle_mx_quantize_cols(_ptr(Y), _bptr(codes), _bptr(scales),
+                                                 _L(slices), _L(n), _L(d)), "mx_quantize_cols")
+        return codes, scales
+
+    def mx_decode_rows(self, codes, scales) -> np.ndarray:
+        codes, scales = _u8(codes), _u8(scales)
+        d = codes.shape[-1]
+        if scales.shape != codes.shape[:-1] + (d // 32,):
+            raise ValueError("scales must be [..., d / 32]")
+        Y = np.empty(codes.shape, dtype=np.float64)
+        _check(self._lib.oracle_mx_decode_rows(_bptr(codes), _bptr(scales), _ptr(Y),
+                                               _L(codes.size // max(d, 1)), _L(d)), "mx_decode_rows")
+        return Y
+
+    def mx_decode_cols(self, codes, scales) -> np.ndarray:
+        codes, scales = _u8(codes), _u8(scales)
+        n, d = codes.shape[-2], codes.shape[-1]
+        if scales.shape != codes.shape[:-2] + ((n + 31) // 32, d):
+            raise ValueError("scales must be [..., ceil(n / 32), d]")
+        slices = int(np.prod(codes.shape[:-2])) if codes.ndim > 2 else 1
+        Y = np.empty(codes.shape, dtype=np.float64)
+        _check(self._lib.oracle_mx_decode_cols(_bptr(codes), _bptr(scales), _ptr(Y),
+                                               _L(slices), _L(n), _L(d)), "mx_decode_cols")
+        return Y
+
+    def attn_fwd_fp8_mx(self, Q8, q_sc, K8, k_sc, V8, v_sc, scale: float, causal: bool):
+        """attn_fwd on block-quantized FP8 inputs: Q and K with one scale per
+        32 head columns of a row, V with one per 32 keys of a column
+        ([B, H, N, d] codes; scales [B, H, N, d/32] and [B, H, ceil(N/32), d])."""
+        return self.attn_fwd(self.mx_decode_rows(Q8, q_sc), self.mx_decode_rows(K8, k_sc),
+                             self.mx_decode_cols(V8, v_sc), scale, causal)
+
     def attn_bwd(self, Q, K, V, dO, scale: float, causal: bool):
         """Gradients of sum(dO * O) with respect to Q, K, V for the attention
         forward, by the chain rule with the probabilities recomputed from Q
@@ -266,3 +366,31 @@ def attn_fwd_fp8(Q8, K8, V8, q_scale, k_scale, v_scale, scale, causal):
 
 def attn_bwd(Q, K, V, dO, scale, causal):
     return default().attn_bwd(Q, K, V, dO, scale, causal)
+
+
+def fp8_encode(x, s=1.0):
+    return default().fp8_encode(x, s)
+
+
+def hadamard_rotate(X, signs):
+    return default().hadamard_rotate(X, signs)
+
+
+def mx_quantize_rows(Y):
+    return default().mx_quantize_rows(Y)
+
+
+def mx_quantize_cols(Y):
+    return default().mx_quantize_cols(Y)
+
+
+def mx_decode_rows(codes, scales):
+    return default().mx_decode_rows(codes, scales)
+
+
+def mx_decode_cols(codes, scales):
+    return default().mx_decode_cols(codes, scales)
+
+
+def attn_fwd_fp8_mx(Q8, q_sc, K8, k_sc, V8, v_sc, scale, causal):
+    return default().attn_fwd_fp8_mx(Q8, q_sc, K8, k_sc, V8, v_sc, scale, causal)

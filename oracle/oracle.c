@@ -21,7 +21,7 @@
  * Layouts: Q, K, V, O are contiguous [B][H][N][d] row-major; lse is [B][H][N];
  * x and y of the row softmax are [B][N].  All buffers are host memory owned by
  * the caller.  Return value: 0 on success, -1 on a bad argument, -2 when a
- * scratch allocation fails.
+ * scratch allocation fails, -3 when a value has no FP8 code (the encoders).
  */
 #include <math.h>
 #include <stdlib.h>
@@ -497,5 +497,171 @@ int oracle_fp8_e4m3_decode(const unsigned char *x, double s, double *y, long n)
             v = ldexp(1.0 + (double)m / 8.0, e - 7);  /* normal: 1.m * 2^(e - 7) */
         y[i] = (sign ? -v : v) * s;
     }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ *
+ * FP8 encoding: value -> nearest E4M3 code, ties to the even code (the
+ * code whose mantissa field is even), sign kept (negative values that round
+ * to zero give the code of -0).  The grid is the one oracle_fp8_e4m3_decode
+ * reads: normals 1.m * 2^E for E = -6 .. 8 (largest 1.75 * 2^8 = 448),
+ * subnormals m * 2^-9.  Encodes x_i / s; returns -3 if some |x_i / s|
+ * exceeds 448 or is NaN (no code holds it).
+ * ------------------------------------------------------------------------ */
+static int fp8_e4m3_encode_one(double x, unsigned char *code)
+{
+    if (isnan(x)) return -3;
+    const int sign = signbit(x) ? 1 : 0;
+    const double a = fabs(x);
+    if (a > 448.0) return -3;
+    int c;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: steps of 2^-9; m = 8 is the smallest normal */
+        c = (int)rint(a * 512.0);
+    } else {
+        int ex;
+        frexp(a, &ex);                              /* a = f * 2^ex, f in [0.5, 1) */
+        int E = ex - 1;                             /* a = mant * 2^E, mant in [1, 2) */
+        int q = (int)rint((ldexp(a, -E) - 1.0) * 8.0);  /* 3 mantissa bits, ties to even */
+        if (q == 8) { q = 0; E += 1; }
+        c = ((E + 7) << 3) | q;
+    }
+    *code = (unsigned char)((sign << 7) | c);
+    return 0;
+}
+
+int oracle_fp8_e4m3_encode(const double *x, double s, unsigned char *out, long n)
+{
+    if (!x || !out || n < 0 || !(s > 0.0)) return -1;
+    for (long i = 0; i < n; ++i)
+        if (fp8_e4m3_encode_one(x[i] / s, &out[i]) != 0) return -3;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ *
+ * Incoherent processing ([GEN] section 4.6): before quantizing, Q and K are
+ * both multiplied by one random orthogonal matrix M made of random signs and
+ * a Hadamard matrix, which leaves Q K^T unchanged because M M^T = I:
+ *   Y = X M,  M = diag(s) H / sqrt(d),
+ * H the d x d Hadamard matrix of Sylvester's doubling construction, whose
+ * entry (t, k) is (-1)^(number of bits set in both t and k), s_t = +-1.
+ * Plain O(d^2) products per row (the pages' O(d log d) fast transform is
+ * the kernel's business).  X, Y: [rows][d], d a power of two.
+ * ------------------------------------------------------------------------ */
+int oracle_hadamard_rotate(const double *X, const double *signs, double *Y, long rows, long d)
+{
+    if (!X || !signs || !Y || rows < 0 || d <= 0 || (d & (d - 1)) != 0) return -1;
+    const double norm = 1.0 / sqrt((double)d);
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; ++r) {
+        const double *x = X + r * d;
+        for (long k = 0; k < d; ++k) {
+            double acc = 0.0;
+            for (long t = 0; t < d; ++t) {
+                const int odd = __builtin_popcountl((unsigned long)(t & k)) & 1;
+                acc += x[t] * signs[t] * (odd ? -1.0 : 1.0);
+            }
+            Y[r * d + k] = acc * norm;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ *
+ * Block quantization ([GEN] section 4.6: one scale per block instead of one
+ * per tensor).  Blocks are 32 consecutive elements along the axis the
+ * attention contracts: along a row for Q and K (the head dimension), along
+ * the rows of each column for V (the key axis).  A block's scale is a power
+ * of two 2^e, stored as the byte e + 127, with e the smallest integer for
+ * which the block's largest magnitude amax fits: amax <= 448 * 2^e (e = 0
+ * for an all-zero block; the byte is clamped to 0 .. 254).  Each element is
+ * the E4M3 code of x / 2^e, and decodes as value(code) * 2^(byte - 127).
+ * ------------------------------------------------------------------------ */
+static int mx_exponent(double amax)
+{
+    if (amax == 0.0) return 0;
+    int ex;
+    frexp(amax, &ex);                                 /* amax < 2^ex */
+    int e = ex - 8;                                   /* 448 * 2^(ex - 8) > 2^ex: fits */
+    while (amax <= 448.0 * ldexp(1.0, e - 1)) --e;    /* the smallest that fits */
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* Y [rows][d] -> codes [rows][d], scales [rows][d / 32]; d a multiple of 32. */
+int oracle_mx_quantize_rows(const double *Y, unsigned char *codes, unsigned char *scales,
+                            long rows, long d)
+{
+    if (!Y || !codes || !scales || rows < 0 || d <= 0 || d % 32 != 0) return -1;
+    int failed = 0;
+#pragma omp parallel for schedule(static) reduction(| : failed)
+    for (long r = 0; r < rows; ++r)
+        for (long blk = 0; blk < d / 32; ++blk) {
+            const double *y = Y + r * d + blk * 32;
+            double amax = 0.0;
+            for (long t = 0; t < 32; ++t)
+                if (fabs(y[t]) > amax) amax = fabs(y[t]);
+            const int e = mx_exponent(amax);
+            scales[r * (d / 32) + blk] = (unsigned char)(e + 127);
+            for (long t = 0; t < 32; ++t)
+                if (fp8_e4m3_encode_one(ldexp(y[t], -e), &codes[r * d + blk * 32 + t]) != 0)
+                    failed = 1;
+        }
+    return failed ? -3 : 0;
+}
+
+/* Y [slices][n][d] -> codes [slices][n][d], scales [slices][ceil(n / 32)][d]:
+ * block (i, t) of a slice holds rows 32 i .. min(32 i + 31, n - 1) of
+ * column t. */
+int oracle_mx_quantize_cols(const double *Y, unsigned char *codes, unsigned char *scales,
+                            long slices, long n, long d)
+{
+    if (!Y || !codes || !scales || slices < 0 || n < 0 || d <= 0) return -1;
+    const long nb = (n + 31) / 32;
+    int failed = 0;
+#pragma omp parallel for schedule(static) reduction(| : failed)
+    for (long sl = 0; sl < slices; ++sl)
+        for (long i = 0; i < nb; ++i)
+            for (long t = 0; t < d; ++t) {
+                const long r0 = 32 * i, r1 = (32 * i + 32 < n) ? 32 * i + 32 : n;
+                double amax = 0.0;
+                for (long r = r0; r < r1; ++r) {
+                    const double a = fabs(Y[(sl * n + r) * d + t]);
+                    if (a > amax) amax = a;
+                }
+                const int e = mx_exponent(amax);
+                scales[(sl * nb + i) * d + t] = (unsigned char)(e + 127);
+                for (long r = r0; r < r1; ++r)
+                    if (fp8_e4m3_encode_one(ldexp(Y[(sl * n + r) * d + t], -e),
+                                            &codes[(sl * n + r) * d + t]) != 0)
+                        failed = 1;
+            }
+    return failed ? -3 : 0;
+}
+
+/* Decoding of the two block layouts: value(code) * 2^(scale byte - 127). */
+int oracle_mx_decode_rows(const unsigned char *codes, const unsigned char *scales, double *Y,
+                          long rows, long d)
+{
+    if (!codes || !scales || !Y || rows < 0 || d <= 0 || d % 32 != 0) return -1;
+    if (oracle_fp8_e4m3_decode(codes, 1.0, Y, rows * d) != 0) return -1;
+    for (long r = 0; r < rows; ++r)
+        for (long t = 0; t < d; ++t)
+            Y[r * d + t] = ldexp(Y[r * d + t], (int)scales[r * (d / 32) + t / 32] - 127);
+    return 0;
+}
+
+int oracle_mx_decode_cols(const unsigned char *codes, const unsigned char *scales, double *Y,
+                          long slices, long n, long d)
+{
+    if (!codes || !scales || !Y || slices < 0 || n < 0 || d <= 0) return -1;
+    const long nb = (n + 31) / 32;
+    if (oracle_fp8_e4m3_decode(codes, 1.0, Y, slices * n * d) != 0) return -1;
+    for (long sl = 0; sl < slices; ++sl)
+        for (long r = 0; r < n; ++r)
+            for (long t = 0; t < d; ++t)
+                Y[(sl * n + r) * d + t] =
+                    ldexp(Y[(sl * n + r) * d + t], (int)scales[(sl * nb + r / 32) * d + t] - 127);
     return 0;
 }

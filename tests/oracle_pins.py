@@ -543,4 +543,188 @@ def pin_fp8_decode_library(orc):
     np.testing.assert_array_equal(got[~nan], lib[~nan])
 
 
+def _e4m3_grid():
+    """All finite E4M3 values (code, value), from the decode pins' encoding."""
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]
+    return codes
+
+
+def pin_fp8_encode_grid(orc):
+    # Every finite code encodes back to itself; a midpoint between two
+    # neighbouring codes goes to the one with the even mantissa field (the even
+    # code), and a value a hair off the midpoint to the nearer code; the scale
+    # divides; values past 448 have no code.
+    codes = _e4m3_grid()
+    vals = orc.fp8_decode(codes)
+    np.testing.assert_array_equal(orc.fp8_encode(vals), codes)
+    pos = np.arange(0x00, 0x7E, dtype=np.uint8)  # each with its upper neighbour
+    lo, hi = orc.fp8_decode(pos), orc.fp8_decode(pos + 1)
+    mid = 0.5 * (lo + hi)
+    even = np.where(pos % 2 == 0, pos, pos + 1).astype(np.uint8)
+    np.testing.assert_array_equal(orc.fp8_encode(mid), even)
+    np.testing.assert_array_equal(orc.fp8_encode(-mid), even | 0x80)
+    np.testing.assert_array_equal(orc.fp8_encode(np.nextafter(mid, 0)), pos)
+    np.testing.assert_array_equal(orc.fp8_encode(np.nextafter(mid, 1e9)), (pos + 1).astype(np.uint8))
+    np.testing.assert_array_equal(orc.fp8_encode(vals * 0.375, 0.375), codes)
+    for bad in (448.5, np.nan, -np.inf):
+        try:
+            orc.fp8_encode(np.array([bad]))
+        except RuntimeError:
+            continue
+        raise AssertionError(f"{bad} was encoded")
+
+
+def pin_fp8_encode_library(orc):
+    # Against torch's float8_e4m3fn conversion (round to nearest even, an
+    # independent implementation) on float32 values spread over the whole
+    # finite range, subnormals and signed zeros included.
+    import torch
+    rng = _rng(70)
+    x = (rng.uniform(-1, 1, 20000) * np.exp2(rng.integers(-14, 9, 20000))).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(orc.fp8_encode(x.astype(np.float64)), lib)
+
+
+def pin_hadamard_library(orc):
+    # With all signs +1 the rotation of the identity is H / sqrt(d), H from
+    # scipy's Sylvester construction; a sign flips its input column.
+    import scipy.linalg
+    for d in (1, 2, 4, 32, 128):
+        H = scipy.linalg.hadamard(d).astype(np.float64)
+        _close(orc.hadamard_rotate(np.eye(d), np.ones(d)), H / np.sqrt(d), 1e-15,
+               what=f"H_{d}")
+    rng = _rng(71)
+    X = rng.standard_normal((5, 64))
+    s = rng.choice([-1.0, 1.0], 64)
+    _close(orc.hadamard_rotate(X, s), orc.hadamard_rotate(X * s, np.ones(64)), 1e-14,
+           what="signs act on input columns")
+
+
+def pin_hadamard_orthogonal(orc):
+    # M M^T = I, so (Q M)(K M)^T = Q K^T and norms are kept; H is its own
+    # inverse up to d, so rotating twice with unit signs returns the input.
+    rng = _rng(72)
+    Q, K = rng.standard_normal((20, 128)), rng.standard_normal((30, 128))
+    s = rng.choice([-1.0, 1.0], 128)
+    Qr, Kr = orc.hadamard_rotate(Q, s), orc.hadamard_rotate(K, s)
+    _close(Qr @ Kr.T, Q @ K.T, 1e-12, what="scores")
+    _close(np.linalg.norm(Qr, axis=1), np.linalg.norm(Q, axis=1), 1e-12, what="norms")
+    one = np.ones(128)
+    _close(orc.hadamard_rotate(orc.hadamard_rotate(Q, one), one), Q, 1e-12, what="H H = d I")
+
+
+def pin_mx_rows_definition(orc):
+    # Per block of 32: the scale is the smallest power of two 2^e with
+    # amax <= 448 * 2^e (byte e + 127; e = 0 for a zero block), hand-checked
+    # on edge blocks, and each element decodes to the nearest point of the
+    # scaled E4M3 grid (brute force over every code).
+    Y = np.zeros((6, 64))
+    Y[0, :32] = 1.0
+    Y[0, 0] = 448.0              # amax exactly 448 -> e = 0
+    Y[1, 0] = 449.0              # just above -> e = 1
+    Y[2, :32] = -224.0           # 224 = 448 / 2 -> e = -1
+    Y[3, 32:] = 0.75 * 2.0 ** -20  # tiny block
+    rng = _rng(73)
+    Y[4] = rng.standard_normal(64) * 3
+    Y[5] = rng.standard_normal(64) * np.exp2(rng.integers(-6, 6, 64))
+    codes, sc = orc.mx_quantize_rows(Y)
+    assert sc.shape == (6, 2)
+    assert list(sc[:4, 0]) == [127, 128, 126, 127] and sc[3, 1] == 127 + (-29), sc
+    e = sc.astype(np.int64) - 127
+    amax = np.abs(Y).reshape(6, 2, 32).max(axis=2)
+    nz = amax > 0
+    assert np.all(amax <= 448.0 * np.exp2(e)) and np.all(amax[nz] > 224.0 * np.exp2(e[nz]))
+    grid_codes = _e4m3_grid()
+    grid = orc.fp8_decode(grid_codes)
+    dec = orc.mx_decode_rows(codes, sc)
+    for r in range(6):
+        for t in range(64):
+            g = grid * np.exp2(e[r, t // 32])
+            dist = np.abs(g - Y[r, t])
+            best = dist.min()
+            assert abs(dec[r, t] - Y[r, t]) == best, (r, t, dec[r, t], Y[r, t])
+
+
+def pin_mx_cols_transpose(orc):
+    # Column blocks are row blocks of the transposed slice: quantizing the
+    # rows of each column of V in blocks of 32 equals quantizing the rows of
+    # V^T; a ragged last block (n = 45) behaves as if padded with zeros.
+    rng = _rng(74)
+    V = rng.standard_normal((2, 3, 64, 32)) * np.exp2(rng.integers(-4, 4, (2, 3, 64, 32)))
+    c, s = orc.mx_quantize_cols(V)
+    cr, sr = orc.mx_quantize_rows(np.swapaxes(V, -1, -2))
+    np.testing.assert_array_equal(c, np.swapaxes(cr, -1, -2))
+    np.testing.assert_array_equal(s, np.swapaxes(sr, -1, -2))
+    W = V[:, :, :45]
+    cw, sw = orc.mx_quantize_cols(W)
+    Wp = np.concatenate([W, np.zeros((2, 3, 19, 32))], axis=2)
+    cp, sp = orc.mx_quantize_cols(Wp)
+    np.testing.assert_array_equal(cw, cp[:, :, :45])
+    np.testing.assert_array_equal(sw, sp)
+    _close(orc.mx_decode_cols(cw, sw), orc.mx_decode_cols(cp, sp)[:, :, :45], 0.0)
+
+
+def pin_mx_decode_values(orc):
+    # value(code) * 2^(byte - 127): 1.0 at byte 130 is 8, -2 at byte 120 is
+    # -2^-6, the largest subnormal at byte 127 is 7 * 2^-9.
+    codes = np.zeros((1, 32), dtype=np.uint8)
+    codes[0, :3] = [0x38, 0xC0, 0x07]
+    for byte, want in ((130, [8.0, -16.0, 7 * 2.0 ** -6]), (120, [2.0 ** -7, -(2.0 ** -6), 7 * 2.0 ** -16])):
+        got = orc.mx_decode_rows(codes, np.array([[byte]], dtype=np.uint8))
+        assert list(got[0, :3]) == want and not got[0, 3:].any(), (byte, got[0, :3])
+    cv = np.zeros((33, 1), dtype=np.uint8)
+    cv[0, 0], cv[32, 0] = 0x38, 0x38
+    got = orc.mx_decode_cols(cv, np.array([[127], [129]], dtype=np.uint8))
+    assert got[0, 0] == 1.0 and got[32, 0] == 4.0
+
+
+def pin_attn_fp8_mx_unit_scales(orc):
+    # With every block scale 2^0 the block-quantized attention is the FP8
+    # attention with unit tensor scales.
+    rng = _rng(75)
+    B, H, N, d = 1, 2, 40, 64
+    Q8, K8, V8 = (rng.integers(0, 256, (B, H, N, d)).astype(np.uint8) & 0xB7 for _ in range(3))
+    one_r = np.full((B, H, N, d // 32), 127, dtype=np.uint8)
+    one_c = np.full((B, H, (N + 31) // 32, d), 127, dtype=np.uint8)
+    for causal in (False, True):
+        a = orc.attn_fwd_fp8_mx(Q8, one_r, K8, one_r, V8, one_c, 0.125, causal)
+        b = orc.attn_fwd_fp8(Q8, K8, V8, 1.0, 1.0, 1.0, 0.125, causal)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+
+
+def pin_incoherent_processing_outliers(orc):
+    # The claim of the FP8 section: with outliers, one scale per tensor loses
+    # accuracy that block scales after a random-sign Hadamard rotation of Q
+    # and K recover (the pages report a 2.6x lower RMSE of O).  Inputs: N(0,1)
+    # with four head channels of Q and K scaled by 20; O compared with exact
+    # attention on the unquantized values.
+    rng = _rng(76)
+    B, H, N, d = 1, 2, 256, 128
+    Q, K, V = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    ch = rng.choice(d, 4, replace=False)
+    Q[..., ch] *= 20.0
+    K[..., ch] *= 20.0
+    scale = 1.0 / np.sqrt(d)
+    O, _ = orc.attn_fwd(Q, K, V, scale, False)
+
+    def tensor_q(X):
+        s = np.nextafter(np.abs(X).max() / 448.0, np.inf)
+        return orc.fp8_decode(orc.fp8_encode(X, s), s)
+
+    def rows_q(X):
+        return orc.mx_decode_rows(*orc.mx_quantize_rows(X))
+
+    Vb = orc.mx_decode_cols(*orc.mx_quantize_cols(V))
+    Ot, _ = orc.attn_fwd(tensor_q(Q), tensor_q(K), tensor_q(V), scale, False)
+    s = rng.choice([-1.0, 1.0], d)
+    Or, _ = orc.attn_fwd(rows_q(orc.hadamard_rotate(Q, s)), rows_q(orc.hadamard_rotate(K, s)),
+                         Vb, scale, False)
+    rmse_t = np.sqrt(np.mean((Ot - O) ** 2))
+    rmse_r = np.sqrt(np.mean((Or - O) ** 2))
+    assert rmse_r * 2.0 < rmse_t, (rmse_t, rmse_r)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -65,6 +65,30 @@ MUTANTS = [
     ("fp8_subnormal_scale", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
     ("fp8_no_nan", "if (e == 15 && m == 7)", "if (e == 16)"),
     ("fp8_scale_dropped", "y[i] = (sign ? -v : v) * s;", "y[i] = (sign ? -v : v);"),
+    ("encode_ties_away", "int q = (int)rint((ldexp(a, -E) - 1.0) * 8.0);",
+     "int q = (int)round((ldexp(a, -E) - 1.0) * 8.0);"),
+    ("encode_subnormal_step", "c = (int)rint(a * 512.0);", "c = (int)rint(a * 256.0);"),
+    ("encode_exponent_bias", "c = ((E + 7) << 3) | q;", "c = ((E + 8) << 3) | q;"),
+    ("encode_sign_dropped", "*code = (unsigned char)((sign << 7) | c);", "*code = (unsigned char)c;"),
+    ("encode_scale_multiplies", "if (fp8_e4m3_encode_one(x[i] / s, &out[i]) != 0) return -3;",
+     "if (fp8_e4m3_encode_one(x[i] * s, &out[i]) != 0) return -3;"),
+    ("hadamard_not_normalised", "Y[r * d + k] = acc * norm;", "Y[r * d + k] = acc;"),
+    ("hadamard_sign_on_output", "acc += x[t] * signs[t] * (odd ? -1.0 : 1.0);",
+     "acc += x[t] * signs[k] * (odd ? -1.0 : 1.0);"),
+    ("hadamard_parity_of_or", "__builtin_popcountl((unsigned long)(t & k)) & 1",
+     "__builtin_popcountl((unsigned long)(t | k)) & 1"),
+    ("mx_scale_not_smallest", "while (amax <= 448.0 * ldexp(1.0, e - 1)) --e;",
+     "while (amax <= 448.0 * ldexp(1.0, e - 2)) --e;"),
+    ("mx_fit_strict", "while (amax <= 448.0 * ldexp(1.0, e - 1)) --e;",
+     "while (amax < 448.0 * ldexp(1.0, e - 1)) --e;"),
+    ("mx_scale_bias", "scales[r * (d / 32) + blk] = (unsigned char)(e + 127);",
+     "scales[r * (d / 32) + blk] = (unsigned char)(e + 128);"),
+    ("mx_decode_rows_block_index", "scales[r * (d / 32) + t / 32] - 127",
+     "scales[r * (d / 32) + t % (d / 32)] - 127"),
+    ("mx_cols_block_short", "r1 = (32 * i + 32 < n) ? 32 * i + 32 : n;",
+     "r1 = (32 * i + 31 < n) ? 32 * i + 31 : n;"),
+    ("mx_decode_cols_row_block", "scales[(sl * nb + r / 32) * d + t] - 127",
+     "scales[(sl * nb + r / 33) * d + t] - 127"),
 ]
 
 

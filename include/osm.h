@@ -30,6 +30,16 @@
  *    section 4.6.  Its own tolerance, from the rounding of the
  *    probabilities to fp8, is stated with the function below.
  *
+ *  fp8_quantize_rows / fp8_quantize_cols / attn_fwd_fp8_mx
+ *    The two accuracy devices of the same FP8 section: block quantization
+ *    (one scale per block of elements instead of one per tensor) and
+ *    incoherent processing (Q and K multiplied by one random orthogonal
+ *    matrix, random signs times a Hadamard matrix, before quantizing; the
+ *    product Q K^T is unchanged because the matrix times its transpose is
+ *    the identity).  The blocks are 32 elements along each contracted axis
+ *    with power-of-two scales, the block format the gfx950 fp8 matrix cores
+ *    apply themselves; attn_fwd_fp8_mx is the attention on such inputs.
+ *
  *  attn_fwd_varlen
  *    The same attention over a batch of sequences of different lengths
  *    packed end to end with no padding: the padding mask of Lesson 22,
@@ -98,7 +108,8 @@ typedef enum {
     OSM_ERR_SPLITS = 9,   /* a split count is outside its documented range     */
     OSM_ERR_WORKSPACE = 10, /* workspace_bytes is below what the call requires */
     OSM_ERR_HEADS = 11,    /* Hkv is not a divisor of H in 1 .. H               */
-    OSM_ERR_SCRATCH = 12   /* the problem exceeds the static scratch's limit    */
+    OSM_ERR_SCRATCH = 12,  /* the problem exceeds the static scratch's limit    */
+    OSM_ERR_SIGNS = 13     /* a rotation sign is neither +1 nor -1              */
 } osm_status;
 
 /*
@@ -165,6 +176,74 @@ int attn_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* ls
 int attn_fwd_fp8(const void* Q, const void* K, const void* V, float q_scale, float k_scale,
                  float v_scale, void* O, float* lse, int B, int H, int Hkv, int N, int d,
                  float scale, int causal, void* stream);
+
+/*
+ * Block-quantized FP8 ("Moving less: four generations of FlashAttention",
+ * section 4.6, block quantization and incoherent processing).
+ *
+ * A block is 32 consecutive elements along the axis the attention contracts:
+ * 32 head columns of one row (Q, K), or 32 consecutive rows of one column of
+ * a [N][d] slice (V; the last block of a slice may be shorter).  Its scale
+ * is a power of two 2^e stored as the byte e + 127 (E8M0): e is the smallest
+ * integer with amax <= 448 * 2^e, amax the block's largest magnitude (e = 0
+ * for an all-zero block), and each element is stored as the E4M3 code of
+ * x / 2^e, rounded to nearest with ties to the even code.  A code x with
+ * scale byte s stands for decode(x) * 2^(s - 127).  Scale byte 255 is NaN.
+ */
+
+/*
+ * fp8_quantize_rows -- block quantization along rows, optionally after the
+ * random-sign Hadamard rotation.
+ *   X      : bf16 [rows][d] (device), d = 64 or 128 (else OSM_ERR_HEAD_DIM);
+ *            finite values.
+ *   signs  : NULL (no rotation), or a HOST array of d values, each +1 or -1
+ *            (else OSM_ERR_SIGNS): the rows are first replaced by
+ *            x diag(signs) H / sqrt(d), H the d x d Hadamard matrix of
+ *            Sylvester's doubling construction (entry (t, k) =
+ *            (-1)^popcount(t & k)), computed in fp32 by the fast
+ *            Walsh-Hadamard transform.  Use the same signs for Q and K.
+ *   codes  : uint8 [rows][d] (device, 8-byte aligned), the E4M3 codes.
+ *   scales : uint8 [rows][d / 32] (device), the block scale bytes.
+ *   rows >= 0 (else OSM_ERR_SIZE); rows = 0 enqueues nothing.
+ * X must be 16-byte aligned; no two buffers may overlap (OSM_ERR_ALIAS).
+ * Returns an osm_status.
+ */
+int fp8_quantize_rows(const void* X, const signed char* signs, void* codes, void* scales,
+                      long long rows, int d, void* stream);
+
+/*
+ * fp8_quantize_cols -- block quantization along the rows of each column, the
+ * layout attn_fwd_fp8_mx takes for V.
+ *   X      : bf16 [slices][n][d] (device, 16-byte aligned), d = 64 or 128.
+ *   codes  : uint8 [slices][n][d] (device, 8-byte aligned).
+ *   scales : uint8 [slices][ceil(n / 32)][d] (device): byte (s, i, t) is the
+ *            scale of rows 32 i .. min(32 i + 31, n - 1) of column t of
+ *            slice s.
+ *   slices, n >= 0 (else OSM_ERR_SIZE).  No two buffers may overlap.
+ * Returns an osm_status.
+ */
+int fp8_quantize_cols(const void* X, void* codes, void* scales, long long slices, int n, int d,
+                      void* stream);
+
+/*
+ * attn_fwd_fp8_mx -- attention forward on block-quantized fp8 inputs.
+ *   Q : uint8 [B][H][N][d] codes, q_scales : uint8 [B][H][N][d / 32]
+ *   K : uint8 [B][Hkv][N][d] codes, k_scales : uint8 [B][Hkv][N][d / 32]
+ *   V : uint8 [B][Hkv][N][d] codes, v_scales : uint8 [B][Hkv][ceil(N/32)][d]
+ *       (the layouts fp8_quantize_rows and fp8_quantize_cols write).
+ *   O, lse, B, H, Hkv, N, d, scale, causal, stream : as for attn_fwd_fp8,
+ *       with the values the codes and scales stand for as its inputs.
+ * The matrix cores apply every block scale (exact: powers of two); the
+ * rounding and summation error of attn_fwd_fp8 applies unchanged, with
+ * sum_d |q_d k_d| taken over the decoded values.  When Q and K were rotated
+ * with the same signs, O and lse are those of the unrotated attention (the
+ * rotation is orthogonal) up to that error.  Q, K, V, O need 16-byte
+ * alignment, lse 4; O and lse may not overlap any input or each other.
+ * Returns an osm_status.
+ */
+int attn_fwd_fp8_mx(const void* Q, const void* q_scales, const void* K, const void* k_scales,
+                    const void* V, const void* v_scales, void* O, float* lse, int B, int H,
+                    int Hkv, int N, int d, float scale, int causal, void* stream);
 
 /*
  * attn_fwd_varlen -- attn_fwd over packed variable-length sequences.

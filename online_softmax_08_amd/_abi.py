@@ -38,6 +38,13 @@ _lib.attn_fwd_gqa.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _
 _lib.attn_fwd_gqa.restype = _i
 _lib.attn_fwd_fp8.argtypes = [_vp, _vp, _vp, _f, _f, _f, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]
 _lib.attn_fwd_fp8.restype = _i
+_lib.attn_fwd_fp8_mx.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
+                                 _i, _vp]
+_lib.attn_fwd_fp8_mx.restype = _i
+_lib.fp8_quantize_rows.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_longlong, _i, _vp]
+_lib.fp8_quantize_rows.restype = _i
+_lib.fp8_quantize_cols.argtypes = [_vp, _vp, _vp, ctypes.c_longlong, _i, _i, _vp]
+_lib.fp8_quantize_cols.restype = _i
 _lib.attn_fwd_splitkv_plan.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(_i),
                                        ctypes.POINTER(_sz)]
 _lib.attn_fwd_splitkv_plan.restype = _i
@@ -66,7 +73,9 @@ _lib.attn_bwd_varlen.restype = _i
 _lib.osm_status_str.argtypes = [_i]
 _lib.osm_status_str.restype = ctypes.c_char_p
 
-EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_gqa", "attn_fwd_fp8", "attn_fwd_varlen", "attn_fwd_splitkv_plan", "attn_fwd_splitkv",
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_gqa", "attn_fwd_fp8", "attn_fwd_fp8_mx",
+           "fp8_quantize_rows", "fp8_quantize_cols", "attn_fwd_varlen", "attn_fwd_splitkv_plan",
+           "attn_fwd_splitkv",
            "attn_combine", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_varlen",
            "attn_bwd_split_plan", "attn_bwd_split", "row_softmax", "osm_status_str")
 
@@ -83,6 +92,7 @@ OSM_ERR_SPLITS = 9
 OSM_ERR_WORKSPACE = 10
 OSM_ERR_HEADS = 11
 OSM_ERR_SCRATCH = 12
+OSM_ERR_SIGNS = 13
 # attn_bwd_noalloc's limit on B * H * N (include/osm.h OSM_NOALLOC_BWD_MAX_ROWS)
 NOALLOC_BWD_MAX_ROWS = 1 << 22
 
@@ -194,6 +204,31 @@ def attn_fwd_fp8(Q: int, K: int, V: int, q_scale: float, k_scale: float, v_scale
     """Attention forward on OCP FP8 E4M3 inputs with per-tensor scales; see include/osm.h."""
     _call("attn_fwd_fp8", Q, K, V, q_scale, k_scale, v_scale, O, lse, B, H, Hkv, N, d, scale,
           int(bool(causal)), stream)
+
+
+def attn_fwd_fp8_mx(Q: int, q_scales: int, K: int, k_scales: int, V: int, v_scales: int, O: int,
+                    lse: int, B: int, H: int, Hkv: int, N: int, d: int, scale: float,
+                    causal: bool, stream: int = 0) -> None:
+    """Attention forward on block-quantized FP8 inputs; see include/osm.h."""
+    _call("attn_fwd_fp8_mx", Q, q_scales, K, k_scales, V, v_scales, O, lse, B, H, Hkv, N, d,
+          scale, int(bool(causal)), stream)
+
+
+def fp8_quantize_rows(X: int, signs, codes: int, scales: int, rows: int, d: int,
+                      stream: int = 0) -> None:
+    """Block quantization along rows, after the random-sign Hadamard rotation
+    when signs (a host sequence of d values +-1) is given; see include/osm.h."""
+    sp = None
+    if signs is not None:
+        vals = [int(x) for x in signs]
+        sp = ctypes.cast((ctypes.c_byte * len(vals))(*vals), _vp)
+    _call("fp8_quantize_rows", X, sp, codes, scales, rows, d, stream)
+
+
+def fp8_quantize_cols(X: int, codes: int, scales: int, slices: int, n: int, d: int,
+                      stream: int = 0) -> None:
+    """Block quantization along the rows of each column; see include/osm.h."""
+    _call("fp8_quantize_cols", X, codes, scales, slices, n, d, stream)
 
 
 def attn_fwd_varlen(Q: int, K: int, V: int, O: int, lse: int, cu_seqlens: int, B: int, H: int,

@@ -181,6 +181,75 @@ int attn_fwd_fp8(const void* Q, const void* K, const void* V, float q_scale, flo
                                            static_cast<hipStream_t>(stream)));
 }
 
+int attn_fwd_fp8_mx(const void* Q, const void* q_scales, const void* K, const void* k_scales,
+                    const void* V, const void* v_scales, void* O, float* lse, int B, int H,
+                    int Hkv, int N, int d, float scale, int causal, void* stream)
+{
+    int st = check_attn_shape(B, H, N, d, scale, 2);
+    if (st != OSM_OK || B == 0 || H == 0 || N == 0) return st;
+    if ((st = check_heads(H, Hkv)) != OSM_OK) return st;
+    if (!Q || !K || !V || !q_scales || !k_scales || !v_scales || !O || !lse) return OSM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(lse, 4))
+        return OSM_ERR_ALIGN;
+    const long long bh = (long long)B * H, bhkv = (long long)B * Hkv;
+    const size_t qbytes = (size_t)bh * N * d, kvbytes = (size_t)bhkv * N * d;
+    const size_t qsb = (size_t)bh * N * (d / 32), ksb = (size_t)bhkv * N * (d / 32);
+    const size_t vsb = (size_t)bhkv * ((N + 31) / 32) * d;
+    const size_t obytes = (size_t)bh * N * d * 2, lbytes = (size_t)bh * N * sizeof(float);
+    const void* in[6] = {Q, K, V, q_scales, k_scales, v_scales};
+    const size_t inb[6] = {qbytes, kvbytes, kvbytes, qsb, ksb, vsb};
+    for (int i = 0; i < 6; ++i)
+        if (overlaps(O, obytes, in[i], inb[i]) || overlaps(lse, lbytes, in[i], inb[i]))
+            return OSM_ERR_ALIAS;
+    if (overlaps(lse, lbytes, O, obytes)) return OSM_ERR_ALIAS;
+    if ((st = check_device()) != OSM_OK) return st;
+    return finish(osm::launch_attn_fwd_fp8_mx(Q, q_scales, K, k_scales, V, v_scales, O, lse, B, H,
+                                              Hkv, N, d, scale, causal != 0,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int fp8_quantize_rows(const void* X, const signed char* signs, void* codes, void* scales,
+                      long long rows, int d, void* stream)
+{
+    if (rows < 0) return OSM_ERR_SIZE;
+    if (d != 64 && d != 128) return OSM_ERR_HEAD_DIM;
+    uint64_t neg[2] = {0, 0};
+    if (signs) {
+        for (int t = 0; t < d; ++t) {
+            if (signs[t] != 1 && signs[t] != -1) return OSM_ERR_SIGNS;
+            if (signs[t] == -1) neg[t / 64] |= 1ull << (t % 64);
+        }
+    }
+    if (rows == 0) return OSM_OK;
+    if (!X || !codes || !scales) return OSM_ERR_NULL;
+    if (!aligned(X, 16) || !aligned(codes, 8)) return OSM_ERR_ALIGN;
+    const size_t xb = (size_t)rows * d * 2, cb = (size_t)rows * d, sb = (size_t)rows * (d / 32);
+    if (overlaps(codes, cb, X, xb) || overlaps(scales, sb, X, xb) || overlaps(scales, sb, codes, cb))
+        return OSM_ERR_ALIAS;
+    int st = check_device();
+    if (st != OSM_OK) return st;
+    return finish(osm::launch_fp8_quant_rows(X, codes, scales, rows, d, signs != nullptr, neg[0],
+                                             neg[1], static_cast<hipStream_t>(stream)));
+}
+
+int fp8_quantize_cols(const void* X, void* codes, void* scales, long long slices, int n, int d,
+                      void* stream)
+{
+    if (slices < 0 || n < 0) return OSM_ERR_SIZE;
+    if (d != 64 && d != 128) return OSM_ERR_HEAD_DIM;
+    if (slices == 0 || n == 0) return OSM_OK;
+    if (!X || !codes || !scales) return OSM_ERR_NULL;
+    if (!aligned(X, 16) || !aligned(codes, 8)) return OSM_ERR_ALIGN;
+    const size_t xb = (size_t)slices * n * d * 2, cb = (size_t)slices * n * d;
+    const size_t sb = (size_t)slices * ((n + 31) / 32) * d;
+    if (overlaps(codes, cb, X, xb) || overlaps(scales, sb, X, xb) || overlaps(scales, sb, codes, cb))
+        return OSM_ERR_ALIAS;
+    int st = check_device();
+    if (st != OSM_OK) return st;
+    return finish(osm::launch_fp8_quant_cols(X, codes, scales, slices, n, d,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int attn_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* lse, int B,
                  int H, int N, int d, float scale, int causal, void* stream)
 {
@@ -541,6 +610,7 @@ const char* osm_status_str(int status)
     case OSM_ERR_WORKSPACE: return "the workspace is smaller than the call requires";
     case OSM_ERR_HEADS: return "key/value heads must divide the query heads (1 <= Hkv <= H)";
     case OSM_ERR_SCRATCH: return "the problem needs more than the library's static scratch";
+    case OSM_ERR_SIGNS: return "every rotation sign must be +1 or -1";
     default: return "unknown status";
     }
 }

@@ -4,12 +4,15 @@
 // (v_mfma_*_32x32x64_f8f6f4, twice the bf16 rate), the softmax in fp32.
 //
 // Inputs are Q, K, V in fp8 with one scale per tensor (a stored byte x
-// stands for decode(x) * q_scale, and so on); O is written in bf16 and lse in
-// fp32.  The arithmetic:
+// stands for decode(x) * q_scale, and so on), or block-quantized (the
+// section's block quantization: one power-of-two scale per 32 elements along
+// each contracted axis, applied by the matrix cores, see MX below); O is
+// written in bf16 and lse in fp32.  The arithmetic:
 //  * S = (Q K^T) * q_scale * k_scale * scale on the matrix cores, which form
 //    the fp8 products exactly and sum each 64-term block at reduced
 //    precision (measured: errors up to ~2e-5 of the block's sum of
-//    |products| on Gaussian data), the blocks in fp32;
+//    |products| on Gaussian data), the blocks in fp32 (with block scales:
+//    each 32-term block sum times its two scales);
 //  * the online softmax of attn_fwd_bf16_pp_kernel (running reference, fp32
 //    row sums), with the probabilities formed as p' = 2^(S log2 e - r) against
 //    a reference r kept 4 (log2 units) below the row's running maximum, so the
@@ -28,11 +31,14 @@
 // operand layout of the fp8 products:
 //  * S^T = K Q^T: lane (i, h) of the A operand holds 32 bytes of key row i,
 //    the B operand 32 bytes of query row j; byte b of half h is the same
-//    reduction index in both (measured), so any common order of the 64 head
-//    columns works: half h takes columns 64 kk + 32 h .. + 31.
+//    reduction index in both (measured), and the product's two scale blocks
+//    are bytes 0-15 and 16-31 of both halves (measured): half h takes head
+//    columns 64 kk + 16 h .. + 15 and 64 kk + 32 + 16 h .. + 15, so that scale
+//    block kb is the quantization block of columns 64 kk + 32 kb .. + 31.
 //  * O^T += V^T P^T: the B operand is the tile's p' in fp8 straight from the
 //    S^T accumulators of the lane, in register order (32 bytes: both 32-key
-//    score tiles' 16 values); the A operand gathers the same keys in the same
+//    score tiles' 16 values, so scale block kb is keys 32 kb .. + 31 of the
+//    tile); the A operand gathers the same keys in the same
 //    order from the row-major V tile with four ds_read_b64_tr_b8, which hand
 //    lane q of each 16 lanes byte q % 8 of the 8 bytes addressed by lanes
 //    q / 8, q / 8 + 2, .., q / 8 + 14 (measured).  Each addressing lane names
@@ -79,19 +85,40 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, lds_void_t*
 #endif
 }
 
-// One 32x32x64 fp8 x fp8 product (both operands E4M3, no block scaling:
-// scale exponents 127 = 2^0).
-__device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c)
+// One 32x32x64 fp8 x fp8 product (both operands E4M3) with E8M0 block
+// scales: the 64-element reduction is two blocks of 32, block kb being bytes
+// 16 kb .. 16 kb + 15 of both lane halves of a row (measured), and the scale
+// of row i's block kb is byte OPA (OPB) of the scale operand of lane
+// i + 32 kb of A (B).  Scale byte 127 is 2^0.  The byte selects must be
+// constants: the switch folds once the callers' loops are unrolled.
+template <int OPB>
+__device__ __forceinline__ f32x16 mfma8s_b(i32x8 a, i32x8 b, f32x16 c, int sa, int opa, int sb)
 {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    switch (opa) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, OPB, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 1, sa, OPB, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 2, sa, OPB, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 3, sa, OPB, sb);
+    }
+}
+__device__ __forceinline__ f32x16 mfma8s(i32x8 a, i32x8 b, f32x16 c, int sa, int opa, int sb, int opb)
+{
+    return opb == 0 ? mfma8s_b<0>(a, b, c, sa, opa, sb) : mfma8s_b<1>(a, b, c, sa, opa, sb);
 }
 
-template <int D, bool CAUSAL>
+// With MX (block-quantized inputs) a stored byte x of Q or K stands for
+// decode(x) * 2^(s - 127) with s the scale byte of its row's 32-column block
+// (Qs, Ks: [slice][N][D / 32]), a byte of V for decode(x) * 2^(s - 127) with
+// s the byte of its column's 32-key block (Vs: [slice][ceil(N / 32)][D]);
+// the matrix cores apply every block scale, so qk_scale is the softmax
+// scale alone and v_scale is 1.  Without MX the scale pointers are unused.
+template <int D, bool CAUSAL, bool MX>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_fp8_pp_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
-                       const uint8_t* __restrict__ V, __bf16* __restrict__ O,
-                       float* __restrict__ lse, int N, int BH, int nqt, float qk_scale,
-                       float v_scale, int H, int Hkv)
+                       const uint8_t* __restrict__ V, const uint8_t* __restrict__ Qs,
+                       const uint8_t* __restrict__ Ks, const uint8_t* __restrict__ Vs,
+                       __bf16* __restrict__ O, float* __restrict__ lse, int N, int BH, int nqt,
+                       float qk_scale, float v_scale, int H, int Hkv)
 {
     constexpr int NW = 8, BC = 64, BR = 256;
     constexpr int TB = BC * D;                         // tile bytes (unpadded rows of D bytes)
@@ -113,22 +140,69 @@ attn_fwd_fp8_pp_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
     const int q0 = qt * BR;
     const int b = bh / H, hh = bh - b * H;
     const size_t base = (size_t)bh * N * D;
-    const size_t kvbase = ((size_t)b * Hkv + hh / (H / Hkv)) * N * D;
+    const size_t kvs = (size_t)b * Hkv + hh / (H / Hkv);  // key/value slice
+    const size_t kvbase = kvs * N * D;
     const uint32_t slice_b = (uint32_t)N * D;
     const int qw0 = q0 + wave * 32;
     const int qrow = qw0 + j;
 
-    // Q rows as B operands: qf[kk] holds head columns 64 kk + 32 h .. + 31.
+    // Q rows as B operands: qf[kk] holds head columns 64 kk + 16 h .. + 15
+    // in bytes 0-15 and 64 kk + 32 + 16 h .. + 15 in bytes 16-31, so that the
+    // product's reduction block kb is head columns 64 kk + 32 kb .. + 31: one
+    // quantization block of 32 columns.
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, slice_b);
     i32x8 qf[D / 64];
 #pragma unroll
     for (int kk = 0; kk < D / 64; ++kk) {
-        const uint32_t off = (uint32_t)(qrow * D + 64 * kk + 32 * h);
+        const uint32_t off = (uint32_t)(qrow * D + 64 * kk + 16 * h);
         const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
-        const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(qrs, off + 16, 0, 0);
+        const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(qrs, off + 32, 0, 0);
         qf[kk] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
+    // Block scales (MX).  Lane (i, h) supplies the scale of block h of its
+    // row in each product: for Q, byte kk of qsc is block 2 kk + h of query
+    // row qrow.  Rows past N read as zero (and their codes are zero).
+    constexpr int SPR = D / 32;  // scale bytes per row (Q, K)
+    const int nkb = (N + 31) / 32;
+    // Without MX every byte of every scale operand is 127 (2^0).
+    constexpr int kUnitScales = 0x7F7F7F7F;
+    int qsc = kUnitScales;
+    const __amdgpu_buffer_rsrc_t ksrs = make_rsrc(MX ? Ks + kvs * N * SPR : K, MX ? (uint32_t)N * SPR : 0u);
+    const __amdgpu_buffer_rsrc_t vsrs = make_rsrc(MX ? Vs + kvs * nkb * D : V, MX ? (uint32_t)nkb * D : 0u);
+    if constexpr (MX) {
+        const __amdgpu_buffer_rsrc_t qsrs = make_rsrc(Qs + (size_t)bh * N * SPR, (uint32_t)N * SPR);
+        qsc = 0;
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk)
+            qsc |= (int)__builtin_amdgcn_raw_buffer_load_b8(qsrs, (uint32_t)(qrow * SPR + 2 * kk + h), 0, 0)
+                   << (8 * kk);
+    }
+    // K scales of tile kt: byte mt * D / 64 + kk is block 2 kk + h of key row
+    // 64 kt + 32 mt + j.  V scales of tile kt: byte dt is the block of keys
+    // 64 kt + 32 h .. + 31 of head column 32 dt + j.
+    auto load_ksc = [&](int kt) __attribute__((always_inline)) -> int {
+        int w = 0;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int kk = 0; kk < D / 64; ++kk)
+                w |= (int)__builtin_amdgcn_raw_buffer_load_b8(
+                         ksrs, (uint32_t)((64 * kt + 32 * mt + j) * SPR + 2 * kk + h), 0, 0)
+                     << (8 * (mt * (D / 64) + kk));
+        return w;
+    };
+    auto load_vsc = [&](int kt) __attribute__((always_inline)) -> int {
+        int w = 0;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+            w |= (int)__builtin_amdgcn_raw_buffer_load_b8(
+                     vsrs, (uint32_t)((2 * kt + h) * D + 32 * dt + j), 0, 0)
+                 << (8 * dt);
+        return w;
+    };
+    int ksc = kUnitScales, vsc = kUnitScales;  // scales of the next S^T and P V products
+    if constexpr (MX) ksc = load_ksc(0);
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -179,8 +253,9 @@ attn_fwd_fp8_pp_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
     };
 
     // Operand read addresses.  K (S^T A operand): lane (i, h) reads key row
-    // 32 mt + i, chunks 4 kk + 2 h and + 1: kb ^ (64 kk + 16 e).
-    const int kb = j * D + 16 * (kkey(j) ^ (2 * h));
+    // 32 mt + i, chunks 4 kk + h and 4 kk + 2 + h (the arrangement of qf):
+    // kb ^ (64 kk) and kb ^ (64 kk + 32).
+    const int kb = j * D + 16 * (kkey(j) ^ h);
     // V (P V A operand, d-tile dt, read rr): lane l of 16-lane group gq
     // addresses key row 32 (rr >> 1) + 16 (rr & 1) + 8 (b2 >> 2) + 4 h + (b2 & 3)
     // (b2 = (l % 16) / 2: the key of byte b2 of the receiving lanes), bytes
@@ -197,7 +272,7 @@ attn_fwd_fp8_pp_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
     using B1 = std::integral_constant<int, 1>;
     auto kread = [&](auto kbc, int mt, int kk) __attribute__((always_inline)) -> i32x8 {
         const char* p0 = kbuf(kbc) + mt * 32 * D + (kb ^ (64 * kk));
-        const char* p1 = kbuf(kbc) + mt * 32 * D + (kb ^ (64 * kk + 16));
+        const char* p1 = kbuf(kbc) + mt * 32 * D + (kb ^ (64 * kk + 32));
         const u32x4 lo = *reinterpret_cast<const u32x4*>(p0);
         const u32x4 hi = *reinterpret_cast<const u32x4*>(p1);
         return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
@@ -209,7 +284,8 @@ attn_fwd_fp8_pp_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
 #pragma unroll
         for (int kk = 0; kk < D / 64; ++kk)
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) s[mt] = mfma8(kread(kbc, mt, kk), qf[kk], s[mt]);
+            for (int mt = 0; mt < 2; ++mt)
+                s[mt] = mfma8s(kread(kbc, mt, kk), qf[kk], s[mt], ksc, mt * (D / 64) + kk, qsc, kk);
     };
     auto pv = [&](auto vbc) __attribute__((always_inline)) {
 #pragma unroll
@@ -222,7 +298,7 @@ attn_fwd_fp8_pp_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
                 va[2 * rr] = w[0];
                 va[2 * rr + 1] = w[1];
             }
-            acc[dt] = mfma8(va, pf, acc[dt]);
+            acc[dt] = mfma8s(va, pf, acc[dt], vsc, dt, 127, 0);
         }
     };
 
@@ -241,7 +317,13 @@ attn_fwd_fp8_pp_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
             __builtin_amdgcn_sched_barrier(0);
         }
         pv(vbc);
-        if (i < T) qk(kbc);
+        if (i < T) {
+            qk(kbc);
+            if constexpr (MX) {  // scales of P V (tile i) and S^T (tile i + 1), next phase
+                vsc = load_vsc(i);
+                ksc = load_ksc(i + 1);
+            }
+        }
     };
     // Vector phase of step i: mask (last tile only), p' and row sums, fp8
     // conversion, and the rare move of the reference.
@@ -319,10 +401,18 @@ attn_fwd_fp8_pp_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
         if constexpr (!LATE) {
             if (1 < ntiles) load_part(K, kbuf1, 1);
             qk(B0{});
+            if constexpr (MX) {
+                vsc = load_vsc(0);
+                ksc = load_ksc(1);
+            }
             vector_phase(0);
         } else {
             load_part(V, vbuf0, 0);
             qk(B0{});
+            if constexpr (MX) {
+                vsc = load_vsc(0);
+                ksc = load_ksc(1);
+            }
         }
         __syncthreads();  // K(1) and V(0) have landed
         for (int i = 1; i <= ntiles; i += 2) {
@@ -365,16 +455,32 @@ attn_fwd_fp8_pp_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
             (uint32_t)qrow * 4, 0, 0);
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_fp8(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
-                      int N, float qk_scale, float v_scale, int H, int Hkv, hipStream_t stream)
+struct Fp8Args {
+    const void *Q, *K, *V, *Qs, *Ks, *Vs;
+    void* O;
+    float* lse;
+    int BH, N, H, Hkv;
+    float qk_scale, v_scale;
+};
+
+template <int D, bool CAUSAL, bool MX>
+hipError_t launch_fp8(const Fp8Args& a, hipStream_t stream)
 {
-    const int nqt = (N + 255) / 256;
-    attn_fwd_fp8_pp_kernel<D, CAUSAL><<<dim3((unsigned)(nqt * BH)), dim3(512), 0, stream>>>(
-        static_cast<const uint8_t*>(Q), static_cast<const uint8_t*>(K),
-        static_cast<const uint8_t*>(V), static_cast<__bf16*>(O), lse, N, BH, nqt, qk_scale,
-        v_scale, H, Hkv);
+    const int nqt = (a.N + 255) / 256;
+    attn_fwd_fp8_pp_kernel<D, CAUSAL, MX><<<dim3((unsigned)(nqt * a.BH)), dim3(512), 0, stream>>>(
+        static_cast<const uint8_t*>(a.Q), static_cast<const uint8_t*>(a.K),
+        static_cast<const uint8_t*>(a.V), static_cast<const uint8_t*>(a.Qs),
+        static_cast<const uint8_t*>(a.Ks), static_cast<const uint8_t*>(a.Vs),
+        static_cast<__bf16*>(a.O), a.lse, a.N, a.BH, nqt, a.qk_scale, a.v_scale, a.H, a.Hkv);
     return hipGetLastError();
+}
+
+template <bool MX>
+hipError_t dispatch_fp8(const Fp8Args& a, int d, bool causal, hipStream_t stream)
+{
+    if (d == 64)
+        return causal ? launch_fp8<64, true, MX>(a, stream) : launch_fp8<64, false, MX>(a, stream);
+    return causal ? launch_fp8<128, true, MX>(a, stream) : launch_fp8<128, false, MX>(a, stream);
 }
 
 }  // namespace
@@ -383,12 +489,16 @@ hipError_t launch_attn_fwd_fp8(const void* Q, const void* K, const void* V, void
                                int B, int H, int Hkv, int N, int d, float qk_scale, float v_scale,
                                bool causal, hipStream_t stream)
 {
-    const int BH = B * H;
-    if (d == 64)
-        return causal ? launch_fp8<64, true>(Q, K, V, O, lse, BH, N, qk_scale, v_scale, H, Hkv, stream)
-                      : launch_fp8<64, false>(Q, K, V, O, lse, BH, N, qk_scale, v_scale, H, Hkv, stream);
-    return causal ? launch_fp8<128, true>(Q, K, V, O, lse, BH, N, qk_scale, v_scale, H, Hkv, stream)
-                  : launch_fp8<128, false>(Q, K, V, O, lse, BH, N, qk_scale, v_scale, H, Hkv, stream);
+    const Fp8Args a{Q, K, V, nullptr, nullptr, nullptr, O, lse, B * H, N, H, Hkv, qk_scale, v_scale};
+    return dispatch_fp8<false>(a, d, causal, stream);
+}
+
+hipError_t launch_attn_fwd_fp8_mx(const void* Q, const void* Qs, const void* K, const void* Ks,
+                                  const void* V, const void* Vs, void* O, float* lse, int B, int H,
+                                  int Hkv, int N, int d, float scale, bool causal, hipStream_t stream)
+{
+    const Fp8Args a{Q, K, V, Qs, Ks, Vs, O, lse, B * H, N, H, Hkv, scale, 1.0f};
+    return dispatch_fp8<true>(a, d, causal, stream);
 }
 
 }  // namespace osm

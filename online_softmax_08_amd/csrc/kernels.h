@@ -66,6 +66,22 @@ hipError_t launch_attn_bwd_bf16_varlen(const void* Q, const void* K, const void*
 hipError_t launch_attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* lse,
                                int B, int H, int Hkv, int N, int d, float qk_scale, float v_scale,
                                bool causal, hipStream_t stream);
+// Block-quantized fp8 forward: Q, K, V codes as above; Qs [B*H][N][d/32] and
+// Ks [B*Hkv][N][d/32] hold one E8M0 scale byte per 32 head columns of a row,
+// Vs [B*Hkv][ceil(N/32)][d] one per 32 keys of a column; scale is the softmax
+// scale.
+hipError_t launch_attn_fwd_fp8_mx(const void* Q, const void* Qs, const void* K, const void* Ks,
+                                  const void* V, const void* Vs, void* O, float* lse, int B, int H,
+                                  int Hkv, int N, int d, float scale, bool causal, hipStream_t stream);
+// Block quantization of bf16 [rows][d] (d = 64 or 128) to E4M3 codes with one
+// E8M0 scale per 32 columns of a row ([rows][d/32]), after the random-sign
+// Hadamard rotation when rot (bit t of neg_hi:neg_lo set: column t negated).
+hipError_t launch_fp8_quant_rows(const void* X, void* codes, void* scales, long long rows, int d,
+                                 bool rot, uint64_t neg_lo, uint64_t neg_hi, hipStream_t stream);
+// Block quantization of bf16 [slices][n][d] with one scale per 32 rows of a
+// column of each slice ([slices][ceil(n/32)][d]).
+hipError_t launch_fp8_quant_cols(const void* X, void* codes, void* scales, long long slices,
+                                 int n, int d, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const float* Q, const float* K, const float* V, float* O,
                                float* lse, int BH, int N, int d, float scale, bool causal,
                                hipStream_t stream);

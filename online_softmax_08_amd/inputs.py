@@ -157,6 +157,51 @@ def attn_inputs_fp8(w: AttnWorkload, *, B: int | None = None, H: int | None = No
     return (q8, k8, v8), (qs, ks, vs)
 
 
+def hadamard_signs(d: int, seed: int) -> list:
+    """d random signs (+1 or -1) for the Hadamard rotation, from a generator
+    of their own; the rotation itself is the method's and is not here."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return [1 if b else -1 for b in torch.randint(0, 2, (d,), generator=g).tolist()]
+
+
+def attn_inputs_outliers(*, B: int, H: int, N: int, d: int, seed: int, channels: int = 4,
+                         factor: float = 20.0):
+    """bf16 Q, K, V of N(0, 1) draws (attn_inputs' order) whose Q and K carry
+    outlier head channels: ``channels`` columns, drawn from the same
+    generator, multiplied by ``factor`` (the large, channel-aligned values
+    that make one scale per tensor lose precision).  CPU tensors."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    shape = (B, H, N, d)
+    q, k, v = (torch.randn(shape, generator=g, dtype=torch.float32) for _ in range(3))
+    ch = torch.randperm(d, generator=g)[:channels]
+    q[..., ch] *= factor
+    k[..., ch] *= factor
+    return tuple(t.to(torch.bfloat16).contiguous() for t in (q, k, v))
+
+
+def attn_inputs_blockwise(*, B: int, H: int, N: int, d: int, seed: int, Hkv: int | None = None):
+    """bf16 Q, K, V of N(0, 1) draws whose 32-element blocks along each
+    contracted axis (32 head columns of a Q or K row, 32 rows of a V column)
+    are multiplied by powers of two from 2^-4 to 2^4, and with some blocks
+    set to zero: inputs whose block scales all differ.  CPU tensors."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    shape = (B, H, N, d)
+    q, k, v = (torch.randn(shape, generator=g, dtype=torch.float32) for _ in range(3))
+    nb = (N + 31) // 32
+    for t in (q, k):
+        e = torch.randint(-4, 5, (B, H, N, d // 32), generator=g).to(torch.float32)
+        e[torch.rand((B, H, N, d // 32), generator=g) < 0.02] = float("-inf")  # zero blocks
+        t *= torch.exp2(e).repeat_interleave(32, dim=-1)
+    e = torch.randint(-4, 5, (B, H, nb, d), generator=g).to(torch.float32)
+    v *= torch.exp2(e).repeat_interleave(32, dim=2)[:, :, :N]
+    if Hkv is not None:
+        k, v = k[:, :Hkv], v[:, :Hkv]
+    return tuple(t.to(torch.bfloat16).contiguous() for t in (q, k, v))
+
+
 def grad_output(shape, seed: int, dtype: str = "bf16") -> torch.Tensor:
     """The upstream gradient dO for a backward test: N(0, 1) of ``shape`` from
     its own generator (seed), so Q, K, V stay those of the forward recipe."""

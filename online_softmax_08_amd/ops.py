@@ -92,6 +92,94 @@ def attention_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_scale: fl
     return out, lse
 
 
+def quantize_fp8_rows(x: torch.Tensor, signs=None):
+    """Block quantization of a bf16 tensor [..., d] (contiguous, on a GPU) along
+    its last axis: one power-of-two scale per 32 elements, after the
+    random-sign Hadamard rotation when signs (d values +-1, any sequence or
+    CPU tensor) is given.  Returns (codes uint8 [..., d], scale bytes uint8
+    [..., d / 32])."""
+    if not x.is_cuda or x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 GPU tensor")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if signs is not None:
+        signs = [int(s) for s in (signs.tolist() if isinstance(signs, torch.Tensor) else signs)]
+        if len(signs) != d:
+            raise ValueError("signs must hold d values")
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(tuple(x.shape[:-1]) + (d // 32,), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        _abi.fp8_quantize_rows(x.data_ptr(), signs, codes.data_ptr(), scales.data_ptr(), rows, d,
+                               _stream_handle(x.device))
+    return codes, scales
+
+
+def quantize_fp8_cols(x: torch.Tensor):
+    """Block quantization of a bf16 tensor [..., n, d] along the rows of each
+    column of every [n, d] slice (the layout attention_fp8_mx takes for V).
+    Returns (codes uint8 [..., n, d], scale bytes uint8 [..., ceil(n / 32), d])."""
+    if not x.is_cuda or x.dtype != torch.bfloat16 or not x.is_contiguous() or x.dim() < 2:
+        raise ValueError("x must be a contiguous bf16 GPU tensor [..., n, d]")
+    n, d = x.shape[-2], x.shape[-1]
+    slices = x.numel() // (n * d) if n * d else 0
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(tuple(x.shape[:-2]) + ((n + 31) // 32, d), dtype=torch.uint8,
+                         device=x.device)
+    with torch.cuda.device(x.device):
+        _abi.fp8_quantize_cols(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), slices, n, d,
+                               _stream_handle(x.device))
+    return codes, scales
+
+
+def attention_fp8_mx(q8: torch.Tensor, q_scales: torch.Tensor, k8: torch.Tensor,
+                     k_scales: torch.Tensor, v8: torch.Tensor, v_scales: torch.Tensor,
+                     causal: bool = False, scale: float | None = None):
+    """attention() on block-quantized fp8 inputs: codes q8 [B, H, N, d], k8, v8
+    [B, Hkv, N, d] (uint8 or float8_e4m3fn) with scale bytes q_scales
+    [B, H, N, d/32], k_scales [B, Hkv, N, d/32], v_scales [B, Hkv, ceil(N/32), d]
+    (what quantize_fp8_rows / quantize_fp8_cols return).  Returns (O bf16,
+    lse fp32); scale defaults to 1/sqrt(d)."""
+    ts = (q8, k8, v8, q_scales, k_scales, v_scales)
+    if not all(t.is_cuda and t.is_contiguous() for t in ts):
+        raise ValueError("every tensor must be a contiguous GPU tensor")
+    if not all(t.dtype in (torch.uint8, torch.float8_e4m3fn) for t in (q8, k8, v8)):
+        raise ValueError("q8, k8, v8 must hold FP8 E4M3 codes (uint8 or float8_e4m3fn)")
+    if not all(t.dtype == torch.uint8 for t in (q_scales, k_scales, v_scales)):
+        raise ValueError("scale bytes must be uint8")
+    if q8.dim() != 4 or k8.shape != v8.shape:
+        raise ValueError("q8 must be [B, H, N, d] and k8, v8 one [B, Hkv, N, d] shape")
+    B, H, N, d = q8.shape
+    Hkv = k8.shape[1]
+    if k8.shape[0] != B or k8.shape[2] != N or k8.shape[3] != d or Hkv < 1 or H % Hkv:
+        raise ValueError("k8, v8 must be [B, Hkv, N, d] with Hkv dividing q8's H")
+    if (q_scales.shape != (B, H, N, d // 32) or k_scales.shape != (B, Hkv, N, d // 32)
+            or v_scales.shape != (B, Hkv, (N + 31) // 32, d)):
+        raise ValueError("scale bytes must be [B, H, N, d/32], [B, Hkv, N, d/32] and "
+                         "[B, Hkv, ceil(N/32), d]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    with torch.cuda.device(q8.device):
+        _abi.attn_fwd_fp8_mx(q8.data_ptr(), q_scales.data_ptr(), k8.data_ptr(), k_scales.data_ptr(),
+                             v8.data_ptr(), v_scales.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                             B, H, Hkv, N, d, scale, causal, _stream_handle(q8.device))
+    return out, lse
+
+
+def attention_fp8_block(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, signs=None,
+                        causal: bool = False, scale: float | None = None):
+    """FP8 attention of bf16 q, k, v with the accuracy devices of the FP8
+    method: q and k rotated by diag(signs) H / sqrt(d) (skipped when signs is
+    None) and block-quantized along the head dimension, v block-quantized
+    along the keys, then attention_fp8_mx.  Every step runs in the HIP
+    library.  Returns (O bf16, lse fp32), the attention of the unrotated
+    inputs up to the fp8 error."""
+    q8, qs = quantize_fp8_rows(q, signs)
+    k8, ks = quantize_fp8_rows(k, signs)
+    v8, vs = quantize_fp8_cols(v)
+    return attention_fp8_mx(q8, qs, k8, ks, v8, vs, causal=causal, scale=scale)
+
+
 def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = False,
                      scale: float | None = None):

@@ -24,7 +24,8 @@ def abi():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_gqa",
-                                            "attn_fwd_fp8",
+                                            "attn_fwd_fp8", "attn_fwd_fp8_mx",
+                                            "fp8_quantize_rows", "fp8_quantize_cols",
                                             "attn_fwd_varlen",
                                             "attn_fwd_splitkv_plan",
                                             "attn_fwd_splitkv", "attn_combine",
@@ -59,14 +60,14 @@ def test_status_code_numbering(abi):
     assert codes == {"OSM_OK": 0, "OSM_ERR_NULL": 1, "OSM_ERR_SIZE": 2, "OSM_ERR_HEAD_DIM": 3,
                      "OSM_ERR_SCALE": 4, "OSM_ERR_ALIAS": 5, "OSM_ERR_HIP": 6, "OSM_ERR_ALIGN": 7,
                      "OSM_ERR_DEVICE": 8, "OSM_ERR_SPLITS": 9, "OSM_ERR_WORKSPACE": 10,
-                     "OSM_ERR_HEADS": 11, "OSM_ERR_SCRATCH": 12}
+                     "OSM_ERR_HEADS": 11, "OSM_ERR_SCRATCH": 12, "OSM_ERR_SIGNS": 13}
     for name, value in codes.items():
         assert getattr(abi, name) == value, name
     assert "runtime" in abi.osm_status_str(6) and "aligned" in abi.osm_status_str(7)
 
 
 def test_status_strings(abi):
-    for st in range(0, 13):
+    for st in range(0, 14):
         assert abi.osm_status_str(st) and abi.osm_status_str(st) != "unknown status"
     assert abi.osm_status_str(99) == "unknown status"
 
@@ -445,3 +446,73 @@ def test_fp8_validation(abi):
     assert status(lse=far["O"] + 1024) == abi.OSM_ERR_ALIAS
     assert status() in (abi.OSM_ERR_HIP, abi.OSM_ERR_DEVICE)
     abi.attn_fwd_fp8(0, 0, 0, 1.0, 1.0, 1.0, 0, 0, 0, 4, 4, 128, 64, 0.125, 0)  # empty: no-op
+
+
+def test_fp8_mx_validation(abi):
+    # attn_fwd_fp8_mx checks sizes, pointers (codes and scale bytes),
+    # alignment and overlaps of O and lse with all six inputs before any HIP
+    # call.
+    names = ("Q", "qs", "K", "ks", "V", "vs", "O", "lse")
+    far = {n: (i + 1) << 36 for i, n in enumerate(names)}
+
+    def status(**kw):
+        a = dict(far, B=1, H=4, Hkv=2, N=100, d=128, scale=0.125, causal=1)
+        a.update(kw)
+        with pytest.raises(abi.OsmError) as e:
+            abi.attn_fwd_fp8_mx(*(a[n] for n in names), a["B"], a["H"], a["Hkv"], a["N"],
+                                a["d"], a["scale"], a["causal"])
+        return e.value.status
+    assert status(d=96) == abi.OSM_ERR_HEAD_DIM
+    assert status(N=-1) == abi.OSM_ERR_SIZE
+    assert status(scale=float("nan")) == abi.OSM_ERR_SCALE
+    assert status(Hkv=3) == abi.OSM_ERR_HEADS
+    for n in names:
+        assert status(**{n: 0}) == abi.OSM_ERR_NULL, n
+    assert status(V=far["V"] + 8) == abi.OSM_ERR_ALIGN
+    assert status(lse=far["lse"] + 2) == abi.OSM_ERR_ALIGN
+    # v_scales of [1][2][ceil(100/32)=4][128] = 1024 bytes: O just inside, then just past
+    assert status(O=far["vs"] + 1008) == abi.OSM_ERR_ALIAS
+    assert status(O=far["vs"] + 1024) in (abi.OSM_ERR_HIP, abi.OSM_ERR_DEVICE)
+    assert status(lse=far["ks"] + 796) == abi.OSM_ERR_ALIAS  # k_scales: 2 * 100 * 4 = 800 bytes
+    assert status(lse=far["O"] + 1024) == abi.OSM_ERR_ALIAS
+    assert status() in (abi.OSM_ERR_HIP, abi.OSM_ERR_DEVICE)
+    abi.attn_fwd_fp8_mx(*([0] * 8), 1, 4, 4, 0, 64, 0.125, 0)  # empty: no-op
+
+
+def test_fp8_quantize_validation(abi):
+    far = {n: (i + 1) << 36 for i, n in enumerate(("X", "c", "s"))}
+
+    def rows_status(signs=None, **kw):
+        a = dict(far, rows=10, d=128)
+        a.update(kw)
+        with pytest.raises(abi.OsmError) as e:
+            abi.fp8_quantize_rows(a["X"], signs, a["c"], a["s"], a["rows"], a["d"])
+        return e.value.status
+
+    def cols_status(**kw):
+        a = dict(far, slices=3, n=45, d=64)
+        a.update(kw)
+        with pytest.raises(abi.OsmError) as e:
+            abi.fp8_quantize_cols(a["X"], a["c"], a["s"], a["slices"], a["n"], a["d"])
+        return e.value.status
+    assert rows_status(d=96) == abi.OSM_ERR_HEAD_DIM
+    assert rows_status(rows=-1) == abi.OSM_ERR_SIZE
+    assert rows_status(signs=[1] * 127 + [0]) == abi.OSM_ERR_SIGNS
+    assert rows_status(signs=[1] * 64 + [2] + [-1] * 63) == abi.OSM_ERR_SIGNS
+    assert rows_status(c=0) == abi.OSM_ERR_NULL
+    assert rows_status(X=far["X"] + 8) == abi.OSM_ERR_ALIGN
+    assert rows_status(c=far["c"] + 4) == abi.OSM_ERR_ALIGN
+    assert rows_status(s=far["X"] + 2558) == abi.OSM_ERR_ALIAS  # X: 10 * 128 * 2 bytes
+    assert rows_status(s=far["c"] + 1279) == abi.OSM_ERR_ALIAS  # codes: 1280 bytes
+    assert rows_status() in (abi.OSM_ERR_HIP, abi.OSM_ERR_DEVICE)
+    assert rows_status(signs=[1, -1] * 64) in (abi.OSM_ERR_HIP, abi.OSM_ERR_DEVICE)
+    abi.fp8_quantize_rows(0, None, 0, 0, 0, 64)  # empty: no-op
+    assert cols_status(d=32) == abi.OSM_ERR_HEAD_DIM
+    assert cols_status(n=-5) == abi.OSM_ERR_SIZE
+    assert cols_status(X=0) == abi.OSM_ERR_NULL
+    assert cols_status(c=far["c"] + 12) == abi.OSM_ERR_ALIGN
+    # scales: 3 * ceil(45 / 32) * 64 = 384 bytes
+    assert cols_status(c=far["s"] + 376) == abi.OSM_ERR_ALIAS
+    assert cols_status(c=far["s"] + 384) in (abi.OSM_ERR_HIP, abi.OSM_ERR_DEVICE)
+    assert cols_status() in (abi.OSM_ERR_HIP, abi.OSM_ERR_DEVICE)
+    abi.fp8_quantize_cols(0, 0, 0, 0, 45, 64)  # empty: no-op

@@ -254,7 +254,7 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10, warm_ms=15.
     of the headline workload (its FLOPs counted as 2.5 times the forward's,
     the five products of the gradient; the kernels compute seven), the
     split backward on the long-row input, and the fp8 forward on the headline
-    shape."""
+    shape with per-tensor and with block scales (and the block quantizers)."""
     import torch
 
     from online_softmax_08_amd import inputs
@@ -389,8 +389,34 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10, warm_ms=15.
         fp8["causal" if causal else "noncausal"] = {
             "tflops_median": round(tf, 1), "frac_median": round(tf / PEAK_FP8_TFLOPS, 4),
             "ms_median": round(median(t), 4), "ms_min": round(min(t), 4)}
+    # The block-quantized fp8 forward on the same inputs: Q and K rotated
+    # (random signs, Hadamard) and quantized with a power-of-two scale per 32
+    # head columns, V per 32 keys of a column, by the library's quantizers
+    # (timed on their own, HBM bytes: 2 read + 1 + 1/32 written per element);
+    # the attention against the fp8 peak.
+    signs = inputs.hadamard_signs(wa.d, seed=wa.seed + 1)
+    qm, qsm = osm.quantize_fp8_rows(q, signs)
+    km, ksm = osm.quantize_fp8_rows(k, signs)
+    vm, vsm = osm.quantize_fp8_cols(v)
+    qbytes = q.numel() * (3 + 1 / 32)
+    t_rows = median(launch_times(lambda: osm.quantize_fp8_rows(q, signs)))
+    t_cols = median(launch_times(lambda: osm.quantize_fp8_cols(v)))
+    fp8mx = {"workload": f"fp8 (E4M3, block scales per 32 elements, Q and K rotated) "
+                         f"B={wa.B} H={wa.H} N={wa.N} d={wa.d}, inputs of the headline recipe",
+             "peak_tflops": PEAK_FP8_TFLOPS,
+             "quantize_rows_rotated_gbs": round(qbytes / (t_rows * 1e-3) / 1e9, 1),
+             "quantize_cols_gbs": round(qbytes / (t_cols * 1e-3) / 1e9, 1),
+             "quantize_rows_ms": round(t_rows, 4), "quantize_cols_ms": round(t_cols, 4)}
+    for causal in (False, True):
+        t = launch_times(lambda: osm.attention_fp8_mx(qm, qsm, km, ksm, vm, vsm, causal=causal))
+        flops = 4.0 * wa.B * wa.H * wa.N * wa.N * wa.d / (2 if causal else 1)
+        tf = flops / (median(t) * 1e-3) / 1e12
+        fp8mx["causal" if causal else "noncausal"] = {
+            "tflops_median": round(tf, 1), "frac_median": round(tf / PEAK_FP8_TFLOPS, 4),
+            "ms_median": round(median(t), 4), "ms_min": round(min(t), 4)}
     return {
         "attn_fp8": fp8,
+        "attn_fp8_block": fp8mx,
         "attn_backward": {"workload": f"{wa.name} backward (dQ, dK, dV)",
                           "value": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 1), "unit": "TFLOPS",
                           "flops_per_call": bwd_flops, "call_ms": round(bwd_ms, 4)},

@@ -182,15 +182,24 @@ attn_fwd_fp8_pp_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
     // 64 kt + 32 mt + j.  V scales of tile kt: byte dt is the block of keys
     // 64 kt + 32 h .. + 31 of head column 32 dt + j.
     auto load_ksc = [&](int kt) __attribute__((always_inline)) -> int {
-        int w = 0;
+        if constexpr (D == 128) {
+            // the two rows' four scale bytes each, then bytes h and 2 + h of
+            // row 32 mt + j into bytes 2 mt and 2 mt + 1 (v_perm_b32: selector
+            // values 0-3 pick bytes of the second operand, 4-7 of the first)
+            const uint32_t r0 = __builtin_amdgcn_raw_buffer_load_b32(
+                ksrs, (uint32_t)((64 * kt + j) * SPR), 0, 0);
+            const uint32_t r1 = __builtin_amdgcn_raw_buffer_load_b32(
+                ksrs, (uint32_t)((64 * kt + 32 + j) * SPR), 0, 0);
+            return (int)__builtin_amdgcn_perm(r1, r0, 0x06040200u + 0x01010101u * (uint32_t)h);
+        } else {
+            int w = 0;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int kk = 0; kk < D / 64; ++kk)
+            for (int mt = 0; mt < 2; ++mt)
                 w |= (int)__builtin_amdgcn_raw_buffer_load_b8(
-                         ksrs, (uint32_t)((64 * kt + 32 * mt + j) * SPR + 2 * kk + h), 0, 0)
-                     << (8 * (mt * (D / 64) + kk));
-        return w;
+                         ksrs, (uint32_t)((64 * kt + 32 * mt + j) * SPR + h), 0, 0)
+                     << (8 * mt);
+            return w;
+        }
     };
     auto load_vsc = [&](int kt) __attribute__((always_inline)) -> int {
         int w = 0;
@@ -244,9 +253,14 @@ attn_fwd_fp8_pp_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
     // a tile past the last one gets an empty range (its loads fill dst with
     // zeros, which no later step reads).
     auto load_part = [&](const uint8_t* X, char* dst, int kt) __attribute__((always_inline)) {
+        // kt and the range are wave-uniform; said explicitly, because the
+        // compiler otherwise keeps the late group's range in a vector
+        // register and wraps each load in a loop over its distinct values.
+        kt = __builtin_amdgcn_readfirstlane(kt);
         const int kv0 = kt * BC;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(X + kvbase + (size_t)kv0 * D,
-                                                    kt < ntiles ? (uint32_t)(N - kv0) * D : 0u);
+        const uint32_t range = (uint32_t)__builtin_amdgcn_readfirstlane(
+            kt < ntiles ? (int)((uint32_t)(N - kv0) * D) : 0);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(X + kvbase + (size_t)kv0 * D, range);
         lds_void_t* const d = (lds_void_t*)(dst + g * LPW * 1024);
         lds_dma16<0>(rs, d, src[0]);
         if constexpr (LPW > 1) lds_dma16<1024>(rs, d, src[1]);

@@ -18,14 +18,15 @@
 // element is the E4M3 code of x / 2^e, rounded to nearest with ties to the
 // even code by v_cvt_pk_fp8_f32 (measured on every midpoint of the format).
 //
-// Both kernels are HBM bound: 2 bytes read and 1 + 1/32 written per element.
-//  * fp8_quant_rows_kernel: d / 8 lanes per row, 8 elements per lane (one
-//    16-byte load).  The rotation: sign flips, the fast Walsh-Hadamard
-//    transform in fp32 (three butterfly stages inside the lane, log2(d / 8)
-//    across lanes by lane swaps), then 1 / sqrt(d).  A block is 4 lanes; its
-//    maximum takes two lane swaps.
-//  * fp8_quant_cols_kernel: one workgroup per block row (32 rows x d) of a
-//    slice, coalesced row loads, the column maxima through LDS.
+// Both kernels move 2 bytes in and 1 + 1/32 out per element (HBM bound),
+// and keep each block in one thread so that its maximum needs no exchange:
+//  * fp8_quant_rows_kernel: d / 32 lanes per row, one block of 32 elements
+//    per lane.  The rotation is the fast Walsh-Hadamard transform in fp32:
+//    five butterfly stages inside the lane and log2(d / 32) across the lanes
+//    of the row by DPP swaps, after the sign flips and before 1 / sqrt(d).
+//  * fp8_quant_cols_kernel: a quad of threads per 8 columns of a 32-row
+//    block, 8 rows per thread held in registers, the column maxima combined
+//    by DPP swaps inside the quad.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -59,112 +60,142 @@ __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d)
     return (uint32_t)w;
 }
 
+// Lane swaps inside quads (DPP quad_perm): the value of lane ^ 1 or lane ^ 2.
+template <int M>
+__device__ __forceinline__ float quad_xor(float v)
+{
+    static_assert(M == 1 || M == 2, "quad_perm swaps");
+    constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;  // [1,0,3,2] / [2,3,0,1]
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+
+// Rows: D / 32 lanes per row (a quad or half a quad), each holding one block
+// of 32 consecutive elements (four 16-byte loads), so a block's maximum is
+// in-lane.  The rotation: sign flips, the five butterfly stages of the
+// element bits inside the lane, the one or two of the lane bits by DPP lane
+// swaps, then 1 / sqrt(D).
 template <int D, bool ROT>
 __global__ void __launch_bounds__(256)
 fp8_quant_rows_kernel(const __bf16* __restrict__ X, uint8_t* __restrict__ codes,
                       uint8_t* __restrict__ scales, long long rows, uint64_t neg_lo,
                       uint64_t neg_hi)
 {
-    constexpr int LPR = D / 8, RPB = 256 / LPR;
-    const int l = threadIdx.x % LPR;  // this lane holds elements 8 l .. 8 l + 7 of its row
+    constexpr int LPR = D / 32, RPB = 256 / LPR;
+    const int l = threadIdx.x % LPR;  // this lane holds elements 32 l .. 32 l + 31 of its row
+    // bit u set: element 32 l + u is negated (s_t = -1)
+    const uint32_t neg = l == 0 ? (uint32_t)neg_lo : l == 1 ? (uint32_t)(neg_lo >> 32)
+                       : l == 2 ? (uint32_t)neg_hi : (uint32_t)(neg_hi >> 32);
     for (long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR; row < rows;
          row += (long long)gridDim.x * RPB) {
-        const bf16x8 xv = *reinterpret_cast<const bf16x8*>(X + row * D + 8 * l);
-        float v[8];
+        float v[32];
+        const __bf16* src = X + row * D + 32 * l;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (float)xv[e];
+        for (int k = 0; k < 4; ++k) {
+            const bf16x8 xv = *reinterpret_cast<const bf16x8*>(src + 8 * k);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[8 * k + e] = (float)xv[e];
+        }
         if constexpr (ROT) {
-            // x diag(s): bit t of (neg_hi:neg_lo) set means s_t = -1.
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = 8 * l + e;
-                const uint64_t bit = t < 64 ? (neg_lo >> t) & 1u : (neg_hi >> (t - 64)) & 1u;
-                if (bit) v[e] = -v[e];
-            }
-            // y = x H (Sylvester order, y_k = sum_t x_t (-1)^popcount(t & k)):
-            // one butterfly stage per bit of the element index, (a, b) ->
-            // (a + b, a - b) for the pair whose index differs in that bit.
+            for (int u = 0; u < 32; ++u)
+                v[u] = __int_as_float(__float_as_int(v[u]) ^ (int)((neg >> u) << 31));
+            // y = x H (Sylvester order): one butterfly stage per bit of the
+            // element index, (a, b) -> (a + b, a - b) for the pair whose
+            // index differs in that bit.
 #pragma unroll
-            for (int st = 1; st < 8; st <<= 1)
+            for (int st = 1; st < 32; st <<= 1)
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (!(e & st)) {
-                        const float a = v[e], b = v[e + st];
-                        v[e] = a + b;
-                        v[e + st] = a - b;
+                for (int u = 0; u < 32; ++u)
+                    if (!(u & st)) {
+                        const float a = v[u], b = v[u + st];
+                        v[u] = a + b;
+                        v[u + st] = a - b;
                     }
+            // lane bits: own + partner where the bit is clear, partner - own
+            // where it is set
+            const float s1 = (l & 1) ? -1.f : 1.f;
 #pragma unroll
-            for (int m = 1; m < LPR; m <<= 1)
+            for (int u = 0; u < 32; ++u) v[u] = fmaf(v[u], s1, quad_xor<1>(v[u]));
+            if constexpr (LPR == 4) {
+                const float s2 = (l & 2) ? -1.f : 1.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float p = __shfl_xor(v[e], m);
-                    v[e] = (l & m) ? p - v[e] : v[e] + p;
-                }
+                for (int u = 0; u < 32; ++u) v[u] = fmaf(v[u], s2, quad_xor<2>(v[u]));
+            }
             const float norm = D == 64 ? 0.125f : 0.0883883476483184406f;  // 1 / sqrt(D)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] *= norm;
+            for (int u = 0; u < 32; ++u) v[u] *= norm;
         }
         float am = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(v[e]));
-        am = fmaxf(am, __shfl_xor(am, 1));
-        am = fmaxf(am, __shfl_xor(am, 2));
+        for (int u = 0; u < 32; ++u) am = fmaxf(am, fabsf(v[u]));
         const int ex = block_exponent(am);
+        u32x4 c[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = ldexpf(v[e], -ex);
-        const uint2 c8 = {pack4(v[0], v[1], v[2], v[3]), pack4(v[4], v[5], v[6], v[7])};
-        *reinterpret_cast<uint2*>(codes + row * D + 8 * l) = c8;
-        if ((l & 3) == 0) scales[row * (D / 32) + l / 4] = (uint8_t)(ex + 127);
+        for (int w = 0; w < 8; ++w)
+            c[w >> 2][w & 3] = pack4(ldexpf(v[4 * w], -ex), ldexpf(v[4 * w + 1], -ex),
+                                     ldexpf(v[4 * w + 2], -ex), ldexpf(v[4 * w + 3], -ex));
+        uint8_t* dst = codes + row * D + 32 * l;
+        *reinterpret_cast<u32x4*>(dst) = c[0];
+        *reinterpret_cast<u32x4*>(dst + 16) = c[1];
+        scales[row * (D / 32) + l] = (uint8_t)(ex + 127);
     }
 }
 
+// Columns: a quad of threads owns 8 adjacent columns of one block (32 rows
+// of one slice), each thread 8 of its rows (one 16-byte load per row; the
+// D / 2 threads of a block read each row whole); the column maxima are
+// combined over the quad by two DPP swaps.
 template <int D>
 __global__ void __launch_bounds__(256)
 fp8_quant_cols_kernel(const __bf16* __restrict__ X, uint8_t* __restrict__ codes,
                       uint8_t* __restrict__ scales, long long nblocks, int n)
 {
-    constexpr int LPR = D / 8, RPT = 256 / LPR, TRIPS = 32 / RPT;
-    __shared__ float mag[32][D];
-    __shared__ int ecol[D];
+    constexpr int TPB = D / 2, BPW = 256 / TPB;  // threads per block, blocks per workgroup
     const int nb = (n + 31) / 32;
-    const int c8 = threadIdx.x % LPR;
-    for (long long blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+    const int rq = threadIdx.x & 3, c8 = (threadIdx.x % TPB) >> 2;
+    for (long long blk = (long long)blockIdx.x * BPW + threadIdx.x / TPB; blk < nblocks;
+         blk += (long long)gridDim.x * BPW) {
         const long long sl = blk / nb;
         const int r0 = (int)(blk - sl * nb) * 32;
-        const __bf16* xs = X + (size_t)sl * n * D;
-        float v[TRIPS][8];
+        const int nr = min(32, n - r0);
+        const __bf16* xs = X + ((size_t)sl * n + r0) * D + 8 * c8;
+        u32x4 raw[8];
 #pragma unroll
-        for (int it = 0; it < TRIPS; ++it) {
-            const int r = it * RPT + threadIdx.x / LPR;
-            bf16x8 xv = {};
-            if (r0 + r < n) xv = *reinterpret_cast<const bf16x8*>(xs + (size_t)(r0 + r) * D + 8 * c8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                v[it][e] = (float)xv[e];
-                mag[r][8 * c8 + e] = fabsf(v[it][e]);
-            }
+        for (int k = 0; k < 8; ++k) {
+            const int r = 8 * rq + k;
+            raw[k] = r < nr ? *reinterpret_cast<const u32x4*>(xs + (size_t)r * D) : u32x4{0, 0, 0, 0};
         }
-        __syncthreads();
-        if (threadIdx.x < D) {
-            float am = 0.f;
-#pragma unroll 8
-            for (int r = 0; r < 32; ++r) am = fmaxf(am, mag[r][threadIdx.x]);
-            const int ex = block_exponent(am);
-            ecol[threadIdx.x] = ex;
-            scales[((size_t)sl * nb + r0 / 32) * D + threadIdx.x] = (uint8_t)(ex + 127);
-        }
-        __syncthreads();
+        float am[8] = {};
 #pragma unroll
-        for (int it = 0; it < TRIPS; ++it) {
-            const int r = it * RPT + threadIdx.x / LPR;
-            if (r0 + r >= n) continue;
+        for (int k = 0; k < 8; ++k) {
+            const bf16x8 xv = __builtin_bit_cast(bf16x8, raw[k]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) am[e] = fmaxf(am[e], fabsf((float)xv[e]));
+        }
+        int ex[8];
+        uint32_t sb[2] = {0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            am[e] = fmaxf(am[e], quad_xor<1>(am[e]));
+            am[e] = fmaxf(am[e], quad_xor<2>(am[e]));
+            ex[e] = block_exponent(am[e]);
+            sb[e >> 2] |= (uint32_t)(ex[e] + 127) << (8 * (e & 3));
+        }
+        if (rq == 0)
+            *reinterpret_cast<uint2*>(scales + ((size_t)sl * nb + r0 / 32) * D + 8 * c8) =
+                uint2{sb[0], sb[1]};
+        uint8_t* dst = codes + ((size_t)sl * n + r0) * D + 8 * c8;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int r = 8 * rq + k;
+            if (r >= nr) break;
+            const bf16x8 xv = __builtin_bit_cast(bf16x8, raw[k]);
             float w[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = ldexpf(v[it][e], -ecol[8 * c8 + e]);
-            const uint2 c = {pack4(w[0], w[1], w[2], w[3]), pack4(w[4], w[5], w[6], w[7])};
-            *reinterpret_cast<uint2*>(codes + ((size_t)sl * n + r0 + r) * D + 8 * c8) = c;
+            for (int e = 0; e < 8; ++e) w[e] = ldexpf((float)xv[e], -ex[e]);
+            *reinterpret_cast<uint2*>(dst + (size_t)r * D) =
+                uint2{pack4(w[0], w[1], w[2], w[3]), pack4(w[4], w[5], w[6], w[7])};
         }
-        __syncthreads();  // mag and ecol are rewritten by the next block
     }
 }
 
@@ -172,7 +203,7 @@ template <int D>
 hipError_t rows_launch(const void* X, void* codes, void* scales, long long rows, bool rot,
                        uint64_t neg_lo, uint64_t neg_hi, hipStream_t stream)
 {
-    constexpr int RPB = 256 / (D / 8);
+    constexpr int RPB = 256 / (D / 32);
     const long long need = (rows + RPB - 1) / RPB;
     const unsigned grid = (unsigned)(need < 65536 ? need : 65536);
     const auto* x = static_cast<const __bf16*>(X);
@@ -198,7 +229,8 @@ hipError_t launch_fp8_quant_cols(const void* X, void* codes, void* scales, long 
                                  int n, int d, hipStream_t stream)
 {
     const long long nblocks = slices * ((n + 31) / 32);
-    const unsigned grid = (unsigned)(nblocks < 65536 ? nblocks : 65536);
+    const long long need = (nblocks + 256 / (d / 2) - 1) / (256 / (d / 2));
+    const unsigned grid = (unsigned)(need < 65536 ? need : 65536);
     const auto* x = static_cast<const __bf16*>(X);
     auto* c = static_cast<uint8_t*>(codes);
     auto* s = static_cast<uint8_t*>(scales);

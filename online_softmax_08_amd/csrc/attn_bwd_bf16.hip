@@ -199,16 +199,24 @@ attn_bwd_delta_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ d
     const int c8 = threadIdx.x % LPR;
     for (long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR; row < rows;
          row += (long long)gridDim.x * RPB) {
+        // all three loads first (every lane of the row reads its lse, one
+        // cache line), so that a row costs one memory round trip
         const bf16x8 o = *reinterpret_cast<const bf16x8*>(O + row * D + 8 * c8);
         const bf16x8 g = *reinterpret_cast<const bf16x8*>(dO + row * D + 8 * c8);
+        float L = lse[row];
+        asm volatile("" : "+v"(L));  // keeps the load here instead of sunk into the branch
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) s = fmaf((float)o[e], (float)g[e], s);
-#pragma unroll
-        for (int w = LPR / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, LPR);
+        // sum over the row's LPR lanes (a 16- or 8-lane group) by DPP:
+        // quads, then the two quads of a half-row, then the two half-rows
+        s += dpp<0xB1>(s);   // quad_perm [1,0,3,2]
+        s += dpp<0x4E>(s);   // quad_perm [2,3,0,1]
+        s += dpp<0x141>(s);  // row_half_mirror
+        if constexpr (LPR == 16) s += dpp<0x140>(s);  // row_mirror
         if (c8 == 0) {
             Dl[row] = s;
-            Lc[row] = lse[row] * kLog2e;
+            Lc[row] = L * kLog2e;
         }
     }
 }

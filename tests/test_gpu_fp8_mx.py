@@ -77,6 +77,29 @@ def test_quantize_cols_exact(osm, shape):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+def test_quantize_extreme_magnitudes(osm, d):
+    # Blocks near the top of the bf16 range (2^125), tiny normals (2^-120),
+    # bf16 subnormals (2^-130, whose scale byte clamps at 0 = 2^-127), mixed
+    # blocks and exact zeros: scales and codes bit for bit, rows and columns.
+    g = torch.Generator().manual_seed(9150 + d)
+    x = torch.randn((1, 1, 64, d), generator=g)
+    mags = [2.0 ** 125, 2.0 ** -120, 2.0 ** -130, 1.0, 0.0, 2.0 ** 100, 2.0 ** -133, 3.0]
+    for r in range(64):
+        x[0, 0, r] *= mags[r % len(mags)]
+    x[0, 0, 3, :16] *= 2.0 ** -20  # a block mixing two magnitudes
+    x = x.to(torch.bfloat16)
+    codes, scales = osm.quantize_fp8_rows(x.cuda())
+    vcodes, vscales = osm.quantize_fp8_cols(x.cuda())
+    torch.cuda.synchronize()
+    oc, osc = oracle.mx_quantize_rows(x)
+    np.testing.assert_array_equal(_np(scales), osc)
+    np.testing.assert_array_equal(_zero_same(_np(codes)), _zero_same(oc))
+    vc, vsc = oracle.mx_quantize_cols(x)
+    np.testing.assert_array_equal(_np(vscales), vsc)
+    np.testing.assert_array_equal(_zero_same(_np(vcodes)), _zero_same(vc))
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_quantize_rows_rotated(osm, d):
     # Rows of the outlier recipe and of the block-scale recipe, rotated.
     qa, ka, _ = inputs.attn_inputs_outliers(B=1, H=2, N=700, d=d, seed=9200 + d)

@@ -60,6 +60,31 @@ def test_gqa_forward_full(osm, shape, causal):
     assert eo <= TOL_O and el <= TOL_LSE
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 16, 4, 3000, 128), (1, 32, 8, 3000, 64)])
+def test_gqa_phase_staggered_slices(osm, shape, causal):
+    # Grids large enough for the phase-staggered kernel (more than 256 blocks
+    # of 256 rows), with groups of 4 query heads per key/value head and a
+    # ragged N; whole (b, h) slices at the ends of groups against the oracle
+    # on the slice's own key/value head.
+    B, H, Hkv, N, d = shape
+    G = H // Hkv
+    q, k, v = _case(B, H, Hkv, N, d, seed=60 + d)
+    dev = torch.device("cuda:0")
+    O, lse = osm.attention(q.to(dev), k.to(dev), v.to(dev), causal=causal)
+    torch.cuda.synchronize()
+    O, lse = O.float().cpu(), lse.cpu()
+    worst = (0.0, 0.0)
+    for b, h in ((0, 0), (0, G - 1), (B - 1, G), (B - 1, H - 1)):
+        kv = h // G
+        Oref, lref = oracle.attn_fwd(q[b:b + 1, h:h + 1], k[b:b + 1, kv:kv + 1], v[b:b + 1, kv:kv + 1],
+                                     1.0 / math.sqrt(d), causal)
+        worst = (max(worst[0], _maxabs(O[b, h], Oref[0, 0])), max(worst[1], _maxabs(lse[b, h], lref[0, 0])))
+    print(f"gqa pp B{B}H{H}Hkv{Hkv}N{N}d{d} causal={causal}: max|dO|={worst[0]:.3e} "
+          f"max|dlse|={worst[1]:.3e}", flush=True)
+    assert worst[0] <= TOL_O and worst[1] <= TOL_LSE
+
+
 def test_gqa_with_all_heads_is_attn_fwd(osm):
     q, k, v = _case(2, 16, 16, 1024, 128, seed=61)
     dev = torch.device("cuda:0")

@@ -167,13 +167,15 @@ def test_bwd_headline_shape_sampled_slices(osm):
 
 @pytest.mark.parametrize("case", [((1, 16, 2048, 64), False), ((1, 16, 2048, 64), True),
                                   ((1, 16, 2048, 128), False), ((1, 16, 2048, 128), True),
-                                  ((2, 16, 2048, 64), False), ((2, 16, 2048, 128), False)])
+                                  ((2, 16, 2048, 64), False), ((2, 16, 2048, 64), True),
+                                  ((2, 16, 2048, 128), False)])
 def test_bwd_workgroup_sizes(osm, case):
     # The launch picks 8-, 4- or 2-wave workgroups for the dK/dV and dQ
     # kernels from how many it takes to cover the chip: [1, 16, 2048, d]
     # runs 4-wave workgroups (under both masks and at both head sizes),
-    # [2, 16, 2048, d] unmasked 8-wave ones.  The whole GPU problem, four
-    # whole (b, h) slices recomputed by the oracle.
+    # [2, 16, 2048, d] 8-wave ones (d = 64 under both masks; d = 128 causal is
+    # the headline test's).  The whole GPU problem, four whole (b, h) slices
+    # recomputed by the oracle.
     (B, H, N, d), causal = case
     q, k, v, g = _case(B, H, N, d, seed=6000 + B * 7 + d)
     label = f"bwd B{B}H{H}N{N}d{d} causal={causal}"

@@ -147,3 +147,46 @@ def test_varlen_backward_against_per_sequence_oracle(osm, heads, causal):
           f"bars={[f'{2e-2 * s:.3e}' for s in scales]}", flush=True)
     assert all(np.isfinite(x).all() for x in got)
     assert all(e <= 2e-2 * s for e, s in zip(errs, scales))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,heads", [(128, (4, 4)), (64, (8, 4))])
+def test_varlen_backward_eight_wave(osm, d, heads, causal):
+    # Long packed sequences (8 of them, up to 4096) with 4 key/value heads:
+    # enough 256-row blocks that both backward kernels run their packed
+    # 8-wave workgroups (at d = 64 with two query heads per key/value head).
+    # Four sequences, of lengths 17, 2048, 3000 and 255, against the oracle's
+    # gradients of each sequence alone.
+    H, Hkv = heads
+    G = H // Hkv
+    lengths = [4096, 17, 2048, 3000, 1, 900, 4000, 255]
+    total = sum(lengths)
+    base = inputs.ATTN["attn_bf16_B2H8N1024d64" if d == 64 else "attn_bf16_B4H16N2048d128"]
+    q = inputs.attn_inputs(base, B=1, H=H, N=total, d=d, seed=960 + d)[0][0]
+    _, k, v = inputs.attn_inputs(base, B=1, H=Hkv, N=total, d=d, seed=961 + d)
+    k, v = k[0], v[0]
+    g = inputs.grad_output(q.shape, 962 + d)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, g))
+    cu_t = torch.from_numpy(cu).to(dev)
+    O, lse = osm.attention_varlen(qd, kd, vd, cu_t, max(lengths), causal=causal)
+    dq, dk, dv = osm.attention_varlen_backward(qd, kd, vd, O, lse, gd, cu_t, max(lengths),
+                                               causal=causal)
+    torch.cuda.synchronize()
+    got = [t.float().cpu().numpy() for t in (dq, dk, dv)]
+    assert all(np.isfinite(x).all() for x in got)
+    errs, scales = [0.0] * 3, [1.0] * 3
+    for b in (1, 2, 3, 7):
+        a, e = int(cu[b]), int(cu[b + 1])
+        rq, rk, rv = oracle.attn_bwd(q[None, :, a:e], k[None, :, a:e].repeat_interleave(G, dim=1),
+                                     v[None, :, a:e].repeat_interleave(G, dim=1), g[None, :, a:e],
+                                     1 / math.sqrt(d), causal)
+        rk = rk[0].reshape(Hkv, G, e - a, d).sum(axis=1)
+        rv = rv[0].reshape(Hkv, G, e - a, d).sum(axis=1)
+        for i, (x, r) in enumerate(zip(got, (rq[0], rk, rv))):
+            errs[i] = max(errs[i], float(np.max(np.abs(x[:, a:e] - r))))
+            scales[i] = max(scales[i], float(np.max(np.abs(r))))
+    print(f"varlen bwd 8-wave d={d} H{H}Hkv{Hkv} causal={causal}: errs={[f'{x:.3e}' for x in errs]} "
+          f"bars={[f'{2e-2 * s:.3e}' for s in scales]}", flush=True)
+    assert all(e <= 2e-2 * s for e, s in zip(errs, scales))

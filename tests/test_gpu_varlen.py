@@ -47,10 +47,13 @@ def _gpu_varlen(osm, q, k, v, cu, causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
-def test_varlen_against_per_sequence_oracle(osm, d, causal):
+@pytest.mark.parametrize("H", [2, 8])
+def test_varlen_against_per_sequence_oracle(osm, H, d, causal):
+    # With 2 heads the packed 64-row (4-wave) kernel runs, with 8 heads the
+    # 128-row one under the mask and the phase-staggered one without it.
     lengths = [1, 100, 0, 256, 513, 1000, 64, 65]
-    q, k, v, cu = _packed(lengths, H=2, d=d, seed=700 + d)
-    print(f"varlen d={d} causal={causal} lengths={lengths}", flush=True)
+    q, k, v, cu = _packed(lengths, H=H, d=d, seed=700 + d + H)
+    print(f"varlen H={H} d={d} causal={causal} lengths={lengths}", flush=True)
     O, lse = _gpu_varlen(osm, q, k, v, cu, causal)
     eo = el = 0.0
     for b in range(len(lengths)):

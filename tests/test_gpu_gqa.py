@@ -47,8 +47,10 @@ def _maxabs(a, b):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("shape", [(2, 8, 2, 300, 64), (1, 8, 1, 257, 128), (2, 4, 4, 100, 128)])
+@pytest.mark.parametrize("shape", [(2, 8, 2, 300, 64), (1, 8, 1, 257, 128), (2, 4, 4, 100, 128),
+                                   (1, 16, 4, 2048, 128)])
 def test_gqa_forward_full(osm, shape, causal):
+    # The last shape runs the 128-row workgroups with two key groups.
     B, H, Hkv, N, d = shape
     q, k, v = _case(B, H, Hkv, N, d, seed=40 + N + d)
     dev = torch.device("cuda:0")

@@ -6,7 +6,8 @@ one stable row softmax over fp32 [32768, 8192].  Inputs are seeded synthetic
 tensors already resident in HBM.  W untimed warm-up steps, then K timed steps
 between device synchronisations; HIP events recorded on the launch stream
 (torch's current stream) around each launch give each kernel's mean launch
-duration.  The defaults (50 warm-up, 100 timed steps, about 80 ms of GPU
+duration (timing-only events, without the system-scope fence a default
+event performs).  The defaults (50 warm-up, 100 timed steps, about 80 ms of GPU
 work) measure the sustained state: once the softmax starts alternating with
 the attention, the GPU's clock management lowers the attention kernel's
 clock for roughly the first 30 steps (its launches run up to 15% longer)
@@ -73,6 +74,18 @@ def median(xs):
     return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
 
 
+def hip_runtime():
+    """The HIP runtime this process already has loaded (torch's), never a
+    second copy of it."""
+    import ctypes
+    for name in ("libamdhip64.so.7", "libamdhip64.so"):
+        try:
+            return ctypes.CDLL(name, mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+        except OSError:
+            continue
+    raise RuntimeError("the HIP runtime is not loaded in this process")
+
+
 def device_info(torch) -> dict:
     """Name, architecture, compute-unit count and peak engine clock of the GPU
     the run used, from the HIP device attributes."""
@@ -80,16 +93,67 @@ def device_info(torch) -> dict:
     props = torch.cuda.get_device_properties(0)
     info = {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
             "max_sclk_mhz": None}
-    try:
-        hip = ctypes.CDLL("libamdhip64.so")
-        val = ctypes.c_int(0)
-        # hipDeviceAttributeClockRate (peak clock in kHz) is entry 5 of
-        # hipDeviceAttribute_t in hip_runtime_api.h.
-        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, torch.cuda.current_device()) == 0:
-            info["max_sclk_mhz"] = val.value // 1000
-    except OSError:
-        pass
+    val = ctypes.c_int(0)
+    # hipDeviceAttributeClockRate (peak clock in kHz) is entry 5 of
+    # hipDeviceAttribute_t in hip_runtime_api.h.
+    if hip_runtime().hipDeviceGetAttribute(ctypes.byref(val), 5, torch.cuda.current_device()) == 0:
+        info["max_sclk_mhz"] = val.value // 1000
     return info
+
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventCreateWithFlags flag (hip_runtime_api.h)
+TIMER = "HIP events on the launch stream, created with hipEventDisableSystemFence"
+
+
+class KernelTimer:
+    """Timing-only HIP events recorded on torch's current stream (the stream
+    the kernels are launched on).
+
+    They are created with hipEventDisableSystemFence, the flag HIP documents
+    for events that only measure time: recording a default event performs a
+    system-scope release, which writes back and invalidates the L2 inside the
+    interval the event closes and leaves the next launch a cold cache.  The
+    host orders itself with torch.cuda.synchronize(), not through these
+    events."""
+
+    def __init__(self, torch):
+        import ctypes
+        self.ct = ctypes
+        hip = hip_runtime()
+        vp = ctypes.c_void_p
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [vp, vp]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        hip.hipEventDestroy.argtypes = [vp]
+        self.hip = hip
+        self.stream = vp(torch.cuda.current_stream().cuda_stream)
+        self.events = []
+
+    def _check(self, st, what):
+        if st != 0:
+            raise RuntimeError(f"{what} returned HIP error {st}")
+
+    def event(self):
+        e = self.ct.c_void_p()
+        self._check(self.hip.hipEventCreateWithFlags(self.ct.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE),
+                    "hipEventCreateWithFlags")
+        self.events.append(e)
+        return e
+
+    def record(self, e):
+        self._check(self.hip.hipEventRecord(e, self.stream), "hipEventRecord")
+
+    def ms(self, a, b):
+        """Milliseconds between two recorded events (both complete: call after
+        a device synchronisation)."""
+        f = self.ct.c_float()
+        self._check(self.hip.hipEventElapsedTime(self.ct.byref(f), a, b), "hipEventElapsedTime")
+        return f.value
+
+    def free(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
 
 
 def measured_traffic(tag: str, sources) -> float | None:
@@ -174,15 +238,16 @@ def main() -> int:
     # softmax give each kernel's launch duration; their means over the K
     # steps are the per-kernel figures.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    timer = KernelTimer(torch)
+    ev = [[timer.event() for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e in ev:
-        e[0].record()
+        timer.record(e[0])
         osm.attention(q, k, v, causal=wa.causal, out=O, lse=lse)
-        e[1].record()
+        timer.record(e[1])
         osm.softmax(x, out=y)
-        e[2].record()
+        timer.record(e[2])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if args.copy_probe:
@@ -190,8 +255,9 @@ def main() -> int:
             cdst.copy_(csrc)
         torch.cuda.synchronize()
 
-    attn_t = [e[0].elapsed_time(e[1]) for e in ev]
-    sm_t = [e[1].elapsed_time(e[2]) for e in ev]
+    attn_t = [timer.ms(e[0], e[1]) for e in ev]
+    sm_t = [timer.ms(e[1], e[2]) for e in ev]
+    timer.free()
     attn_ms, sm_ms = sum(attn_t) / K, sum(sm_t) / K
     attn_tflops = wa.flops / (attn_ms * 1e-3) / 1e12
     sm_gbs = ws.bytes / (sm_ms * 1e-3) / 1e9
@@ -224,7 +290,8 @@ def main() -> int:
                      "kernel": "attn_fwd_bf16_pp_kernel", "kernel_ms": round(attn_ms, 4),
                      "kernel_ms_median": round(median(attn_t), 4),
                      "kernel_ms_min": round(min(attn_t), 4),
-                     "flops_per_launch": wa.flops, "algorithmic_bytes": attn_bytes},
+                     "flops_per_launch": wa.flops, "algorithmic_bytes": attn_bytes,
+                     "timer": TIMER},
         "softmax": {"value": round(sm_gbs, 1), "unit": "GB/s", "kernel_ms": round(sm_ms, 4),
                     "kernel_ms_median": round(median(sm_t), 4),
                     "kernel_ms_min": round(min(sm_t), 4)},
@@ -270,15 +337,17 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10, warm_ms=15.
             for _ in range(warm):
                 fn()
             torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps)]
+        timer = KernelTimer(torch)
+        ev = [(timer.event(), timer.event()) for _ in range(reps)]
         torch.cuda.synchronize()
         for a, b in ev:
-            a.record()
+            timer.record(a)
             fn()
-            b.record()
+            timer.record(b)
         torch.cuda.synchronize()
-        return [a.elapsed_time(b) for a, b in ev]
+        t = [timer.ms(a, b) for a, b in ev]
+        timer.free()
+        return t
 
     def per_launch_ms(fn):
         t = launch_times(fn)
@@ -409,13 +478,16 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10, warm_ms=15.
         for _ in range(5):
             fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        timer = KernelTimer(torch)
+        e0, e1 = timer.event(), timer.event()
+        timer.record(e0)
         for _ in range(n):
             fn()
-        e1.record()
+        timer.record(e1)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
+        t = timer.ms(e0, e1) / n
+        timer.free()
+        return t
     t_rows = back_to_back_ms(lambda: osm.quantize_fp8_rows(q4, signs))
     t_cols = back_to_back_ms(lambda: osm.quantize_fp8_cols(v4))
     del q4, v4

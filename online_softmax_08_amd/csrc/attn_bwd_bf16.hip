@@ -236,7 +236,16 @@ attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     using TV = Tile<D, BK>;
     constexpr int LPW = (TQ::INST + NW - 1) / NW;  // loads per wave per tile
     constexpr int VPW = (TV::INST + NW - 1) / NW;  // loads per wave of the V block
-    __shared__ __attribute__((aligned(1024))) char vblk[TV::BYTES];
+    // The V block of 8-wave workgroups sits in dynamic LDS (the launch passes
+    // its size), the smaller workgroups' in a static array.  The compiler
+    // schedules for the static footprint it sees: with all 137 KiB static at
+    // D = 128 (one workgroup per CU) it schedules the 8-wave kernel's loop
+    // looser and the call runs 2-3% slower; the 4-wave kernel, which does run
+    // one workgroup per CU with more than 256 registers, loses 3% the other
+    // way round.  Same instructions, bitwise-equal gradients.
+    extern __shared__ __attribute__((aligned(1024))) char vdyn[];
+    __shared__ __attribute__((aligned(1024))) char vsta[NW == 8 ? 16 : TV::BYTES];
+    char* const vblk = NW == 8 ? vdyn : vsta;
     __shared__ __attribute__((aligned(1024))) char qb0[TQ::BYTES];
     __shared__ __attribute__((aligned(1024))) char qb1[TQ::BYTES];
     __shared__ __attribute__((aligned(1024))) char ob0[TQ::BYTES];
@@ -692,6 +701,10 @@ attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 constexpr long long kCUs = 256;
 
 // N is the sequence length, or with cu (packed sequences) the longest one.
+// Dynamic LDS of attn_bwd_dkdv_kernel<D, NW>: the V block for 8 waves.
+template <int D, int NW>
+constexpr unsigned dkdv_dynamic_lds() { return NW == 8 ? (unsigned)Tile<D, NW * 32>::BYTES : 0u; }
+
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_dkdv(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* g,
                        const float* Lc, const float* Dl, void* dK, void* dV, int B, int H,
@@ -701,7 +714,8 @@ hipError_t launch_dkdv(const __bf16* q, const __bf16* k, const __bf16* v, const 
     auto go = [&](auto nwc) {
         constexpr int NW = decltype(nwc)::value;
         const int nkb = (N + NW * 32 - 1) / (NW * 32);
-        attn_bwd_dkdv_kernel<D, NW, CAUSAL, VARLEN><<<dim3((unsigned)(nkb * BHkv)), dim3(NW * 64), 0, stream>>>(
+        attn_bwd_dkdv_kernel<D, NW, CAUSAL, VARLEN><<<dim3((unsigned)(nkb * BHkv)), dim3(NW * 64),
+                                                      dkdv_dynamic_lds<D, NW>(), stream>>>(
             q, k, v, g, Lc, Dl, static_cast<__bf16*>(dK), static_cast<__bf16*>(dV), N, BHkv, H, Hkv,
             scale, cu, total, nullptr, 1);
         return hipGetLastError();
@@ -784,7 +798,8 @@ hipError_t launch_bwd_split(const void* Q, const void* K, const void* V, const v
     const int nb = (N + 255) / 256;
     float* const pkv = part;
     float* const pq = part + (size_t)2 * nsplit * BHkv * N * D;
-    attn_bwd_dkdv_kernel<D, 8, CAUSAL, false, true><<<dim3((unsigned)(nb * nsplit * BHkv)), dim3(512), 0, stream>>>(
+    attn_bwd_dkdv_kernel<D, 8, CAUSAL, false, true><<<dim3((unsigned)(nb * nsplit * BHkv)), dim3(512),
+                                                      dkdv_dynamic_lds<D, 8>(), stream>>>(
         q, k, v, g, Lc, Dl, nullptr, nullptr, N, BHkv, H, Hkv, scale, nullptr, 0, pkv, nsplit);
     if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     attn_bwd_dq_kernel<D, 8, CAUSAL, false, true><<<dim3((unsigned)(nb * nsplit * BH)), dim3(512), 0, stream>>>(

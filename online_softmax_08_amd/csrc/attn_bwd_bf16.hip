@@ -11,8 +11,12 @@
 //   dQ = scale dS K,  dK = scale dS^T Q
 // (D_i equals sum_j P_ij dP_ij because O_i = sum_j P_ij V_j).
 //
-// gfx950 design -- three kernels, no atomics, bitwise deterministic:
-//  * attn_bwd_delta_kernel: D and L log2(e) per row (HBM bound, reads O, dO).
+// gfx950 design -- two kernels, no atomics, bitwise deterministic:
+//  * row statistics D and L log2(e): formed by the dQ kernel (below), which
+//    holds each row's dO in VGPRs anyway and loads its O row next to it; it
+//    runs first and stores them for the dK/dV kernel.  The split backward
+//    takes them from attn_bwd_delta_kernel (HBM bound, reads O, dO), since
+//    its dQ workgroups cover a query block several times.
 //  * attn_bwd_dkdv_kernel: one workgroup per (batch*key/value head, 256 keys),
 //    summing over the query heads that share the key/value head, a wave
 //    per 32 keys (two per SIMD), the keys' K rows held in VGPRs and their V
@@ -516,7 +520,8 @@ template <int D, int NW, bool CAUSAL, bool VARLEN, bool SPLIT = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                   const float* __restrict__ Lc, const float* __restrict__ Dl,
+                   const __bf16* __restrict__ O, const float* __restrict__ lse,
+                   float* __restrict__ Lc, float* __restrict__ Dl,
                    __bf16* __restrict__ dQ, int Nmax, int BH, int nqb, int H, int Hkv,
                    float scale, const int* __restrict__ cu, int total,
                    float* __restrict__ part, int nsplit)
@@ -565,8 +570,32 @@ attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             gf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0));
         }
     }
-    const float lq = q < N ? Lc[qrow0 + q] : 0.f;
-    const float dq = q < N ? Dl[qrow0 + q] : 0.f;
+    // Row statistics of this lane's query.  With SPLIT they come from
+    // attn_bwd_delta_kernel.  Otherwise this kernel forms them (it runs
+    // before the dK/dV kernel, which reads them): D = sum_t dO_t O_t in fp32
+    // over the lane's 64 elements of the row (chunks 2 kk + h, as Q and dO
+    // above) plus the other lane half's, and L log2(e) from lse.
+    float lq, dq;
+    if constexpr (SPLIT) {
+        lq = q < N ? Lc[qrow0 + q] : 0.f;
+        dq = q < N ? Dl[qrow0 + q] : 0.f;
+    } else {
+        const __amdgpu_buffer_rsrc_t ors = make_rsrc(O + base, slice_b);
+        float sd = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const bf16x8 o = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                ors, (uint32_t)(q * D + kk * 16 + 8 * h) * 2, 0, 0));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sd = fmaf((float)o[e], (float)gf[kk][e], sd);
+        }
+        dq = combine_xor32(sd, SumOp());  // rows past N: zeros, never stored
+        lq = q < N ? lse[qrow0 + q] * kLog2e : 0.f;
+        if (h == 0 && q < N) {
+            Lc[qrow0 + q] = lq;
+            Dl[qrow0 + q] = dq;
+        }
+    }
     f32x16 acc[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
@@ -727,16 +756,17 @@ hipError_t launch_dkdv(const __bf16* q, const __bf16* k, const __bf16* v, const 
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_dq(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* g,
-                     const float* Lc, const float* Dl, void* dQ, int B, int H, int Hkv, int N,
-                     float scale, const int* cu, int total, hipStream_t stream)
+                     const __bf16* o, const float* lse, float* Lc, float* Dl, void* dQ, int B,
+                     int H, int Hkv, int N, float scale, const int* cu, int total,
+                     hipStream_t stream)
 {
     const int BH = B * H;
     auto go = [&](auto nwc) {
         constexpr int NW = decltype(nwc)::value;
         const int nqb = (N + NW * 32 - 1) / (NW * 32);
         attn_bwd_dq_kernel<D, NW, CAUSAL, VARLEN><<<dim3((unsigned)(nqb * BH)), dim3(NW * 64), 0, stream>>>(
-            q, k, v, g, Lc, Dl, static_cast<__bf16*>(dQ), N, BH, nqb, H, Hkv, scale, cu, total,
-            nullptr, 1);
+            q, k, v, g, o, lse, Lc, Dl, static_cast<__bf16*>(dQ), N, BH, nqb, H, Hkv, scale, cu,
+            total, nullptr, 1);
         return hipGetLastError();
     };
     if ((long long)((N + 255) / 256) * BH >= kCUs) return go(std::integral_constant<int, 8>{});
@@ -750,26 +780,19 @@ hipError_t launch_bwd(const void* Q, const void* K, const void* V, const void* O
                       float scale, float* Dl, float* Lc, const int* cu, int total,
                       hipStream_t stream)
 {
-    const int BH = B * H;
     const __bf16* q = static_cast<const __bf16*>(Q);
     const __bf16* k = static_cast<const __bf16*>(K);
     const __bf16* v = static_cast<const __bf16*>(V);
     const __bf16* g = static_cast<const __bf16*>(dO);
-    // Row statistics for every query row: B H N dense rows, or H total packed.
-    const long long rows = VARLEN ? (long long)H * total : (long long)BH * N;
-    {
-        constexpr int RPB = 256 / (D / 8);
-        const long long need = (rows + RPB - 1) / RPB;
-        attn_bwd_delta_kernel<D><<<dim3((unsigned)(need < 65536 ? need : 65536)), dim3(256), 0, stream>>>(
-            static_cast<const __bf16*>(O), g, lse, Dl, Lc, rows);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (const hipError_t e = launch_dkdv<D, CAUSAL, VARLEN>(q, k, v, g, Lc, Dl, dK, dV, B, H, Hkv, N,
-                                                            scale, cu, total, stream);
+    // dQ first: its workgroups also form the row statistics (D and L log2 e
+    // of every query row of a sequence), which the dK/dV kernel reads.
+    if (const hipError_t e = launch_dq<D, CAUSAL, VARLEN>(q, k, v, g, static_cast<const __bf16*>(O),
+                                                          lse, Lc, Dl, dQ, B, H, Hkv, N, scale, cu,
+                                                          total, stream);
         e != hipSuccess)
         return e;
-    return launch_dq<D, CAUSAL, VARLEN>(q, k, v, g, Lc, Dl, dQ, B, H, Hkv, N, scale, cu, total, stream);
+    return launch_dkdv<D, CAUSAL, VARLEN>(q, k, v, g, Lc, Dl, dK, dV, B, H, Hkv, N, scale, cu, total,
+                                          stream);
 }
 
 // Split backward (dense): the dK/dV workgroups divide their query tiles, the
@@ -803,7 +826,7 @@ hipError_t launch_bwd_split(const void* Q, const void* K, const void* V, const v
         q, k, v, g, Lc, Dl, nullptr, nullptr, N, BHkv, H, Hkv, scale, nullptr, 0, pkv, nsplit);
     if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     attn_bwd_dq_kernel<D, 8, CAUSAL, false, true><<<dim3((unsigned)(nb * nsplit * BH)), dim3(512), 0, stream>>>(
-        q, k, v, g, Lc, Dl, nullptr, N, BH, nb, H, Hkv, scale, nullptr, 0, pq, nsplit);
+        q, k, v, g, nullptr, nullptr, Lc, Dl, nullptr, N, BH, nb, H, Hkv, scale, nullptr, 0, pq, nsplit);
     if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     const long long kv8 = (long long)BHkv * N * D / 8, q8 = rows * D / 8;
     const long long kvs = (long long)BHkv * N * D, qs = rows * D;

@@ -281,7 +281,7 @@ int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float*
  *                        would leave compute units idle)
  *   *nsplit_out        : the count attn_fwd_splitkv will use for nsplit
  *   *workspace_bytes   : device bytes attn_fwd_splitkv needs for it:
- *                        nsplit * B * H * N * (d + 1) * 4, or 0 when the
+ *                        nsplit * B * H * N * (2 * d + 4), or 0 when the
  *                        count is 1 (then the call is exactly attn_fwd)
  * Host only; touches no device.  Returns OSM_ERR_NULL for NULL out pointers,
  * OSM_ERR_SIZE, OSM_ERR_HEAD_DIM or OSM_ERR_SPLITS for bad sizes.
@@ -306,9 +306,10 @@ int attn_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int nsplit,
  *                     return are unspecified.  Calls that share a workspace
  *                     must be ordered on one stream.
  * O and lse satisfy attn_fwd's tolerance against the exact result; they are
- * not bitwise equal to attn_fwd's (the partials are merged in fp32).
- * Returns an osm_status (OSM_ERR_WORKSPACE if workspace_bytes is too small,
- * OSM_ERR_SIZE if N * d * 4 does not fit in 32 bits).
+ * not bitwise equal to attn_fwd's (each range's normalised output is kept in
+ * bf16 in the workspace, its logsumexp in fp32, and the merge is computed in
+ * fp32).  Returns an osm_status (OSM_ERR_WORKSPACE if workspace_bytes is too
+ * small, OSM_ERR_SIZE if N * d * 2 does not fit in 32 bits).
  */
 int attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* lse,
                      int B, int H, int Hkv, int N, int d, float scale, int causal, int nsplit,

@@ -117,11 +117,11 @@ int validate_attn(const void* Q, const void* K, const void* V, const void* O, co
     return OSM_OK;
 }
 
-// Bytes of the split-KV workspace: fp32 partial outputs [nsplit][bh][N][d],
+// Bytes of the split-KV workspace: bf16 partial outputs [nsplit][bh][N][d],
 // then the fp32 partial logsumexps [nsplit][bh][N].
 size_t splitkv_workspace(int nsplit, long long bh, int N, int d)
 {
-    return (size_t)nsplit * bh * N * ((size_t)d + 1) * sizeof(float);
+    return (size_t)nsplit * bh * N * ((size_t)d * 2 + sizeof(float));
 }
 
 }  // namespace
@@ -336,8 +336,8 @@ int attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float
     }
     // The partial pass launches bh * ceil(N / 256) * nsplit workgroups of 512
     // work-items, and a dispatch counts at most 2^32 - 1 work-items; offsets
-    // into one fp32 partial slice are 32-bit.
-    if (bh * ((N + 255) / 256) * nsplit * 512 > UINT32_MAX || (long long)N * d * 4 > UINT32_MAX)
+    // into one bf16 partial slice are 32-bit.
+    if (bh * ((N + 255) / 256) * nsplit * 512 > UINT32_MAX || (long long)N * d * 2 > UINT32_MAX)
         return OSM_ERR_SIZE;
     const size_t need = splitkv_workspace(nsplit, bh, N, d);
     if (!workspace) return OSM_ERR_NULL;
@@ -350,8 +350,8 @@ int attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float
         overlaps(workspace, need, lse, lbytes))
         return OSM_ERR_ALIAS;
     if ((st = check_device()) != OSM_OK) return st;
-    float* opart = static_cast<float*>(workspace);
-    float* lpart = opart + (size_t)nsplit * bh * N * d;
+    __bf16* opart = static_cast<__bf16*>(workspace);
+    float* lpart = reinterpret_cast<float*>(opart + (size_t)nsplit * bh * N * d);
     return finish(osm::launch_attn_fwd_bf16_split(Q, K, V, O, lse, B, H, Hkv, N, d, scale,
                                                   causal != 0, nsplit, opart, lpart,
                                                   static_cast<hipStream_t>(stream)));

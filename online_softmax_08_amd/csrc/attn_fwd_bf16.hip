@@ -583,8 +583,8 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 // and lse = M + ln sum_s e^(lse_s - M).  Partials with lse_s = -inf are empty
 // and skipped without reading their O_s; a row with no non-empty partial
 // gets O = 0 and lse = -inf.  Partial s of row `row` sits at s rows + row.
-template <int D>
-__device__ __forceinline__ void merge_row(const float* __restrict__ opart,
+template <int D, class PT>
+__device__ __forceinline__ void merge_row(const PT* __restrict__ opart,
                                           const float* __restrict__ lpart, __bf16* __restrict__ O,
                                           float* __restrict__ lse, int S, long long rows,
                                           long long row, int c4)
@@ -595,7 +595,11 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ opart,
         const size_t pr = (size_t)s * rows + row;
         const float ls = lpart[pr];
         if (ls == kNegInf) continue;
-        const f32x4 o = *reinterpret_cast<const f32x4*>(opart + pr * D + 4 * c4);
+        f32x4 o;
+        if constexpr (std::is_same_v<PT, float>)
+            o = *reinterpret_cast<const f32x4*>(opart + pr * D + 4 * c4);
+        else
+            o = __builtin_convertvector(*reinterpret_cast<const bf16x4*>(opart + pr * D + 4 * c4), f32x4);
         if (ls > M) {
             const float a = exp2_hw((M - ls) * kLog2e);  // M = -inf gives 0
             acc *= a;
@@ -614,16 +618,17 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ opart,
 
 // With SPLIT (dense only) the workgroup computes one of nsplit contiguous
 // ranges of its query block's key tiles and writes the normalised partial
-// output in fp32 and the partial logsumexp (-inf for a row that sees no key
-// of the range) to opart [nsplit][BH][N][D] and lpart [nsplit][BH][N];
-// attn_combine_kernel merges them.
+// output in bf16 (through LDS as whole rows, like O) and the partial
+// logsumexp in fp32 (-inf for a row that sees no key of the range) to opart
+// [nsplit][BH][N][D] and lpart [nsplit][BH][N]; attn_combine_kernel merges
+// them in fp32.
 template <int D, bool CAUSAL, bool VARLEN, bool SPLIT = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                         const __bf16* __restrict__ V, __bf16* __restrict__ O,
                         float* __restrict__ lse, int Nmax, int BH, int nqt, float scale,
                         const int* __restrict__ cu, int H, int Hkv, int total,
-                        float* __restrict__ opart, float* __restrict__ lpart, int nsplit)
+                        __bf16* __restrict__ opart, float* __restrict__ lpart, int nsplit)
 {
     static_assert(!(SPLIT && VARLEN), "split-KV runs on dense tensors");
     // Keys per step: 128 at D = 64 (its 64-key steps are half as long as at
@@ -991,23 +996,19 @@ attn_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 
     const float l_tot = combine_xor32(l, SumOp());
     if constexpr (SPLIT) {
-        // Partial of this key range: O_s = acc / l in fp32 straight from the
-        // registers (lane (j, h): row qw0 + j, columns 32 dt + 8 g + 4 h ..
-        // + 3), lse_s = m scale + ln l, or O_s = 0 and -inf for a row that saw
-        // no key of the range.
+        // Partial of this key range: O_s = acc / l rounded to bf16 and
+        // stored as whole rows through LDS, lse_s = m scale + ln l, or O_s = 0
+        // and -inf for a row that saw no key of the range.  bf16 partials
+        // halve the bytes the partial pass writes and the merge reads; fp32
+        // ones measured 6-17% slower for the whole call ([1, 2, 8192, 128],
+        // [1, 4, 4096, 128], [1, 1, 16384, 128], both masks), with the same
+        // lse and an output within one bf16 rounding.
         const size_t pslice = (size_t)split * BH + bh;
-        const __amdgpu_buffer_rsrc_t prs = make_rsrc(opart + pslice * N * D, (uint32_t)N * D * 4);
+        const __amdgpu_buffer_rsrc_t prs = make_rsrc(opart + pslice * N * D, (uint32_t)N * D * 2);
         const __amdgpu_buffer_rsrc_t plrs = make_rsrc(lpart + pslice * N, (uint32_t)N * 4);
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 o4 = {acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv,
-                                  acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv};
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), prs,
-                                                       (uint32_t)(qrow * D + dt * 32 + 8 * g + 4 * h) * 4, 0, 0);
-            }
+        __syncthreads();  // every wave is done with the tile buffers
+        store_tile_rows<D>(acc, inv, out_stage<D>(wave, kbuf0, kbuf1, vbuf0, vbuf1), prs, qw0, lane);
         if (h == 0) {
             const float ls = l_tot > 0.f ? m * scale + logf(l_tot) : kNegInf;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ls), plrs, (uint32_t)qrow * 4, 0, 0);
@@ -1085,9 +1086,9 @@ hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float*
 
 // Merge of split partials (attn_combine): merge_row for every row, D / 4
 // lanes per row, rows walked grid-stride.
-template <int D>
+template <int D, class PT>
 __global__ void __launch_bounds__(256)
-attn_combine_kernel(const float* __restrict__ opart, const float* __restrict__ lpart,
+attn_combine_kernel(const PT* __restrict__ opart, const float* __restrict__ lpart,
                     __bf16* __restrict__ O, float* __restrict__ lse, int S, long long rows)
 {
     constexpr int LPR = D / 4;         // lanes per row
@@ -1095,22 +1096,23 @@ attn_combine_kernel(const float* __restrict__ opart, const float* __restrict__ l
     const int c4 = threadIdx.x % LPR;  // column group of this lane
     for (long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR; row < rows;
          row += (long long)gridDim.x * RPB)
-        merge_row<D>(opart, lpart, O, lse, S, rows, row, c4);
+        merge_row<D, PT>(opart, lpart, O, lse, S, rows, row, c4);
 }
 
 // Split-KV forward: 8-wave workgroups (256 query rows) over nsplit key ranges
 // each, then the merge.
 template <int D, bool CAUSAL>
 hipError_t launch_split(const void* Q, const void* K, const void* V, void* O, float* lse, int BH,
-                        int N, float scale, int nsplit, float* opart, float* lpart, int H, int Hkv,
+                        int N, float scale, int nsplit, __bf16* opart, float* lpart, int H, int Hkv,
                         hipStream_t stream)
 {
     // Partial pass: the phase-staggered kernel over (256-row query block,
     // key range) workgroups, longest blocks first under the mask; then the
     // merge over all rows.  (Merging each block in the last of its
     // workgroups to finish, behind a per-block counter, was measured 1.7-6x
-    // slower: one workgroup's serial loads cannot move a block's nsplit fp32
-    // partials, ~1 MiB at d = 128, in the time the whole-chip merge takes.)
+    // slower, with fp32 partials: one workgroup's serial loads cannot move a
+    // block's nsplit partials, ~1 MiB at d = 128, in the time the whole-chip
+    // merge takes.)
     constexpr int BR = 256;
     const int nqt = (N + BR - 1) / BR;
     attn_fwd_bf16_pp_kernel<D, CAUSAL, false, true>
@@ -1120,7 +1122,12 @@ hipError_t launch_split(const void* Q, const void* K, const void* V, void* O, fl
             opart, lpart, nsplit);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_attn_combine(opart, lpart, O, lse, nsplit, (long long)BH * N, D, stream);
+    const long long rows = (long long)BH * N;
+    const int rpb = 256 / (D / 4);
+    const long long need = (rows + rpb - 1) / rpb;
+    attn_combine_kernel<D, __bf16><<<dim3((unsigned)(need < 65536 ? need : 65536)), dim3(256), 0, stream>>>(
+        opart, lpart, static_cast<__bf16*>(O), lse, nsplit, rows);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -1133,10 +1140,10 @@ hipError_t launch_attn_combine(const float* opart, const float* lpart, void* O, 
     const long long need = (rows + rpb - 1) / rpb;
     const dim3 grid((unsigned)(need < 65536 ? need : 65536)), block(256);
     if (d == 64)
-        attn_combine_kernel<64><<<grid, block, 0, stream>>>(opart, lpart, static_cast<__bf16*>(O),
+        attn_combine_kernel<64, float><<<grid, block, 0, stream>>>(opart, lpart, static_cast<__bf16*>(O),
                                                             lse, S, rows);
     else
-        attn_combine_kernel<128><<<grid, block, 0, stream>>>(opart, lpart, static_cast<__bf16*>(O),
+        attn_combine_kernel<128, float><<<grid, block, 0, stream>>>(opart, lpart, static_cast<__bf16*>(O),
                                                              lse, S, rows);
     return hipGetLastError();
 }
@@ -1149,7 +1156,7 @@ int attn_splitkv_auto(int BH, int N, int d, bool causal)
     // 2048 waves, twice that under the causal mask (its query blocks differ
     // in length, and more, shorter ranges even them out), with at least 512
     // keys per range.  Rows of 2048 keys or fewer are not split: there the
-    // fp32 partials cost as much HBM time as the occupancy gains (and the
+    // partials cost as much HBM time as the occupancy gains (and the
     // single pass already splits the key loop over two wave groups).
     (void)d;
     const long long rows = (long long)BH * N;
@@ -1163,7 +1170,7 @@ int attn_splitkv_auto(int BH, int N, int d, bool causal)
 
 hipError_t launch_attn_fwd_bf16_split(const void* Q, const void* K, const void* V, void* O,
                                       float* lse, int B, int H, int Hkv, int N, int d, float scale,
-                                      bool causal, int nsplit, float* opart, float* lpart,
+                                      bool causal, int nsplit, __bf16* opart, float* lpart,
                                       hipStream_t stream)
 {
     const int BH = B * H;

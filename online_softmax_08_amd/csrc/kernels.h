@@ -24,12 +24,12 @@ hipError_t launch_attn_fwd_bf16_varlen(const void* Q, const void* K, const void*
                                        float* lse, const int* cu, int B, int H, int Hkv, int total,
                                        int max_seqlen, int d, float scale, bool causal,
                                        hipStream_t stream);
-// Split-KV forward.  opart: fp32 [nsplit][B*H][N][d], lpart: fp32
+// Split-KV forward.  opart: bf16 [nsplit][B*H][N][d], lpart: fp32
 // [nsplit][B*H][N] (workspace); 1 <= nsplit <= kMaxSplits.
 constexpr int kMaxSplits = 64;
 hipError_t launch_attn_fwd_bf16_split(const void* Q, const void* K, const void* V, void* O,
                                       float* lse, int B, int H, int Hkv, int N, int d, float scale,
-                                      bool causal, int nsplit, float* opart, float* lpart,
+                                      bool causal, int nsplit, __bf16* opart, float* lpart,
                                       hipStream_t stream);
 // The number of key ranges the split-KV forward picks when asked to choose.
 int attn_splitkv_auto(int BH, int N, int d, bool causal);

@@ -135,7 +135,7 @@ def test_splitkv_plan(abi):
     # Explicit counts are kept; the workspace holds nsplit fp32 partial
     # outputs and logsumexps per row, none when the count is 1.
     def ws(ns, bh, N, d):  # fp32 partial outputs and logsumexps
-        return ns * bh * N * (d + 1) * 4
+        return ns * bh * N * (2 * d + 4)
     assert abi.attn_fwd_splitkv_plan(2, 8, 1024, 64, False, 1) == (1, 0)
     assert abi.attn_fwd_splitkv_plan(2, 8, 1024, 64, False, 3) == (3, ws(3, 16, 1024, 64))
     assert abi.attn_fwd_splitkv_plan(1, 2, 777, 128, True, 64) == (64, ws(64, 2, 777, 128))
@@ -192,9 +192,9 @@ def test_splitkv_validation(abi):
     assert _splitkv_status(abi, ws=6 * FAKE + 4) == abi.OSM_ERR_ALIGN
     assert _splitkv_status(abi, ws=4 * FAKE) == abi.OSM_ERR_ALIAS          # workspace is O
     assert _splitkv_status(abi, ws=FAKE - 64) == abi.OSM_ERR_ALIAS         # runs into Q
-    # N * d * 4 bytes of one fp32 partial slice must fit in 32 bits.
+    # N * d * 2 bytes of one bf16 partial slice must fit in 32 bits.
     far = {n: (i + 1) << 40 for i, n in enumerate(("Q", "K", "V", "O", "lse"))}
-    assert _splitkv_status(abi, N=1 << 23, d=128, ws=6 << 40, ws_bytes=1 << 45,
+    assert _splitkv_status(abi, N=1 << 24, d=128, ws=6 << 40, ws_bytes=1 << 45,
                            **far) == abi.OSM_ERR_SIZE
     # Empty problems are a no-op with any pointers.
     abi.attn_fwd_splitkv(0, 0, 0, 0, 0, 0, 4, 4, 128, 64, 0.125, 1, 4, 0, 0)

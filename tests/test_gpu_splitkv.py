@@ -111,6 +111,22 @@ def test_splitkv_long_rows_sampled(osm, shape, causal):
     assert eo <= TOL_O and el <= TOL_LSE
 
 
+@pytest.mark.parametrize("shape", [(1, 4, 2048, 64), (1, 8, 2048, 128)])
+def test_splitkv_short_causal_rows_full(osm, shape):
+    # Rows of 2048 keys under the mask on a small grid: the library splits
+    # them into 4 ranges (bf16 partials); every element against the oracle.
+    B, H, N, d = shape
+    assert osm.attn_fwd_splitkv_plan(B, H, N, d, True, 0)[0] == 4
+    q, k, v = _inputs(B, H, N, d, seed=3000 + H + d)
+    print(f"splitkv B{B}H{H}N{N}d{d} causal=1 auto nsplit=4", flush=True)
+    O, lse = _gpu_split(osm, q, k, v, True, 0)
+    Oref, lref = oracle.attn_fwd(q, k, v, 1.0 / math.sqrt(d), True)
+    eo, el = _maxabs(O, Oref), _maxabs(lse, lref)
+    print(f"  max|dO|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse))
+    assert eo <= TOL_O and el <= TOL_LSE
+
+
 def test_splitkv_deterministic_and_one_split_is_attn_fwd(osm):
     q, k, v = _inputs(1, 2, 3000, 128, seed=77)
     dev = torch.device("cuda:0")

@@ -16,8 +16,10 @@
 // S^T = K Q^T is formed so that each lane owns one query row (lane % 32) and
 // 16 of the tile's keys, which makes the row max/sum one in-lane pass plus one
 // exchange with lane ^ 32.  The probabilities then feed O^T += V^T P^T
-// straight from the accumulator registers.  This kernel favours simplicity
-// over speed: single-buffered LDS tiles with two barriers per tile.
+// straight from the accumulator registers.  Tiles are single-buffered in LDS
+// with two barriers per tile; the next tile's K and V rows are fetched into
+// registers (16-byte loads) while the current one is computed, so global
+// latency overlaps the products.
 
 #include "device_common.h"
 #include "kernels.h"
@@ -40,7 +42,7 @@ attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 {
     constexpr int BC = F32_BC, KP = D + 1;
     __shared__ float Ks[BC * KP];
-    __shared__ float Vs[BC * D];
+    __shared__ __attribute__((aligned(16))) float Vs[BC * D];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, h = lane >> 5;
@@ -64,16 +66,34 @@ attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 
     const int kv_end = CAUSAL ? min(N, q0 + F32_BR) : N;
     const int ntiles = (kv_end + BC - 1) / BC;
+    // Thread tid fetches 4-float pieces tid + 256 u (u < NF) of the tile's
+    // K and V rows: piece p is row 4 p / D, columns 4 p % D .. + 3 (zero
+    // for rows past N).
+    constexpr int NF = BC * D / 4 / 256;
+    static_assert(NF * 256 * 4 == BC * D, "whole pieces per thread");
+    f32x4 kreg[NF], vreg[NF];
+    auto fetch = [&](int kt) {
+#pragma unroll
+        for (int u = 0; u < NF; ++u) {
+            const int e = 4 * (tid + 256 * u), r = e / D, col = e - r * D, key = kt * BC + r;
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            kreg[u] = key < N ? *reinterpret_cast<const f32x4*>(K + base + (size_t)key * D + col) : z;
+            vreg[u] = key < N ? *reinterpret_cast<const f32x4*>(V + base + (size_t)key * D + col) : z;
+        }
+    };
+    if (ntiles > 0) fetch(0);
     for (int kt = 0; kt < ntiles; ++kt) {
         const int kv0 = kt * BC;
         __syncthreads();  // the previous tile is no longer read
-        for (int e = tid; e < BC * D; e += 256) {
-            const int r = e / D, col = e - r * D, key = kv0 + r;
-            const bool in = key < N;
-            Ks[r * KP + col] = in ? K[base + (size_t)key * D + col] : 0.f;
-            Vs[r * D + col] = in ? V[base + (size_t)key * D + col] : 0.f;
+#pragma unroll
+        for (int u = 0; u < NF; ++u) {
+            const int e = 4 * (tid + 256 * u), r = e / D, col = e - r * D;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) Ks[r * KP + col + x] = kreg[u][x];  // odd pitch: 4-byte stores
+            *reinterpret_cast<f32x4*>(&Vs[r * D + col]) = vreg[u];
         }
         __syncthreads();
+        if (kt + 1 < ntiles) fetch(kt + 1);      // lands while this tile is computed
         if (CAUSAL && kv0 > qw0 + 31) continue;  // every key of the tile is in this wave's future
 
         f32x16 s = f32x16{};

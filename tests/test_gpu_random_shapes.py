@@ -8,8 +8,8 @@ seed (small grids with lengths log-uniform from 1, and larger grids of 12 to
 32 heads with lengths from 1500, where the 8-wave kernels run), and compares every output
 element with the oracle (key/value heads repeated for grouped queries, the
 gradient of a repeated head summed over its copies).  Bars as for the
-hand-picked cases: bf16 forward 2e-2 on O and 1e-3 on lse; backward
-2e-2 * max(1, max|ref|) per gradient tensor.
+hand-picked cases: bf16 forward 2e-2 on O and 1e-3 on lse, fp32 forward 1e-5;
+backward 2e-2 * max(1, max|ref|) per gradient tensor.
 """
 from __future__ import annotations
 
@@ -83,6 +83,23 @@ def test_random_forward_full(osm, seed):
     print(f"  max|dO|={eo:.3e} max|dlse|={el:.3e}", flush=True)
     assert torch.isfinite(O.float()).all() and torch.isfinite(lse).all()
     assert eo <= TOL_O and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_forward_f32_full(osm, seed):
+    # fp32 inputs (the fp32 matrix-core kernel), lengths to 1500, at the fp32
+    # bar of 1e-5 on O and lse.
+    B, H, _, N, d, causal = _draw(8100 + seed, 1500, bh_max=4)
+    print(f"random fp32 forward seed={seed}: B{B} H{H} N{N} d{d} causal={causal}", flush=True)
+    base = inputs.ATTN["attn_f32_B1H1N128d64"]
+    q, k, v = inputs.attn_inputs(base, B=B, H=H, N=N, d=d, seed=8200 + seed)
+    dev = torch.device("cuda:0")
+    O, lse = osm.attention(q.to(dev), k.to(dev), v.to(dev), causal=causal)
+    torch.cuda.synchronize()
+    Oref, lref = oracle.attn_fwd(q, k, v, 1.0 / math.sqrt(d), causal)
+    eo, el = _maxabs(O.cpu(), Oref), _maxabs(lse.cpu(), lref)
+    print(f"  max|dO|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    assert eo <= 1e-5 and el <= 1e-5
 
 
 @pytest.mark.parametrize("seed", range(20))

@@ -26,7 +26,8 @@ Prints one JSON line:
   supplementary     measured before the warm-up (see main): every other attention
                     workload (fp32 [1,1,128,64], bf16 [2,8,1024,64],
                     [4,16,2048,128], causal [1,32,8192,128]) with mean,
-                    median and fastest launch, the headline shape without
+                    median and fastest launch, the fp32 kernel on the headline
+                    shape (both masks), the headline shape without
                     the mask, a plain device copy of the softmax input as the
                     practical HBM ceiling, the split-KV forward beside the
                     single pass on long rows / few heads, packed
@@ -375,6 +376,24 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10, warm_ms=15.
                          "ms_mean": round(sum(t) / len(t), 4)}
         del qc, kc, vc, Oc, lc
 
+    # The fp32 kernel on an input large enough to fill the chip (the fp32
+    # workload above is one workgroup and launch-bound): the headline shape's
+    # fp32 draws, both masks.
+    wf = inputs.ATTN[inputs.HEADLINE_ATTN]
+    qf, kf, vf = (t.float().to(q.device) for t in inputs.attn_inputs(wf))
+    Of = torch.empty_like(qf)
+    lf = torch.empty((wf.B, wf.H, wf.N), dtype=torch.float32, device=q.device)
+    f32_large = {"workload": f"fp32 B={wf.B} H={wf.H} N={wf.N} d={wf.d} (the headline draws in fp32)",
+                 "peak_tflops": PEAK_FP32_MFMA_TFLOPS}
+    for causal in (False, True):
+        t = launch_times(lambda: osm.attention(qf, kf, vf, causal=causal, out=Of, lse=lf))
+        flops = 4.0 * wf.B * wf.H * wf.N * wf.N * wf.d / (2 if causal else 1)
+        tf = flops / (median(t) * 1e-3) / 1e12
+        f32_large["causal" if causal else "noncausal"] = {
+            "tflops_median": round(tf, 1), "frac_median": round(tf / PEAK_FP32_MFMA_TFLOPS, 4),
+            "ms_median": round(median(t), 4), "ms_min": round(min(t), 4)}
+    del qf, kf, vf, Of, lf
+
     O2 = torch.empty_like(q)
     lse2 = torch.empty((wa.B, wa.H, wa.N), dtype=torch.float32, device=q.device)
     nc_ms = per_launch_ms(lambda: osm.attention(q, k, v, causal=False, out=O2, lse=lse2))
@@ -521,6 +540,7 @@ def supplementary(osm, wa, ws, q, k, v, x, O, lse, reps=30, warm=10, warm_ms=15.
         "attn_backward_split": bsplit,
         "attn_varlen": varlen,
         "attn_configs": configs,
+        "attn_f32_large": f32_large,
     }
 
 

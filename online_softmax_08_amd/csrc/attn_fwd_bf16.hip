@@ -224,7 +224,17 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     __shared__ __attribute__((aligned(1024))) char kbuf0[KS * C::KTILE_B];
     __shared__ __attribute__((aligned(1024))) char kbuf1[KS * C::KTILE_B];
     __shared__ __attribute__((aligned(1024))) char vbuf0[KS * C::VTILE_B];
-    __shared__ __attribute__((aligned(1024))) char vbuf1[KS * C::VTILE_B];
+    // At D = 64 with two key groups the four buffers take 84 KiB, and the
+    // compiler, which schedules for the static LDS it sees, then plans for
+    // one workgroup per CU and gives the 4-wave kernel 176 registers and a
+    // slower loop.  There the second V buffer lives in dynamic LDS (passed
+    // at launch; a separate object, so its loads still provably do not
+    // alias the other buffers): 60 KiB static, 135 registers, +12-15% on
+    // [2, 8, 1024, 64] (both masks) and [1, 8, 2048, 64], same output.
+    constexpr bool VDYN = D == 64 && KS == 2;
+    extern __shared__ __attribute__((aligned(1024))) char vdyn[];
+    __shared__ __attribute__((aligned(1024))) char vsta1[VDYN ? 16 : KS * C::VTILE_B];
+    char* const vbuf1 = VDYN ? vdyn : vsta1;
     auto kbuf = [&](auto bufc) -> char* { if constexpr (decltype(bufc)::value == 0) return kbuf0; else return kbuf1; };
     auto vbuf = [&](auto bufc) -> char* { if constexpr (decltype(bufc)::value == 0) return vbuf0; else return vbuf1; };
 
@@ -1048,7 +1058,8 @@ hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* l
     using C = Cfg<D, QT, NW, BC, KS>;
     const int nqt = (N + C::BR - 1) / C::BR;
     const dim3 grid((unsigned)(nqt * BH)), block(C::T);
-    attn_fwd_bf16_kernel<D, QT, NW, WPE, BC, CAUSAL, VARLEN, KS><<<grid, block, 0, stream>>>(
+    constexpr unsigned dyn = (D == 64 && KS == 2) ? (unsigned)(KS * C::VTILE_B) : 0u;  // VDYN's buffer
+    attn_fwd_bf16_kernel<D, QT, NW, WPE, BC, CAUSAL, VARLEN, KS><<<grid, block, dyn, stream>>>(
         static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
         static_cast<__bf16*>(O), lse, N, BH, nqt, scale, cu, H, Hkv, total);
     return hipGetLastError();

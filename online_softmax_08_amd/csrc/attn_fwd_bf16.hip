@@ -222,19 +222,26 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // then prove that the DMA filling one buffer does not alias reads of the
     // other, and does not stall those reads on the DMA's completion.
     __shared__ __attribute__((aligned(1024))) char kbuf0[KS * C::KTILE_B];
-    __shared__ __attribute__((aligned(1024))) char kbuf1[KS * C::KTILE_B];
+    __shared__ __attribute__((aligned(1024))) char ksta1[(D == 128 && KS == 2) ? 16 : KS * C::KTILE_B];
     __shared__ __attribute__((aligned(1024))) char vbuf0[KS * C::VTILE_B];
-    // At D = 64 with two key groups the four buffers take 84 KiB, and the
-    // compiler, which schedules for the static LDS it sees, then plans for
-    // one workgroup per CU and gives the 4-wave kernel 176 registers and a
-    // slower loop.  There the second V buffer lives in dynamic LDS (passed
-    // at launch; a separate object, so its loads still provably do not
-    // alias the other buffers): 60 KiB static, 135 registers, +12-15% on
-    // [2, 8, 1024, 64] (both masks) and [1, 8, 2048, 64], same output.
-    constexpr bool VDYN = D == 64 && KS == 2;
+    // With two key groups the four buffers take 84 KiB at D = 64 and 148 KiB
+    // at D = 128, and the compiler, which schedules for the static LDS it
+    // sees, then plans for one workgroup per CU: the 4-wave kernels got 176
+    // and 292 registers and slower loops.  So part of the buffers lives in
+    // dynamic LDS (passed at launch): at D = 64 the second V buffer, at
+    // D = 128 the second K and V buffers together (always filled together
+    // and read together, so no load into one part of that object is in
+    // flight while the other part is read; the compiler still proves every
+    // tile load disjoint from the reads it overlaps).  Static LDS 60 and
+    // 74 KiB, 135 and 219 registers, same output bit for bit: +12-15% on
+    // [2, 8, 1024, 64] (both masks) and [1, 8, 2048, 64], +11-13% on
+    // [1, 8, 2048, 128] causal, [2, 4, 1000, 128] and [1, 2, 8192, 128]
+    // causal; the 8-wave workgroups unchanged.
+    constexpr bool VDYN = D == 64 && KS == 2, KVDYN = D == 128 && KS == 2;
     extern __shared__ __attribute__((aligned(1024))) char vdyn[];
-    __shared__ __attribute__((aligned(1024))) char vsta1[VDYN ? 16 : KS * C::VTILE_B];
-    char* const vbuf1 = VDYN ? vdyn : vsta1;
+    __shared__ __attribute__((aligned(1024))) char vsta1[(VDYN || KVDYN) ? 16 : KS * C::VTILE_B];
+    char* const kbuf1 = KVDYN ? vdyn : ksta1;
+    char* const vbuf1 = VDYN ? vdyn : KVDYN ? vdyn + KS * C::KTILE_B : vsta1;
     auto kbuf = [&](auto bufc) -> char* { if constexpr (decltype(bufc)::value == 0) return kbuf0; else return kbuf1; };
     auto vbuf = [&](auto bufc) -> char* { if constexpr (decltype(bufc)::value == 0) return vbuf0; else return vbuf1; };
 
@@ -1058,7 +1065,9 @@ hipError_t launch(const void* Q, const void* K, const void* V, void* O, float* l
     using C = Cfg<D, QT, NW, BC, KS>;
     const int nqt = (N + C::BR - 1) / C::BR;
     const dim3 grid((unsigned)(nqt * BH)), block(C::T);
-    constexpr unsigned dyn = (D == 64 && KS == 2) ? (unsigned)(KS * C::VTILE_B) : 0u;  // VDYN's buffer
+    // the part of the tile buffers in dynamic LDS (VDYN / KVDYN in the kernel)
+    constexpr unsigned dyn = (D == 64 && KS == 2) ? (unsigned)(KS * C::VTILE_B)
+                           : (D == 128 && KS == 2) ? (unsigned)(KS * (C::KTILE_B + C::VTILE_B)) : 0u;
     attn_fwd_bf16_kernel<D, QT, NW, WPE, BC, CAUSAL, VARLEN, KS><<<grid, block, dyn, stream>>>(
         static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
         static_cast<__bf16*>(O), lse, N, BH, nqt, scale, cu, H, Hkv, total);

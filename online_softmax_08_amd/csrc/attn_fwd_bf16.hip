@@ -1176,16 +1176,16 @@ int attn_splitkv_auto(int BH, int N, int d, bool causal)
     // 2048 waves, twice that under the causal mask (its query blocks differ
     // in length, and more, shorter ranges even them out), with at least 512
     // keys per range.  Rows of 1024 keys or fewer are not split, nor rows of
-    // 2048 or fewer without the mask or with more than 16384 rows in all:
-    // there the partials cost as much HBM time as the occupancy gains (and
-    // the single pass already splits the key loop over two wave groups).
-    // Measured with bf16 partials: [1, 4..8, 2048, d] causal gains 4-27%
-    // from 4 ranges, [1, 16..24, 2048, d] causal and [1, 8, 2048, 128]
-    // unmasked gain nothing or lose.
-    (void)d;
+    // 2048 or fewer without the mask or with more than 16384 rows in all
+    // (8192 at d = 64): there the partials cost as much HBM time as the
+    // occupancy gains (and the single pass already splits the key loop over
+    // two wave groups).  Measured with bf16 partials: [1, 4, 2048, 128]
+    // causal gains 14% from 4 ranges, [1, 8, 2048, 128] and [1, 4, 2048, 64]
+    // 3-4%; [1, 8, 2048, 64] and [1, 16..24, 2048, d] causal and
+    // [1, 8, 2048, 128] unmasked lose.
     const long long rows = (long long)BH * N;
     if (N <= 1024 || rows >= 65536) return 1;
-    if (N <= 2048 && (!causal || rows > 16384)) return 1;
+    if (N <= 2048 && (!causal || rows > (d == 64 ? 8192 : 16384))) return 1;
     long long s = (65536 * (causal ? 2 : 1) + rows - 1) / rows;
     const long long cap = N / 512;
     if (s > cap) s = cap;

@@ -218,9 +218,11 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     using C = Cfg<D, QT, NW, BC, KS>;
     static_assert(NW <= 8 && C::KTILE_B >= 2 * 32 * (D + 8) * 2, "output staging fits the tile buffers");
     constexpr int NMT = BC / 32;  // 32-key MFMA tiles per key tile
-    // Four separate LDS objects (not slices of one array): the compiler can
-    // then prove that the DMA filling one buffer does not alias reads of the
-    // other, and does not stall those reads on the DMA's completion.
+    // Separate LDS objects (not slices of one array): the compiler can then
+    // prove that the DMA filling one buffer does not alias reads of the
+    // other, and does not stall those reads on the DMA's completion.  (Below,
+    // two buffers may share the dynamic array only when they are filled
+    // together and read together.)
     __shared__ __attribute__((aligned(1024))) char kbuf0[KS * C::KTILE_B];
     __shared__ __attribute__((aligned(1024))) char ksta1[(D == 128 && KS == 2) ? 16 : KS * C::KTILE_B];
     __shared__ __attribute__((aligned(1024))) char vbuf0[KS * C::VTILE_B];
@@ -231,8 +233,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // dynamic LDS (passed at launch): at D = 64 the second V buffer, at
     // D = 128 the second K and V buffers together (always filled together
     // and read together, so no load into one part of that object is in
-    // flight while the other part is read; the compiler still proves every
-    // tile load disjoint from the reads it overlaps).  Static LDS 60 and
+    // flight while the other part is read).  Static LDS 60 and
     // 74 KiB, 135 and 219 registers, same output bit for bit: +12-15% on
     // [2, 8, 1024, 64] (both masks) and [1, 8, 2048, 64], +11-13% on
     // [1, 8, 2048, 128] causal, [2, 4, 1000, 128] and [1, 2, 8192, 128]

@@ -506,7 +506,11 @@ int attn_bwd_split_plan(int B, int H, int Hkv, int N, int d, int causal, int nsp
         const int st = check_heads(H, Hkv);
         if (st != OSM_OK) return st;
     }
-    if (nsplit == 0) nsplit = (bh == 0 || N == 0) ? 1 : osm::attn_bwd_split_auto((int)bh, N, d, causal != 0);
+    // The count follows the key/value heads: the dK/dV grid has B Hkv key
+    // blocks per row of blocks, and with grouped queries it is the one that
+    // leaves compute units idle.
+    if (nsplit == 0)
+        nsplit = (bh == 0 || N == 0) ? 1 : osm::attn_bwd_split_auto((int)((long long)B * Hkv), N, d, causal != 0);
     *nsplit_out = nsplit;
     *workspace_bytes = (bh == 0 || N == 0) ? 0
                        : nsplit == 1       ? attn_bwd_workspace_bytes(B, H, N)
@@ -521,8 +525,8 @@ int attn_bwd_split(const void* Q, const void* K, const void* V, const void* O, c
 {
     if (nsplit < 0 || nsplit > osm::kMaxSplits) return OSM_ERR_SPLITS;
     const long long bh = (long long)B * H;
-    if (B > 0 && H > 0 && N > 0 && bh <= INT_MAX && nsplit == 0)
-        nsplit = osm::attn_bwd_split_auto((int)bh, N, d, causal != 0);
+    if (B > 0 && H > 0 && N > 0 && bh <= INT_MAX && nsplit == 0 && check_heads(H, Hkv) == OSM_OK)
+        nsplit = osm::attn_bwd_split_auto((int)((long long)B * Hkv), N, d, causal != 0);
     if (nsplit <= 1)
         return attn_bwd(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Hkv, N, d, scale, causal, workspace,
                         workspace_bytes, stream);

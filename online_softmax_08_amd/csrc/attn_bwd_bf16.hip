@@ -842,13 +842,17 @@ hipError_t launch_bwd_split(const void* Q, const void* K, const void* V, const v
 
 int attn_bwd_split_auto(int BH, int N, int d, bool causal)
 {
-    // Measured over [1..2, 1..16, 2048..32768, d] (both masks): no split
+    // BH counts (batch, key/value head) slices: the dK/dV grid's.  Measured
+    // over [1..2, 1..16, 2048..32768, d] (both masks, Hkv = H): no split
     // while 8-wave workgroups of 256 rows cover the 256 compute units, nor
     // for rows of 2048 or fewer once the unsplit launch's 4-wave workgroups
     // do; otherwise enough ranges for about one 8-wave workgroup per CU,
     // twice that under the mask (its ranges are unequal), while each range
     // keeps at least 512 rows of the loop it divides (256 at d = 64, whose
-    // partials cost half the bytes), and at most 16.
+    // partials cost half the bytes), and at most 16.  With grouped queries
+    // (measured on [2, 16/4, 2048, 128], [1, 32/1..8, 4096, 128],
+    // [2, 16/2, 4096, 64], [1, 32/4, 8192, 128]) this count is the best of
+    // the sweep or within 6% of it, and 1.3-4x the unsplit call.
     const long long w = (long long)((N + 255) / 256) * BH;
     if (w >= kCUs || N <= 256) return 1;
     if (N <= 2048 && (long long)((N + 127) / 128) * BH >= kCUs) return 1;

@@ -372,6 +372,12 @@ def test_bwd_split_plan(abi):
     # rows of 2048 when 128-row blocks do ...
     auto = lambda B, H, N, d, c: abi.attn_bwd_split_plan(B, H, H, N, d, c, 0)[0]
     assert auto(2, 16, 4096, 128, True) == 1
+    # ... and with grouped queries the count follows the key/value heads
+    # (the dK/dV grid): [2, 16/4, 2048, 128] has 64 key blocks of 256 rows.
+    assert abi.attn_bwd_split_plan(2, 16, 4, 2048, 128, True, 0)[0] == 4
+    assert abi.attn_bwd_split_plan(2, 16, 4, 2048, 128, False, 0)[0] == 4
+    assert abi.attn_bwd_split_plan(1, 32, 1, 4096, 128, True, 0)[0] == 8
+    assert abi.attn_bwd_split_plan(1, 32, 32, 4096, 128, True, 0)[0] == 1
     assert auto(1, 16, 2048, 128, False) == 1 and auto(2, 8, 2048, 128, True) == 1
     assert auto(1, 1, 256, 64, False) == 1
     # ... below that, about one 8-wave workgroup per CU (twice that under the

@@ -206,3 +206,37 @@ def test_gqa_backward_eight_wave(osm, causal):
                   flush=True)
             ok &= e <= bar
     assert ok
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_backward_split_auto(osm, causal):
+    # attn_bwd_split with the library's count on grouped queries: the count
+    # follows the key/value heads ([2, 16/4, 2048, 128]: 64 key blocks, so 4
+    # ranges), the dK/dV loop walking a range of its group's query heads and
+    # tiles.  The gradients of two whole key/value heads (and their 4 query
+    # heads each) against the oracle on repeated heads.
+    B, H, Hkv, N, d = 2, 16, 4, 2048, 128
+    G = H // Hkv
+    assert osm.attn_bwd_split_plan(B, H, Hkv, N, d, causal, 0)[0] == 4
+    q, k, v = _case(B, H, Hkv, N, d, seed=97)
+    g = inputs.grad_output(q.shape, 98)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, g))
+    O, lse = osm.attention(qd, kd, vd, causal=causal)
+    dq, dk, dv = osm.attention_backward_split(qd, kd, vd, O, lse, gd, causal=causal, nsplit=0)
+    torch.cuda.synchronize()
+    dq, dk, dv = (t.float().cpu() for t in (dq, dk, dv))
+    ok = True
+    for b, kv in ((0, 0), (B - 1, Hkv - 1)):
+        hs = slice(kv * G, kv * G + G)
+        rq, rk, rv = oracle.attn_bwd(q[b:b + 1, hs], _rep(k[b:b + 1, kv:kv + 1], G),
+                                     _rep(v[b:b + 1, kv:kv + 1], G), g[b:b + 1, hs],
+                                     1 / math.sqrt(d), causal)
+        for name, a, ref in (("dQ", dq[b:b + 1, hs], rq), ("dK", dk[b, kv], rk.sum(axis=1)[0]),
+                             ("dV", dv[b, kv], rv.sum(axis=1)[0])):
+            e = _maxabs(a, ref)
+            bar = TOL_G * max(1.0, float(np.max(np.abs(ref))))
+            print(f"gqa bwd split auto b{b} kv{kv} causal={causal}: {name} max|err|={e:.3e} bar={bar:.3e}",
+                  flush=True)
+            ok &= e <= bar
+    assert ok

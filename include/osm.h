@@ -371,8 +371,9 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
  * workspace.
  *   B, H, Hkv, N, d, causal : as for attn_bwd (d must be 64 or 128)
  *   nsplit             : 1 .. 64 ranges, or 0 to let the library choose (it
- *                        splits only when 256-row blocks alone would leave
- *                        compute units idle)
+ *                        splits only when 256-row blocks of the B Hkv
+ *                        key/value slices would leave compute units idle, so
+ *                        grouped queries split sooner)
  *   *nsplit_out        : the count attn_bwd_split will use for nsplit
  *   *workspace_bytes   : device bytes attn_bwd_split needs for it: for a
  *                        count of 1 attn_bwd_workspace_bytes(B, H, N) (the

@@ -1185,6 +1185,14 @@ int attn_splitkv_auto(int BH, int N, int d, bool causal)
     // 3-4%; [1, 8, 2048, 64] and [1, 16..24, 2048, d] causal and
     // [1, 8, 2048, 128] unmasked lose.
     const long long rows = (long long)BH * N;
+    // Unmasked grids of 256-row blocks just past one round of the CUs (the
+    // second round nearly empty): two ranges fill the rounds better.
+    // Measured: [1, 24, 3000, 128] +5%, [1, 17, 4096, 128] and
+    // [2, 9, 3600, 128] +8%, [1, 20, 4096, 64] +15%; [1, 12, 8192, 128] (a
+    // half-full second round) +1%, and longer grids gain less than the
+    // partials cost.
+    const long long w256 = (long long)BH * ((N + 255) / 256);
+    if (!causal && N > 2048 && w256 > 256 && w256 < 512 && w256 % 256 <= 96) return 2;
     if (N <= 1024 || rows >= 65536) return 1;
     if (N <= 2048 && (!causal || rows > (d == 64 ? 8192 : 16384))) return 1;
     long long s = (65536 * (causal ? 2 : 1) + rows - 1) / rows;

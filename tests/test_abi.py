@@ -157,6 +157,12 @@ def test_splitkv_plan(abi):
     assert abi.attn_fwd_splitkv_plan(1, 8, 2048, 128, False, 0) == (1, 0)
     assert abi.attn_fwd_splitkv_plan(1, 16, 2048, 128, True, 0) == (1, 0)
     assert abi.attn_fwd_splitkv_plan(1, 8, 2048, 64, True, 0) == (1, 0)
+    # ... and unmasked grids whose second round of 256-row blocks is nearly
+    # empty take two ranges, however many rows they have.
+    assert abi.attn_fwd_splitkv_plan(1, 24, 3000, 128, False, 0)[0] == 2
+    assert abi.attn_fwd_splitkv_plan(1, 24, 3000, 128, True, 0) == (1, 0)
+    assert abi.attn_fwd_splitkv_plan(1, 12, 8192, 128, False, 0) == (1, 0)
+    assert abi.attn_fwd_splitkv_plan(1, 33, 2048, 128, False, 0) == (1, 0)
     # ... and none for rows of 1024 keys or fewer, or empty problems.
     assert abi.attn_fwd_splitkv_plan(2, 4, 1024, 128, True, 0) == (1, 0)
     assert abi.attn_fwd_splitkv_plan(1, 1, 256, 64, False, 0) == (1, 0)

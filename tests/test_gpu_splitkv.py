@@ -127,6 +127,21 @@ def test_splitkv_short_causal_rows_full(osm, shape):
     assert eo <= TOL_O and el <= TOL_LSE
 
 
+def test_splitkv_nearly_empty_round_full(osm):
+    # 24 heads of 3000 rows unmasked: 288 blocks of 256 rows, a second round
+    # of 32; the library takes two ranges.  Every element against the oracle.
+    B, H, N, d = 1, 24, 3000, 128
+    assert osm.attn_fwd_splitkv_plan(B, H, N, d, False, 0)[0] == 2
+    q, k, v = _inputs(B, H, N, d, seed=3100)
+    print(f"splitkv B{B}H{H}N{N}d{d} causal=0 auto nsplit=2", flush=True)
+    O, lse = _gpu_split(osm, q, k, v, False, 0)
+    Oref, lref = oracle.attn_fwd(q, k, v, 1.0 / math.sqrt(d), False)
+    eo, el = _maxabs(O, Oref), _maxabs(lse, lref)
+    print(f"  max|dO|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse))
+    assert eo <= TOL_O and el <= TOL_LSE
+
+
 def test_splitkv_deterministic_and_one_split_is_attn_fwd(osm):
     q, k, v = _inputs(1, 2, 3000, 128, seed=77)
     dev = torch.device("cuda:0")
